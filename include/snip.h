@@ -1,0 +1,253 @@
+/*
+ * snip.h -- C ABI of libsnip: quantizers, block-scaled GEMMs and the
+ * quantized linear layer of a Llama-like block, for AMD MI355X (gfx950).
+ *
+ * What the operations compute (sources cited by page title and section):
+ *   - "SNIP: An Adaptive Mixed Precision Framework for Subbyte LLM
+ *     Training", Abstract and Fig. 5: every linear layer of the block
+ *     (Fig. 4: Q, K, V, O, Gate, Up, Down) runs its forward GEMM and its two
+ *     backward GEMMs in a per-layer precision (FP8 or FP4; BF16 baseline),
+ *     and statistics of activations and gradients are gathered to judge the
+ *     precision loss.
+ *   - "FP4 All the Way" summary page, Outline: NVFP4 = blocks of 16 E2M1
+ *     values sharing one E4M3 scale; round-to-nearest in the forward pass,
+ *     stochastic rounding in back-propagation and update.
+ *   - "Research on Mixed-Precision Training for LLMs", Core Techniques:
+ *     stochastic rounding rounds up or down by proximity and keeps the
+ *     expected value.
+ *
+ * Conventions
+ *   Ownership   The caller allocates and owns every buffer: inputs, outputs,
+ *               quantized codes/scales, statistics and workspace. The library
+ *               never allocates device memory.
+ *   Pointers    Arguments documented "device" are device addresses; "host"
+ *               ones are host addresses. Device pointers must be 16-byte
+ *               aligned; leading dimensions are in elements.
+ *   Streams     `stream` is a hipStream_t passed as void* (NULL = the null
+ *               stream). Calls enqueue work and return before it completes,
+ *               except snip_layer_stats, which synchronises the stream.
+ *   Errors      Every call returns an int status (SNIP_OK = 0 or a negative
+ *               SNIP_E_* code). Arguments are validated on the host before
+ *               any HIP call, so a rejected call has enqueued nothing.
+ *               snip_last_error() returns a thread-local message for the
+ *               last failure. No C++ exception crosses this interface.
+ *   Threads     Calls hold no global mutable state and may be made from
+ *               several threads; work enqueued on one stream is ordered.
+ *   Workspace   Caller-provided device scratch of at least the size the
+ *               matching snip_*_workspace() returns; its contents need no
+ *               initialisation and are clobbered. Calls that overlap in time
+ *               must not share a workspace.
+ *
+ * Number formats and rounding (the full definitions are in the design notes)
+ *   SNIP_NVFP4     4-bit E2M1 codes {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6},
+ *                  one E4M3 scale per 16 consecutive K elements, and a
+ *                  power-of-two tensor scale 2^e: e is the smallest integer
+ *                  with max|x| / 2^e <= 6 * 448. Block scale = E4M3 RNE of
+ *                  blockmax|x / 2^e| / 6; element r = (x / 2^e) * fp32(1 / s).
+ *   SNIP_FP8_E4M3  8-bit E4M3 ("fn": max 448, no infinities) codes and a
+ *                  power-of-two tensor scale with max|x| / 2^e <= 448.
+ *   SNIP_MXFP4     E2M1 codes, one E8M0 scale per 32 K elements,
+ *                  scale exponent floor(log2 blockmax|x|) - 2.
+ *   SNIP_BF16      no quantization (bf16 values, K-contiguous).
+ *   SNIP_RNE       round to nearest, ties to even, saturating.
+ *   SNIP_SR        stochastic rounding with 16 random bits per element from
+ *                  Philox4x32-10: key (seed lo, seed hi), counter
+ *                  (g lo, g hi, tensor_id, 0), g = idx >> 3, word (idx>>1)&3,
+ *                  half idx & 1, idx = element index in the quantized
+ *                  output layout (row * K + k). Round the magnitude up iff
+ *                  R16 + floor(frac * 2^16) >= 2^16, frac being the position
+ *                  of |r| between its two neighbouring representable values.
+ */
+#ifndef SNIP_H
+#define SNIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define SNIP_OK            0
+#define SNIP_E_NULL       -1  /* a required pointer is NULL                  */
+#define SNIP_E_SHAPE      -2  /* a dimension is out of range or misaligned   */
+#define SNIP_E_ALIGN      -3  /* a device pointer is not 16-byte aligned     */
+#define SNIP_E_FORMAT     -4  /* unknown format / rounding / layout, or a mismatch */
+#define SNIP_E_WORKSPACE  -5  /* workspace missing or too small              */
+#define SNIP_E_HIP        -6  /* a HIP launch or API call failed             */
+#define SNIP_E_NONFINITE  -7  /* statistics report non-finite inputs         */
+
+/* ---- enums ------------------------------------------------------------ */
+#define SNIP_BF16      0
+#define SNIP_FP8_E4M3  1
+#define SNIP_NVFP4     2
+#define SNIP_MXFP4     3
+
+#define SNIP_RNE       0
+#define SNIP_SR        1
+
+#define SNIP_ROWWISE   0  /* blocks along each row: [R, C] -> [R, C]        */
+#define SNIP_COLWISE   1  /* blocks along each column: [R, C] -> [C, R]     */
+
+/* ---- descriptors ------------------------------------------------------ */
+
+/* A quantized operand: `rows` rows of `k` elements, K-contiguous.
+ * Host struct describing caller-owned device buffers:
+ *   codes       device. NVFP4/MXFP4: u8[rows][k/2], element k in the low
+ *               nibble when k is even, bit 3 of a nibble = sign.
+ *               FP8: u8[rows][k]. BF16: bf16[rows][k].
+ *   scales      device. NVFP4: E4M3 u8[rows][k/16]; MXFP4: E8M0 u8[rows][k/32];
+ *               NULL for FP8 and BF16.
+ *   tensor_exp  device int32: exponent e of the tensor scale 2^e for NVFP4
+ *               and FP8 (written by snip_quantize); unused (may be NULL)
+ *               for MXFP4 and BF16. */
+typedef struct snip_qtensor {
+  int32_t  format;
+  int32_t  reserved;
+  int64_t  rows;
+  int64_t  k;
+  void*    codes;
+  void*    scales;
+  int32_t* tensor_exp;
+} snip_qtensor;
+
+/* Per-tensor statistics of one quantize pass (device memory, 24 bytes):
+ *   sum_err2    sum over finite elements of (Q(x) - x)^2 (fp64 total)
+ *   sum_x2      sum over finite elements of x^2
+ *   amax        max |x| over the finite elements (the tensor-scale input)
+ *   n_nonfinite number of NaN / Inf inputs (their blocks' codes are
+ *               unspecified) */
+typedef struct snip_stats {
+  double   sum_err2;
+  double   sum_x2;
+  float    amax;
+  uint32_t n_nonfinite;
+} snip_stats;
+
+/* Host-side report derived from one snip_stats record. */
+typedef struct snip_tensor_report {
+  double   sum_err2;
+  double   sum_x2;
+  double   rel_mse;      /* sum_err2 / sum_x2 (0 when both are 0)            */
+  double   norm_ratio;   /* ||x|| / ||Q(x) - x|| (+inf when the error is 0)  */
+  float    amax;
+  uint32_t n_nonfinite;
+  int32_t  below_sqrt3;  /* 1 when ||x|| < sqrt(3) * ||Q(x) - x||: the regime
+                            where learning on quantized gradients loses
+                            efficiency ("FP4 All the Way", Outline)         */
+  int32_t  reserved;
+} snip_tensor_report;
+
+/* ---- quantizer -------------------------------------------------------- */
+
+/* Quantize one bf16 row-major tensor x[rows][cols] (leading dimension ld).
+ * [FP4 All the Way, Outline] (formats, RTN/SR); [SNIP, Abstract] (stats).
+ *   x          device bf16, 16-byte aligned, ld >= cols, ld % 8 == 0
+ *   rows, cols > 0, cols % 16 == 0. ROWWISE: K = cols (MXFP4: cols % 32 == 0).
+ *              COLWISE: K = rows, rows % 16 == 0 (MXFP4: % 32 == 0).
+ *   layout     SNIP_ROWWISE -> out is [rows][cols]; SNIP_COLWISE -> out is
+ *              [cols][rows] (the transpose, blocks along the source rows).
+ *   format, rounding  as above (BF16 ignores rounding and copies/transposes).
+ *   seed, tensor_id   random stream for SNIP_SR (ignored for SNIP_RNE).
+ *   amax_in    device float or NULL. NULL: the tensor max is computed from x
+ *              (an extra read pass). Non-NULL: used as max|x| (delayed
+ *              scaling; elements beyond it saturate).
+ *   out        host descriptor of caller-owned device buffers; out->format,
+ *              out->rows and out->k must match the call.
+ *   stats      device snip_stats or NULL.
+ *   ws         device workspace of snip_quantize_workspace() bytes.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
+int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                  int layout, int format, int rounding,
+                  uint64_t seed, uint32_t tensor_id, const float* amax_in,
+                  const snip_qtensor* out, snip_stats* stats,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---- block-scaled GEMM ------------------------------------------------- */
+
+/* c[M][N] (fp32, leading dimension ldc, overwritten) = A . B^T, with
+ * A = dequant(a) [M][K] and B = dequant(b) [N][K]; M = a->rows, N = b->rows,
+ * K = a->k = b->k. [SNIP, Fig. 5]: the GEMMs of a linear layer.
+ *   a, b       host descriptors; same format; K % 128 == 0; M, N > 0.
+ *              NVFP4 runs on fp16 MFMA after exact decoding of
+ *              code x block scale; FP8 and MXFP4 on the gfx950 8-bit / 4-bit
+ *              MFMA (MXFP4 with its E8M0 block scales in the instruction);
+ *              BF16 on bf16 MFMA. Accumulation is fp32; the tensor scales
+ *              2^(ea + eb) are applied in the epilogue.
+ *   c          device fp32, ldc >= N.
+ *   ws         may be NULL when ws_bytes == 0 (no workspace needed).
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, HIP. */
+int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t ldc,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* ---- quantized linear layer --------------------------------------------- */
+
+/* Forward: y[T][out] (fp32) = Q_rne(x) . Q_rne(w)^T. [SNIP, Fig. 5];
+ * [FP4 All the Way, Outline] (round-to-nearest forward).
+ *   x          device bf16 [T][in]; w device bf16 [out][in] (contiguous).
+ *   T, in, out > 0; in % 128 == 0 (the GEMM's K); T, out any.
+ *   format     the layer's GEMM format from the plan.
+ *   seed, layer_id  random-stream namespace (tensor ids 8*layer_id + {0,1};
+ *              RTN draws no random bits).
+ *   y          device fp32 [T][out].
+ *   stats2     device snip_stats[2] = {X, W} or NULL.
+ *   ws         device, snip_linear_fwd_workspace() bytes.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
+int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t out,
+                    int format, uint64_t seed, uint32_t layer_id,
+                    float* y, snip_stats* stats2, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward: dx[T][in] = Q_sr(dy) . Q_sr(w^T)^T   (K = out, fmt_dgrad)
+ *           dw[out][in] = Q_sr(dy^T) . Q_sr(x^T)^T (K = T, fmt_wgrad)
+ * [SNIP, Fig. 5]; [FP4 All the Way, Outline] (stochastic rounding in
+ * back-propagation and update).
+ *   dy         device bf16 [T][out]; x [T][in]; w [out][in] (contiguous).
+ *   out % 128 == 0 and in % 16 == 0 when dx is computed; T % 128 == 0 and
+ *   in % 16 == 0, out % 16 == 0 when dw is computed.
+ *   tensor ids 8*layer_id + {2: dY row-wise, 3: W column-wise,
+ *              4: dY column-wise, 5: X column-wise}.
+ *   dx, dw     device fp32 or NULL (NULL skips that GEMM and its operands).
+ *   stats4     device snip_stats[4] = {dY, W^T, dY^T, X^T} or NULL
+ *              (entries of a skipped GEMM are left untouched).
+ *   ws         device, snip_linear_bwd_workspace() bytes.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
+int snip_linear_bwd(const void* dy, const void* x, const void* w,
+                    int64_t T, int64_t in, int64_t out,
+                    int fmt_dgrad, int fmt_wgrad, uint64_t seed, uint32_t layer_id,
+                    float* dx, float* dw, snip_stats* stats4,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronise `stream`, copy n device statistics records to the host and
+ * derive the report of each. [SNIP, Abstract] (statistics for the precision
+ * decision); [FP4 All the Way, Outline] (sqrt(3) threshold).
+ *   dev_stats  device snip_stats[n]; host_out host snip_tensor_report[n].
+ * Returns SNIP_E_NONFINITE (after filling host_out) when any record counts
+ * non-finite inputs. Errors: NULL, SHAPE, HIP, NONFINITE. */
+int snip_layer_stats(const snip_stats* dev_stats, int n, snip_tensor_report* host_out,
+                     void* stream);
+
+/* ---- sizing and diagnostics -------------------------------------------- */
+
+/* Workspace bytes for the calls above (0 on invalid arguments). */
+size_t snip_quantize_workspace(int64_t rows, int64_t cols, int layout, int format);
+size_t snip_qgemm_workspace(int64_t M, int64_t N, int64_t K, int format);
+size_t snip_linear_fwd_workspace(int64_t T, int64_t in, int64_t out, int format);
+size_t snip_linear_bwd_workspace(int64_t T, int64_t in, int64_t out,
+                                 int fmt_dgrad, int fmt_wgrad);
+
+/* Bytes of one part of a quantized operand: part 0 = codes, 1 = scales.
+ * Returns -1 on invalid arguments. */
+int64_t snip_qtensor_bytes(int format, int64_t rows, int64_t k, int part);
+
+/* Thread-local message for the last failed call ("" if none). */
+const char* snip_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int snip_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNIP_H */

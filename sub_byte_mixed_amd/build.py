@@ -1,0 +1,49 @@
+"""Build libsnip.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+Run `python -m sub_byte_mixed_amd.build` or call build(); it always
+recompiles. hipcc flags: -ffp-contract=off keeps the fp32 rounding sequence
+of the quantizers bit-exact, -fno-gpu-flush-denormals-to-zero keeps fp32
+subnormals, and the packed-fp32 instructions are disabled.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libsnip.so")
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc_path() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found")
+    return p
+
+
+def build(verbose: bool = False) -> str:
+    out_tmp = LIB + ".tmp"
+    cmd = [hipcc_path(), *HIPCC_FLAGS, "-o", out_tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
+    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed:\n{errs}")
+    os.replace(out_tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

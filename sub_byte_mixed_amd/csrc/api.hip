@@ -1,0 +1,648 @@
+// Host side of libsnip's C ABI: argument validation (before any HIP call),
+// workspace carving and kernel enqueueing. See include/snip.h for the
+// contract of each entry point.
+//
+// The quantized linear layer follows "SNIP", Fig. 5 (forward GEMM and the
+// two backward GEMMs of a linear layer, each in the layer's plan format) and
+// "FP4 All the Way" summary, Outline (round-to-nearest forward operands,
+// stochastic rounding for back-propagation and update operands).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace snip;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return SNIP_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool valid_format(int f) { return f >= SNIP_BF16 && f <= SNIP_MXFP4; }
+int block_of(int f) { return f == SNIP_MXFP4 ? 32 : 16; }
+bool has_scales(int f) { return f == SNIP_NVFP4 || f == SNIP_MXFP4; }
+bool has_texp(int f) { return f == SNIP_NVFP4 || f == SNIP_FP8_E4M3; }
+bool needs_amax(int f) { return has_texp(f); }
+
+int64_t code_bytes(int f, int64_t rows, int64_t k) {
+  switch (f) {
+    case SNIP_NVFP4:
+    case SNIP_MXFP4: return rows * k / 2;
+    case SNIP_FP8_E4M3: return rows * k;
+    case SNIP_BF16: return rows * k * 2;
+  }
+  return -1;
+}
+int64_t scale_bytes(int f, int64_t rows, int64_t k) {
+  if (f == SNIP_NVFP4) return rows * k / 16;
+  if (f == SNIP_MXFP4) return rows * k / 32;
+  return 0;
+}
+
+constexpr size_t kAlign = 256;
+constexpr size_t kAmaxBytes = align_up(kAmaxWG * sizeof(uint32_t), kAlign);
+constexpr size_t kPartBytes = align_up(kQuantWG * sizeof(StatPart), kAlign);
+// scratch of one quantize pass: amax partials + statistics partials
+constexpr size_t kQuantWS = kAmaxBytes + kPartBytes;
+
+size_t qtensor_ws_bytes(int f, int64_t rows, int64_t k) {
+  return align_up((size_t)code_bytes(f, rows, k), kAlign) +
+         align_up((size_t)scale_bytes(f, rows, k), kAlign) + kAlign;
+}
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+  uint8_t* base;
+  size_t used = 0;
+  explicit Carver(void* p) : base(static_cast<uint8_t*>(p)) {}
+  uint8_t* take(size_t n) {
+    uint8_t* p = base + used;
+    used += align_up(n, kAlign);
+    return p;
+  }
+};
+
+// Grid sizes.
+int amax_wg(int64_t rows, int64_t cols) {
+  const int64_t chunks = rows * cols / 8;
+  int64_t wg = ceil_div(chunks, 256 * 4);
+  if (wg < 1) wg = 1;
+  return (int)(wg > kAmaxWG ? kAmaxWG : wg);
+}
+int quant_wg(int layout, int f, int64_t rows, int64_t cols) {
+  int64_t wg;
+  if (f == SNIP_BF16) {
+    wg = layout == SNIP_ROWWISE ? ceil_div(rows * cols / 8, 256 * 2) : ceil_div(rows, 64) * ceil_div(cols, 64);
+  } else if (layout == SNIP_ROWWISE) {
+    wg = ceil_div(rows * cols / (f == SNIP_MXFP4 ? 32 : 16), 256);
+  } else {
+    wg = ceil_div(rows, kColTileRows) * ceil_div(cols, kColTileCols);
+  }
+  if (wg < 1) wg = 1;
+  return (int)(wg > kQuantWG ? kQuantWG : wg);
+}
+
+hipError_t g_last_hip = hipSuccess;
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return fail(SNIP_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  }
+  return SNIP_OK;
+}
+
+// One planned quantize pass (used by snip_quantize and the linear layer).
+struct QPlan {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  int layout, format;
+  bool sr;
+  uint64_t seed;
+  uint32_t tensor_id;
+  const float* amax_in;
+  const uint32_t* amax_part;   // partials of the amax pass (if any)
+  int n_amax_part;
+  uint8_t* codes;
+  uint8_t* scales;
+  int32_t* texp;
+  StatPart* part;
+  int nwg;
+  snip_stats* stats;
+};
+
+QJob make_qjob(const QPlan& p, int wg0) {
+  QJob j;
+  j.x = p.x;
+  j.rows = p.rows;
+  j.cols = p.cols;
+  j.ld = p.ld;
+  j.codes = p.codes;
+  j.scales = p.scales;
+  j.texp = p.texp;
+  j.amax_in = p.amax_in;
+  j.amax_part = p.amax_part;
+  j.n_amax_part = p.n_amax_part;
+  j.part = p.part;
+  j.seed = p.seed;
+  j.tensor_id = p.tensor_id;
+  j.wg0 = wg0;
+  j.nwg = p.nwg;
+  return j;
+}
+
+// Enqueue a group of quantize passes sharing (layout, format, rounding).
+int run_quant_group(const QPlan* const* ps, int n, hipStream_t s) {
+  if (n == 0) return SNIP_OK;
+  QJobs jobs;
+  std::memset(&jobs, 0, sizeof(jobs));
+  int wg = 0;
+  for (int i = 0; i < n; ++i) {
+    jobs.j[i] = make_qjob(*ps[i], wg);
+    wg += ps[i]->nwg;
+  }
+  for (int i = n; i < kMaxJobs; ++i) jobs.j[i].wg0 = 1 << 30;
+  jobs.n = n;
+  const QPlan& p = *ps[0];
+  hipError_t e;
+  if (p.format == SNIP_BF16) {
+    e = p.layout == SNIP_ROWWISE ? launch_bf16_copy(jobs, wg, s) : launch_bf16_transpose(jobs, wg, s);
+  } else if (p.layout == SNIP_ROWWISE) {
+    e = launch_quant_row(p.format, p.sr, jobs, wg, s);
+  } else {
+    e = launch_quant_col(p.format, p.sr, jobs, wg, s);
+  }
+  return hip_check(e, "quantize launch");
+}
+
+// Amax passes for up to kMaxJobs tensors in one launch.
+struct APlan {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  uint32_t* part;
+  int nwg;
+};
+
+int run_amax(const APlan* ps, int n, hipStream_t s) {
+  if (n == 0) return SNIP_OK;
+  AJobs jobs;
+  std::memset(&jobs, 0, sizeof(jobs));
+  int wg = 0;
+  for (int i = 0; i < n; ++i) {
+    jobs.j[i] = AJob{ps[i].x, ps[i].rows, ps[i].cols, ps[i].ld, ps[i].part, wg, ps[i].nwg};
+    wg += ps[i].nwg;
+  }
+  for (int i = n; i < kMaxJobs; ++i) jobs.j[i].wg0 = 1 << 30;
+  jobs.n = n;
+  return hip_check(launch_amax(jobs, wg, s), "amax launch");
+}
+
+int run_finalize(const QPlan* const* ps, int n, hipStream_t s) {
+  FJobs f;
+  std::memset(&f, 0, sizeof(f));
+  for (int i = 0; i < n; ++i) {
+    if (!ps[i] || !ps[i]->stats) continue;
+    f.j[f.n++] = FJob{ps[i]->part, ps[i]->nwg, ps[i]->stats};
+  }
+  return hip_check(launch_finalize(f, s), "finalize launch");
+}
+
+// Group passes by (layout, format, rounding) and launch each group once.
+int run_quant_all(QPlan* const* ps, int n, hipStream_t s) {
+  bool done[8] = {false};
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    const QPlan* grp[kMaxJobs];
+    int g = 0;
+    for (int j = i; j < n && g < kMaxJobs; ++j) {
+      if (done[j]) continue;
+      if (ps[j]->layout == ps[i]->layout && ps[j]->format == ps[i]->format && ps[j]->sr == ps[i]->sr) {
+        grp[g++] = ps[j];
+        done[j] = true;
+      }
+    }
+    const int rc = run_quant_group(grp, g, s);
+    if (rc) return rc;
+  }
+  return SNIP_OK;
+}
+
+int validate_qtensor(const snip_qtensor* q, const char* name, bool need_codes = true) {
+  if (!q) return fail(SNIP_E_NULL, "%s: descriptor is NULL", name);
+  if (!valid_format(q->format)) return fail(SNIP_E_FORMAT, "%s: unknown format %d", name, q->format);
+  if (q->rows <= 0 || q->k <= 0) return fail(SNIP_E_SHAPE, "%s: rows=%lld k=%lld must be > 0", name,
+                                           (long long)q->rows, (long long)q->k);
+  if (q->k % block_of(q->format)) return fail(SNIP_E_SHAPE, "%s: k=%lld not a multiple of %d", name,
+                                             (long long)q->k, block_of(q->format));
+  if (need_codes && !q->codes) return fail(SNIP_E_NULL, "%s: codes is NULL", name);
+  if (has_scales(q->format) && !q->scales) return fail(SNIP_E_NULL, "%s: scales is NULL", name);
+  if (has_texp(q->format) && !q->tensor_exp) return fail(SNIP_E_NULL, "%s: tensor_exp is NULL", name);
+  if (!aligned(q->codes, 16) || !aligned(q->scales, 16) || !aligned(q->tensor_exp, 4))
+    return fail(SNIP_E_ALIGN, "%s: device pointers must be 16-byte aligned", name);
+  return SNIP_OK;
+}
+
+}  // namespace
+
+// ====================================================================== API
+extern "C" {
+
+const char* snip_last_error(void) { return g_err.c_str(); }
+
+int snip_version(void) { return 100; }
+
+int64_t snip_qtensor_bytes(int format, int64_t rows, int64_t k, int part) {
+  if (!valid_format(format) || rows <= 0 || k <= 0 || (part != 0 && part != 1)) return -1;
+  if (k % block_of(format)) return -1;
+  return part == 0 ? code_bytes(format, rows, k) : scale_bytes(format, rows, k);
+}
+
+size_t snip_quantize_workspace(int64_t rows, int64_t cols, int layout, int format) {
+  if (rows <= 0 || cols <= 0 || !valid_format(format) || (layout != SNIP_ROWWISE && layout != SNIP_COLWISE))
+    return 0;
+  return kQuantWS;
+}
+
+size_t snip_qgemm_workspace(int64_t M, int64_t N, int64_t K, int format) {
+  (void)M; (void)N; (void)K; (void)format;
+  return 0;
+}
+
+size_t snip_linear_fwd_workspace(int64_t T, int64_t in, int64_t out, int format) {
+  if (T <= 0 || in <= 0 || out <= 0 || !valid_format(format)) return 0;
+  return 2 * kQuantWS + qtensor_ws_bytes(format, T, in) + qtensor_ws_bytes(format, out, in);
+}
+
+size_t snip_linear_bwd_workspace(int64_t T, int64_t in, int64_t out, int fmt_dgrad, int fmt_wgrad) {
+  if (T <= 0 || in <= 0 || out <= 0 || !valid_format(fmt_dgrad) || !valid_format(fmt_wgrad)) return 0;
+  return 3 * kAmaxBytes + 4 * kPartBytes + qtensor_ws_bytes(fmt_dgrad, T, out) +
+         qtensor_ws_bytes(fmt_dgrad, in, out) + qtensor_ws_bytes(fmt_wgrad, out, T) +
+         qtensor_ws_bytes(fmt_wgrad, in, T);
+}
+
+int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int layout, int format,
+                  int rounding, uint64_t seed, uint32_t tensor_id, const float* amax_in,
+                  const snip_qtensor* out, snip_stats* stats, void* ws, size_t ws_bytes,
+                  void* stream) {
+  if (!x) return fail(SNIP_E_NULL, "snip_quantize: x is NULL");
+  if (!valid_format(format)) return fail(SNIP_E_FORMAT, "snip_quantize: unknown format %d", format);
+  if (rounding != SNIP_RNE && rounding != SNIP_SR)
+    return fail(SNIP_E_FORMAT, "snip_quantize: unknown rounding %d", rounding);
+  if (layout != SNIP_ROWWISE && layout != SNIP_COLWISE)
+    return fail(SNIP_E_FORMAT, "snip_quantize: unknown layout %d", layout);
+  if (rows <= 0 || cols <= 0) return fail(SNIP_E_SHAPE, "snip_quantize: rows=%lld cols=%lld must be > 0",
+                                          (long long)rows, (long long)cols);
+  if (cols % 16) return fail(SNIP_E_SHAPE, "snip_quantize: cols=%lld not a multiple of 16", (long long)cols);
+  if (ld < cols || ld % 8) return fail(SNIP_E_SHAPE, "snip_quantize: ld=%lld must be >= cols and a multiple of 8",
+                                       (long long)ld);
+  const int blk = block_of(format);
+  const int64_t K = layout == SNIP_ROWWISE ? cols : rows;
+  const int64_t R = layout == SNIP_ROWWISE ? rows : cols;
+  if (K % blk) return fail(SNIP_E_SHAPE, "snip_quantize: K=%lld not a multiple of %d", (long long)K, blk);
+  const int rc = validate_qtensor(out, "snip_quantize: out");
+  if (rc) return rc;
+  if (out->format != format) return fail(SNIP_E_FORMAT, "snip_quantize: out->format %d != format %d",
+                                         out->format, format);
+  if (out->rows != R || out->k != K)
+    return fail(SNIP_E_SHAPE, "snip_quantize: out is [%lld][%lld], expected [%lld][%lld]",
+                (long long)out->rows, (long long)out->k, (long long)R, (long long)K);
+  if (!aligned(x, 16) || !aligned(amax_in, 4) || !aligned(stats, 8) || !aligned(ws, 16))
+    return fail(SNIP_E_ALIGN, "snip_quantize: misaligned pointer");
+  if (!ws || ws_bytes < kQuantWS)
+    return fail(SNIP_E_WORKSPACE, "snip_quantize: workspace of %zu bytes needed", (size_t)kQuantWS);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  uint32_t* apart = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  StatPart* part = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+
+  QPlan p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.rows = rows;
+  p.cols = cols;
+  p.ld = ld;
+  p.layout = layout;
+  p.format = format;
+  p.sr = rounding == SNIP_SR;
+  p.seed = seed;
+  p.tensor_id = tensor_id;
+  p.amax_in = amax_in;
+  p.codes = static_cast<uint8_t*>(out->codes);
+  p.scales = static_cast<uint8_t*>(out->scales);
+  p.texp = has_texp(format) ? out->tensor_exp : nullptr;
+  p.part = part;
+  p.nwg = quant_wg(layout, format, rows, cols);
+  p.stats = stats;
+  if (needs_amax(format) && !amax_in) {
+    APlan a{p.x, rows, cols, ld, apart, amax_wg(rows, cols)};
+    int r = run_amax(&a, 1, s);
+    if (r) return r;
+    p.amax_part = apart;
+    p.n_amax_part = a.nwg;
+  }
+  const QPlan* grp[1] = {&p};
+  int r = run_quant_group(grp, 1, s);
+  if (r) return r;
+  if (stats) {
+    r = run_finalize(grp, 1, s);
+    if (r) return r;
+  }
+  return ok();
+}
+
+int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t ldc, void* ws,
+               size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = validate_qtensor(a, "snip_qgemm: a");
+  if (rc) return rc;
+  rc = validate_qtensor(b, "snip_qgemm: b");
+  if (rc) return rc;
+  if (!c) return fail(SNIP_E_NULL, "snip_qgemm: c is NULL");
+  if (a->format != b->format)
+    return fail(SNIP_E_FORMAT, "snip_qgemm: operand formats differ (%d, %d)", a->format, b->format);
+  if (a->k != b->k) return fail(SNIP_E_SHAPE, "snip_qgemm: K differs (%lld, %lld)", (long long)a->k,
+                                (long long)b->k);
+  if (a->k % 128) return fail(SNIP_E_SHAPE, "snip_qgemm: K=%lld not a multiple of 128", (long long)a->k);
+  if (ldc < b->rows) return fail(SNIP_E_SHAPE, "snip_qgemm: ldc=%lld < N=%lld", (long long)ldc,
+                                 (long long)b->rows);
+  if (!aligned(c, 16)) return fail(SNIP_E_ALIGN, "snip_qgemm: c must be 16-byte aligned");
+  GemmArgs g;
+  g.a = static_cast<const uint8_t*>(a->codes);
+  g.b = static_cast<const uint8_t*>(b->codes);
+  g.as = static_cast<const uint8_t*>(a->scales);
+  g.bs = static_cast<const uint8_t*>(b->scales);
+  g.ea = has_texp(a->format) ? a->tensor_exp : nullptr;
+  g.eb = has_texp(b->format) ? b->tensor_exp : nullptr;
+  g.c = c;
+  g.M = a->rows;
+  g.N = b->rows;
+  g.K = a->k;
+  g.ldc = ldc;
+  rc = hip_check(launch_gemm(a->format, g, static_cast<hipStream_t>(stream)), "gemm launch");
+  if (rc) return rc;
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// A quantized operand carved from the workspace.
+struct QBuf {
+  snip_qtensor t;
+};
+
+QBuf carve_q(Carver& cv, int f, int64_t rows, int64_t k) {
+  QBuf q;
+  q.t.format = f;
+  q.t.reserved = 0;
+  q.t.rows = rows;
+  q.t.k = k;
+  q.t.codes = cv.take((size_t)code_bytes(f, rows, k));
+  q.t.scales = has_scales(f) ? cv.take((size_t)scale_bytes(f, rows, k)) : nullptr;
+  q.t.tensor_exp = reinterpret_cast<int32_t*>(cv.take(4));
+  return q;
+}
+
+int gemm_q(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, hipStream_t s) {
+  GemmArgs g;
+  g.a = static_cast<const uint8_t*>(a.codes);
+  g.b = static_cast<const uint8_t*>(b.codes);
+  g.as = static_cast<const uint8_t*>(a.scales);
+  g.bs = static_cast<const uint8_t*>(b.scales);
+  g.ea = has_texp(a.format) ? a.tensor_exp : nullptr;
+  g.eb = has_texp(b.format) ? b.tensor_exp : nullptr;
+  g.c = c;
+  g.M = a.rows;
+  g.N = b.rows;
+  g.K = a.k;
+  g.ldc = ldc;
+  return hip_check(launch_gemm(a.format, g, s), "gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t out, int format,
+                    uint64_t seed, uint32_t layer_id, float* y, snip_stats* stats2, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!x || !w || !y) return fail(SNIP_E_NULL, "snip_linear_fwd: x, w and y must be non-NULL");
+  if (!valid_format(format)) return fail(SNIP_E_FORMAT, "snip_linear_fwd: unknown format %d", format);
+  if (T <= 0 || in <= 0 || out <= 0) return fail(SNIP_E_SHAPE, "snip_linear_fwd: dimensions must be > 0");
+  if (in % 128) return fail(SNIP_E_SHAPE, "snip_linear_fwd: in=%lld not a multiple of 128", (long long)in);
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(stats2, 8) || !aligned(ws, 16))
+    return fail(SNIP_E_ALIGN, "snip_linear_fwd: misaligned pointer");
+  const size_t need = snip_linear_fwd_workspace(T, in, out, format);
+  if (!ws || ws_bytes < need) return fail(SNIP_E_WORKSPACE, "snip_linear_fwd: workspace of %zu bytes needed", need);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* wsrc = static_cast<const uint16_t*>(w);
+  QPlan px{}, pw{};
+  uint32_t* apx = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  px.part = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+  uint32_t* apw = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  pw.part = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+  QBuf qx, qw;
+  const bool bf = format == SNIP_BF16;
+  if (!bf) {
+    qx = carve_q(cv, format, T, in);
+    qw = carve_q(cv, format, out, in);
+  }
+  auto fill = [&](QPlan& p, const uint16_t* src, int64_t rows, QBuf& q, uint32_t role) {
+    p.x = src;
+    p.rows = rows;
+    p.cols = in;
+    p.ld = in;
+    p.layout = SNIP_ROWWISE;
+    p.format = format;
+    p.sr = false;
+    p.seed = seed;
+    p.tensor_id = 8u * layer_id + role;
+    p.codes = bf ? nullptr : static_cast<uint8_t*>(q.t.codes);
+    p.scales = bf ? nullptr : static_cast<uint8_t*>(q.t.scales);
+    p.texp = bf ? nullptr : q.t.tensor_exp;
+    p.nwg = quant_wg(SNIP_ROWWISE, format, rows, in);
+  };
+  fill(px, xs, T, qx, 0);
+  fill(pw, wsrc, out, qw, 1);
+  px.stats = stats2 ? stats2 + 0 : nullptr;
+  pw.stats = stats2 ? stats2 + 1 : nullptr;
+  int r;
+  if (needs_amax(format)) {
+    APlan a[2] = {{xs, T, in, in, apx, amax_wg(T, in)}, {wsrc, out, in, in, apw, amax_wg(out, in)}};
+    r = run_amax(a, 2, s);
+    if (r) return r;
+    px.amax_part = apx;
+    px.n_amax_part = a[0].nwg;
+    pw.amax_part = apw;
+    pw.n_amax_part = a[1].nwg;
+  }
+  if (!bf || stats2) {           // bf16: statistics-only pass, the GEMM reads x and w
+    const QPlan* grp[2] = {&px, &pw};
+    r = run_quant_group(grp, 2, s);
+    if (r) return r;
+  }
+  if (bf) {
+    snip_qtensor ax{SNIP_BF16, 0, T, in, const_cast<void*>(x), nullptr, nullptr};
+    snip_qtensor aw{SNIP_BF16, 0, out, in, const_cast<void*>(w), nullptr, nullptr};
+    r = gemm_q(ax, aw, y, out, s);
+  } else {
+    r = gemm_q(qx.t, qw.t, y, out, s);
+  }
+  if (r) return r;
+  if (stats2) {
+    const QPlan* grp[2] = {&px, &pw};
+    r = run_finalize(grp, 2, s);
+    if (r) return r;
+  }
+  return ok();
+}
+
+int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int64_t in, int64_t out,
+                    int fmt_dgrad, int fmt_wgrad, uint64_t seed, uint32_t layer_id, float* dx, float* dw,
+                    snip_stats* stats4, void* ws, size_t ws_bytes, void* stream) {
+  if (!dy || !x || !w) return fail(SNIP_E_NULL, "snip_linear_bwd: dy, x and w must be non-NULL");
+  if (!valid_format(fmt_dgrad) || !valid_format(fmt_wgrad))
+    return fail(SNIP_E_FORMAT, "snip_linear_bwd: unknown format (%d, %d)", fmt_dgrad, fmt_wgrad);
+  if (T <= 0 || in <= 0 || out <= 0) return fail(SNIP_E_SHAPE, "snip_linear_bwd: dimensions must be > 0");
+  if (dx) {
+    if (out % 128) return fail(SNIP_E_SHAPE, "snip_linear_bwd: out=%lld not a multiple of 128 (dgrad K)", (long long)out);
+    if (in % 16) return fail(SNIP_E_SHAPE, "snip_linear_bwd: in=%lld not a multiple of 16", (long long)in);
+  }
+  if (dw) {
+    if (T % 128) return fail(SNIP_E_SHAPE, "snip_linear_bwd: T=%lld not a multiple of 128 (wgrad K)", (long long)T);
+    if (in % 16 || out % 16) return fail(SNIP_E_SHAPE, "snip_linear_bwd: in and out must be multiples of 16");
+  }
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w, 16) || !aligned(dx, 16) || !aligned(dw, 16) ||
+      !aligned(stats4, 8) || !aligned(ws, 16))
+    return fail(SNIP_E_ALIGN, "snip_linear_bwd: misaligned pointer");
+  const size_t need = snip_linear_bwd_workspace(T, in, out, fmt_dgrad, fmt_wgrad);
+  if (!ws || ws_bytes < need) return fail(SNIP_E_WORKSPACE, "snip_linear_bwd: workspace of %zu bytes needed", need);
+  if (!dx && !dw) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  const uint16_t* dys = static_cast<const uint16_t*>(dy);
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* wsrc = static_cast<const uint16_t*>(w);
+  uint32_t* ap_dy = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  uint32_t* ap_w = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  uint32_t* ap_x = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  QPlan p[4] = {};
+  for (int i = 0; i < 4; ++i) p[i].part = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+  // p[0]: dY row-wise [T][out]      (dgrad A)
+  // p[1]: W column-wise -> [in][out] (dgrad B)
+  // p[2]: dY column-wise -> [out][T] (wgrad A)
+  // p[3]: X column-wise -> [in][T]   (wgrad B)
+  const uint16_t* src[4] = {dys, wsrc, dys, xs};
+  const int64_t rows[4] = {T, out, T, T};
+  const int64_t cols[4] = {out, in, out, in};
+  const int lay[4] = {SNIP_ROWWISE, SNIP_COLWISE, SNIP_COLWISE, SNIP_COLWISE};
+  const int fmt[4] = {fmt_dgrad, fmt_dgrad, fmt_wgrad, fmt_wgrad};
+  const bool use[4] = {dx != nullptr, dx != nullptr, dw != nullptr, dw != nullptr};
+  QBuf q[4];
+  for (int i = 0; i < 4; ++i) {
+    const int64_t R = lay[i] == SNIP_ROWWISE ? rows[i] : cols[i];
+    const int64_t K = lay[i] == SNIP_ROWWISE ? cols[i] : rows[i];
+    // a bf16 row-wise operand is read in place; everything else is materialised
+    const bool in_place = fmt[i] == SNIP_BF16 && lay[i] == SNIP_ROWWISE;
+    if (use[i] && !in_place) {
+      q[i] = carve_q(cv, fmt[i], R, K);
+    } else {
+      q[i].t = snip_qtensor{fmt[i], 0, R, K, const_cast<uint16_t*>(src[i]), nullptr, nullptr};
+    }
+    p[i].x = src[i];
+    p[i].rows = rows[i];
+    p[i].cols = cols[i];
+    p[i].ld = cols[i];
+    p[i].layout = lay[i];
+    p[i].format = fmt[i];
+    p[i].sr = true;
+    p[i].seed = seed;
+    p[i].tensor_id = 8u * layer_id + 2u + (uint32_t)i;
+    p[i].codes = in_place ? nullptr : static_cast<uint8_t*>(q[i].t.codes);
+    p[i].scales = static_cast<uint8_t*>(q[i].t.scales);
+    p[i].texp = has_texp(fmt[i]) ? q[i].t.tensor_exp : nullptr;
+    p[i].nwg = quant_wg(lay[i], fmt[i], rows[i], cols[i]);
+    p[i].stats = stats4 ? stats4 + i : nullptr;
+  }
+  // amax passes: dY (shared by both of its quantizations), W, X
+  APlan a[3];
+  int na = 0;
+  const bool need_dy = (use[0] && needs_amax(fmt[0])) || (use[2] && needs_amax(fmt[2]));
+  const bool need_w = use[1] && needs_amax(fmt[1]);
+  const bool need_x = use[3] && needs_amax(fmt[3]);
+  if (need_dy) a[na++] = APlan{dys, T, out, out, ap_dy, amax_wg(T, out)};
+  if (need_w) a[na++] = APlan{wsrc, out, in, in, ap_w, amax_wg(out, in)};
+  if (need_x) a[na++] = APlan{xs, T, in, in, ap_x, amax_wg(T, in)};
+  int r = run_amax(a, na, s);
+  if (r) return r;
+  const int n_dy = need_dy ? amax_wg(T, out) : 0;
+  p[0].amax_part = ap_dy; p[0].n_amax_part = n_dy;
+  p[2].amax_part = ap_dy; p[2].n_amax_part = n_dy;
+  p[1].amax_part = ap_w; p[1].n_amax_part = need_w ? amax_wg(out, in) : 0;
+  p[3].amax_part = ap_x; p[3].n_amax_part = need_x ? amax_wg(T, in) : 0;
+
+  QPlan* todo[4];
+  int nt = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (!use[i]) continue;
+    const bool in_place = fmt[i] == SNIP_BF16 && lay[i] == SNIP_ROWWISE;
+    if (in_place && !stats4) continue;
+    todo[nt++] = &p[i];
+  }
+  r = run_quant_all(todo, nt, s);
+  if (r) return r;
+  if (dx) {
+    r = gemm_q(q[0].t, q[1].t, dx, in, s);       // [T][out] . ([in][out])^T
+    if (r) return r;
+  }
+  if (dw) {
+    r = gemm_q(q[2].t, q[3].t, dw, in, s);       // [out][T] . ([in][T])^T
+    if (r) return r;
+  }
+  if (stats4) {
+    const QPlan* fin[4];
+    int nf = 0;
+    for (int i = 0; i < 4; ++i)
+      if (use[i]) fin[nf++] = &p[i];
+    r = run_finalize(fin, nf, s);
+    if (r) return r;
+  }
+  return ok();
+}
+
+int snip_layer_stats(const snip_stats* dev_stats, int n, snip_tensor_report* host_out, void* stream) {
+  if (!dev_stats || !host_out) return fail(SNIP_E_NULL, "snip_layer_stats: NULL pointer");
+  if (n <= 0 || n > 4096) return fail(SNIP_E_SHAPE, "snip_layer_stats: n=%d out of range", n);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<snip_stats> tmp((size_t)n);
+  int r = hip_check(hipMemcpyAsync(tmp.data(), dev_stats, sizeof(snip_stats) * n, hipMemcpyDeviceToHost, s),
+                    "stats copy");
+  if (r) return r;
+  r = hip_check(hipStreamSynchronize(s), "stream sync");
+  if (r) return r;
+  bool nonfinite = false;
+  for (int i = 0; i < n; ++i) {
+    const snip_stats& st = tmp[i];
+    snip_tensor_report& o = host_out[i];
+    o.sum_err2 = st.sum_err2;
+    o.sum_x2 = st.sum_x2;
+    o.rel_mse = st.sum_x2 > 0 ? st.sum_err2 / st.sum_x2 : (st.sum_err2 == 0 ? 0.0 : INFINITY);
+    o.norm_ratio = st.sum_err2 > 0 ? std::sqrt(st.sum_x2) / std::sqrt(st.sum_err2) : INFINITY;
+    o.amax = st.amax;
+    o.n_nonfinite = st.n_nonfinite;
+    o.below_sqrt3 = st.sum_x2 < 3.0 * st.sum_err2 ? 1 : 0;
+    o.reserved = 0;
+    nonfinite = nonfinite || st.n_nonfinite > 0;
+  }
+  if (nonfinite) return fail(SNIP_E_NONFINITE, "snip_layer_stats: non-finite inputs counted");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal launch interface between the host API (api.hip) and the kernels
+// (quantize.hip, gemm.hip). Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/snip.h"
+
+namespace snip {
+
+constexpr int kMaxJobs = 4;       // tensors per multi-tensor launch
+constexpr int kAmaxWG = 512;      // max workgroups of one amax pass (per tensor)
+constexpr int kQuantWG = 2048;    // max workgroups of one quantize pass (per tensor)
+
+// One workgroup's partial statistics (already in the unscaled domain).
+struct StatPart {
+  double e2;           // sum of (Q(x) - x)^2 over finite elements
+  double x2;           // sum of x^2 over finite elements
+  uint32_t nf;         // non-finite count
+  uint32_t amax_bits;  // fp32 bits of max|x| (the tensor max, or this
+                       // workgroup's max for the unquantized copy)
+};
+
+// amax pre-pass over one bf16 tensor: per-workgroup max of the finite
+// |x| as bf16 magnitude bits.
+struct AJob {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  uint32_t* part;      // [nwg]
+  int32_t wg0, nwg;
+};
+struct AJobs {
+  AJob j[kMaxJobs];
+  int32_t n;
+};
+
+// One quantize pass (row-wise or column-wise) of one tensor.
+struct QJob {
+  const uint16_t* x;
+  int64_t rows, cols, ld;        // source bf16 [rows][cols], leading dim ld
+  uint8_t* codes;
+  uint8_t* scales;
+  int32_t* texp;                 // tensor exponent out (NVFP4/FP8) or null
+  const float* amax_in;          // delayed-scaling max or null
+  const uint32_t* amax_part;     // amax pre-pass partials (bf16 magnitude bits)
+  int32_t n_amax_part;
+  StatPart* part;                // [nwg]
+  uint64_t seed;
+  uint32_t tensor_id;
+  int32_t wg0, nwg;
+};
+struct QJobs {
+  QJob j[kMaxJobs];
+  int32_t n;
+};
+
+// Statistics finalisation of one tensor.
+struct FJob {
+  const StatPart* part;
+  int32_t nwg;
+  snip_stats* out;
+};
+struct FJobs {
+  FJob j[kMaxJobs * 2];
+  int32_t n;
+};
+
+// GEMM problem: C[M][N] = A[M][K] . B[N][K]^T * 2^(ea + eb).
+struct GemmArgs {
+  const uint8_t* a;        // codes (bf16 for BF16)
+  const uint8_t* b;
+  const uint8_t* as;       // block scales or null
+  const uint8_t* bs;
+  const int32_t* ea;       // tensor exponents or null
+  const int32_t* eb;
+  float* c;
+  int64_t M, N, K, ldc;
+};
+
+// Launchers (all asynchronous on `s`); they return the hipError_t of the launch.
+hipError_t launch_amax(const AJobs& jobs, int total_wg, hipStream_t s);
+hipError_t launch_quant_row(int format, bool sr, const QJobs& jobs, int total_wg, hipStream_t s);
+hipError_t launch_quant_col(int format, bool sr, const QJobs& jobs, int total_wg, hipStream_t s);
+hipError_t launch_bf16_copy(const QJobs& jobs, int total_wg, hipStream_t s);
+hipError_t launch_bf16_transpose(const QJobs& jobs, int total_wg, hipStream_t s);
+hipError_t launch_finalize(const FJobs& jobs, hipStream_t s);
+hipError_t launch_gemm(int format, const GemmArgs& g, hipStream_t s);
+
+// Work decomposition helpers shared by host and kernels.
+constexpr int kColTileRows = 256;   // column-wise quantizer: source rows per tile
+constexpr int kColTileCols = 128;   // source columns per tile (2 per lane)
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace snip

@@ -1,0 +1,689 @@
+// Quantizer kernels for gfx950: amax pre-pass, row-wise and column-wise
+// NVFP4 / FP8-E4M3 / MX-FP4 quantization with round-to-nearest-even or
+// Philox stochastic rounding, fused per-tensor statistics, bf16 copy /
+// transpose for the unquantized baseline, and statistics finalisation.
+//
+// "FP4 All the Way" summary, Outline: 16 E2M1 values share an E4M3 scale;
+// nearest rounding forward, stochastic rounding backward and in the update.
+// "SNIP", Abstract: activation and gradient statistics feed the precision
+// decision -- every quantize pass accumulates sum (Q(x)-x)^2, sum x^2 and
+// counts non-finite inputs, next to the tensor max.
+//
+// Work layout. Row-wise: one thread per 16-element block (32 for MX, 16
+// elements per thread for FP8); consecutive threads own consecutive blocks,
+// so the packed code stores of a wave are contiguous. Column-wise: a
+// workgroup owns a 256-row x 128-column source tile; each lane reads two
+// adjacent columns with dword loads (a wave covers 256 contiguous bytes of a
+// source row), quantizes 16-row (32 for MX) blocks down the columns, stages
+// the codes in LDS and writes each output row segment (128 bytes of codes)
+// with 8-byte stores. All kernels are HBM-bound scans.
+#include "device.h"
+#include "kernels.h"
+
+namespace snip {
+
+// ------------------------------------------------------------ common
+__device__ __forceinline__ int find_job(const int32_t* wg0, int n) {
+  int j = 0;
+  for (int i = 1; i < n; ++i)
+    if ((int)blockIdx.x >= wg0[i]) j = i;
+  return j;
+}
+
+// Largest finite |x| of a packed pair of bf16 (as magnitude bits).
+__device__ __forceinline__ uint32_t pair_max(uint32_t w, uint32_t m) {
+  uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+  lo = lo >= 0x7F80u ? 0u : lo;
+  hi = hi >= 0x7F80u ? 0u : hi;
+  m = lo > m ? lo : m;
+  return hi > m ? hi : m;
+}
+
+// Tensor exponent: smallest e with A * 2^-e <= limit, limit = 6*448 (NVFP4)
+// or 448 (FP8); 0 for A == 0.
+__device__ __forceinline__ int tensor_exp(float A, int format) {
+  if (!(A > 0.0f)) return 0;
+  int e1;
+  const float f = frexpf(A, &e1);   // A = f * 2^e1, f in [0.5, 1)
+  if (format == SNIP_NVFP4) return e1 - 12 + (f > 0.65625f ? 1 : 0);   // 2688 = 0.65625 * 2^12
+  if (format == SNIP_FP8_E4M3) return e1 - 9 + (f > 0.875f ? 1 : 0);   //  448 = 0.875 * 2^9
+  return 0;
+}
+
+// Workgroup reduction of the amax partials (or the delayed-scaling value).
+__device__ float wg_tensor_amax(const QJob& J, uint32_t* red) {
+  if (J.amax_in) return *J.amax_in;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < J.n_amax_part; i += blockDim.x) {
+    const uint32_t v = J.amax_part[i];
+    m = v > m ? v : m;
+  }
+  m = wave_max_u(m);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = red[w] > m ? red[w] : m;
+  __syncthreads();
+  return __uint_as_float(m << 16);
+}
+
+// Workgroup reduction of one thread's statistics into part[wg].
+__device__ void wg_store_stats(StatPart* part, double e2, double x2, uint32_t nf,
+                               uint32_t amax_bits, double* dred, uint32_t* ured) {
+  e2 = wave_sum(e2);
+  x2 = wave_sum(x2);
+  nf = wave_sum_u(nf);
+  amax_bits = wave_max_u(amax_bits);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    dred[2 * wave] = e2;
+    dred[2 * wave + 1] = x2;
+    ured[2 * wave] = nf;
+    ured[2 * wave + 1] = amax_bits;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    StatPart p{0.0, 0.0, 0u, 0u};
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      p.e2 += dred[2 * w];
+      p.x2 += dred[2 * w + 1];
+      p.nf += ured[2 * w];
+      p.amax_bits = ured[2 * w + 1] > p.amax_bits ? ured[2 * w + 1] : p.amax_bits;
+    }
+    *part = p;
+  }
+}
+
+// ------------------------------------------------------------ amax pass
+__global__ __launch_bounds__(256) void amax_kernel(AJobs jobs) {
+  int32_t wg0[kMaxJobs];
+  for (int i = 0; i < kMaxJobs; ++i) wg0[i] = jobs.j[i].wg0;
+  const int jn = find_job(wg0, jobs.n);
+  const AJob J = jobs.j[jn];
+  const int wg = blockIdx.x - J.wg0;
+  const int64_t cpr = J.cols >> 3;                    // 8-element chunks per row
+  const int64_t nchunk = J.rows * cpr;
+  const bool flat = J.ld == J.cols;
+  uint32_t m = 0;
+  for (int64_t c = (int64_t)wg * 256 + threadIdx.x; c < nchunk; c += (int64_t)J.nwg * 256) {
+    const int64_t off = flat ? c * 8 : (c / cpr) * J.ld + (c % cpr) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(J.x + off);
+    m = pair_max(v.x, m);
+    m = pair_max(v.y, m);
+    m = pair_max(v.z, m);
+    m = pair_max(v.w, m);
+  }
+  m = wave_max_u(m);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int w = 1; w < 4; ++w) r = red[w] > r ? red[w] : r;
+    J.part[wg] = r;
+  }
+}
+
+// ------------------------------------------------------------ block codecs
+// NVFP4: 16 raw values x -> 16 packed nibbles (lo: elements 0..7, hi: 8..15),
+// the E4M3 block scale and the block's stats in the tensor-scaled domain.
+template <bool SR>
+__device__ __forceinline__ void nvfp4_block(const float (&x)[16], int eS, const Words4& d0,
+                                            const Words4& d1, uint32_t& lo, uint32_t& hi,
+                                            uint32_t& sc, float& be2, float& bx2) {
+  float xs[16];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    xs[i] = ldexpf(x[i], -eS);
+    am = fmaxf(am, fabsf(xs[i]));
+  }
+  sc = e4m3_rne(am / 6.0f);
+  const float shat = e4m3_val(sc);
+  lo = 0u;
+  hi = 0u;
+  be2 = 0.0f;
+  bx2 = 0.0f;
+  if (sc != 0u) {
+    const float inv = 1.0f / shat;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float a = fabsf(xs[i] * inv);
+      uint32_t m;
+      if (SR) m = e2m1_sr(a, r16_of(i < 8 ? d0 : d1, i & 7));
+      else m = e2m1_rne(a);
+      const uint32_t code = m | ((__float_as_uint(x[i]) >> 28) & 8u);
+      if (i < 8) lo |= code << (4 * i);
+      else hi |= code << (4 * (i - 8));
+      const float err = e2m1_val(m) * shat - fabsf(xs[i]);
+      be2 = fmaf(err, err, be2);
+      bx2 = fmaf(xs[i], xs[i], bx2);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t code = (__float_as_uint(x[i]) >> 28) & 8u;
+      if (i < 8) lo |= code << (4 * i);
+      else hi |= code << (4 * (i - 8));
+      bx2 = fmaf(xs[i], xs[i], bx2);
+    }
+    be2 = bx2;
+  }
+}
+
+// FP8-E4M3: 16 raw values -> 16 code bytes (4 words), stats in the scaled domain.
+template <bool SR>
+__device__ __forceinline__ void fp8_chunk(const float (&x)[16], int eS, const Words4& d0,
+                                          const Words4& d1, uint32_t (&out)[4], float& be2,
+                                          float& bx2) {
+  be2 = 0.0f;
+  bx2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float r = ldexpf(x[i], -eS);
+    const float a = fabsf(r);
+    uint32_t m;
+    if (SR) m = e4m3_sr(a, r16_of(i < 8 ? d0 : d1, i & 7));
+    else m = e4m3_rne(a);
+    const uint32_t code = m | ((__float_as_uint(x[i]) >> 24) & 0x80u);
+    out[i >> 2] |= code << (8 * (i & 3));
+    const float err = e4m3_val(m) - a;
+    be2 = fmaf(err, err, be2);
+    bx2 = fmaf(r, r, bx2);
+  }
+}
+
+// MX-FP4: 32 raw values -> 32 nibbles (4 words), E8M0 scale; stats are
+// returned already scaled back (fp64) since the scale varies per block.
+template <bool SR>
+__device__ __forceinline__ void mx_block(const float (&x)[32], const Words4 (&d)[4],
+                                         uint32_t (&out)[4], uint32_t& sc, double& e2,
+                                         double& x2, float& bx2_scaled) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
+  int X;
+  if (am > 0.0f) {
+    const int e = (int)(__float_as_uint(am) >> 23);      // biased exponent (0: subnormal)
+    X = e - 129;                                          // floor(log2 am) - 2
+    X = X < -127 ? -127 : X;
+  } else {
+    X = -127;
+  }
+  sc = (uint32_t)(X + 127);
+  const float pw = exp2i(-X);                             // exact power of two
+  float be2 = 0.0f, bx2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = 0u;
+  if (am > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float r = x[i] * pw;
+      const float a = fabsf(r);
+      uint32_t m;
+      if (SR) m = e2m1_sr(a, r16_of(d[i >> 3], i & 7));
+      else m = e2m1_rne(a);
+      out[i >> 3] |= (m | ((__float_as_uint(x[i]) >> 28) & 8u)) << (4 * (i & 7));
+      const float err = e2m1_val(m) - a;
+      be2 = fmaf(err, err, be2);
+      bx2 = fmaf(r, r, bx2);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) out[i >> 3] |= ((__float_as_uint(x[i]) >> 28) & 8u) << (4 * (i & 7));
+  }
+  e2 = ldexp((double)be2, 2 * X);
+  x2 = ldexp((double)bx2, 2 * X);
+  bx2_scaled = bx2;
+}
+
+// Non-finite slow path: count the NaN / Inf inputs, and recompute the raw
+// sum of squares and the max over the finite elements (the codes of such a
+// block are unspecified).
+template <int N>
+__device__ __forceinline__ void nonfinite_stats(const float (&x)[N], uint32_t& nf, double& x2,
+                                             uint32_t& amax_bits) {
+  nf = 0u;
+  x2 = 0.0;
+  for (int i = 0; i < N; ++i) {
+    if (isfinite(x[i])) {
+      x2 += (double)x[i] * (double)x[i];
+      const uint32_t b = __float_as_uint(fabsf(x[i]));
+      amax_bits = b > amax_bits ? b : amax_bits;
+    } else {
+      ++nf;
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack16(const uint4& v0, const uint4& v1, float (&x)[16]) {
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+
+// ------------------------------------------------------------ row-wise
+// One thread item = one 16-element NVFP4 block, 16 FP8 elements, or one
+// 32-element MX block; item `it` covers output elements it*EPT .. +EPT.
+template <int FMT, bool SR>
+__global__ __launch_bounds__(256) void quant_row_kernel(QJobs jobs) {
+  int32_t wg0[kMaxJobs];
+  for (int i = 0; i < kMaxJobs; ++i) wg0[i] = jobs.j[i].wg0;
+  const QJob J = jobs.j[find_job(wg0, jobs.n)];
+  const int wg = blockIdx.x - J.wg0;
+  __shared__ uint32_t ured[8];
+  __shared__ double dred[8];
+
+  const float A = (FMT == SNIP_MXFP4) ? 0.0f : wg_tensor_amax(J, ured);
+  const int eS = tensor_exp(A, FMT);
+  if (wg == 0 && threadIdx.x == 0 && J.texp) *J.texp = eS;
+
+  constexpr int EPT = (FMT == SNIP_MXFP4) ? 32 : 16;
+  const int64_t tpr = J.cols / EPT;
+  const int64_t nitems = J.rows * tpr;
+  const bool flat = J.ld == J.cols;
+  double e2s = 0.0, x2s = 0.0;      // tensor-scaled domain (NVFP4, FP8)
+  double e2r = 0.0, x2r = 0.0;      // raw domain (MX, non-finite blocks)
+  uint32_t nf = 0u, amax_bits = 0u;
+
+  for (int64_t it = (int64_t)wg * 256 + threadIdx.x; it < nitems; it += (int64_t)J.nwg * 256) {
+    const int64_t off = flat ? it * EPT : (it / tpr) * J.ld + (it % tpr) * EPT;
+    const uint4* src = reinterpret_cast<const uint4*>(J.x + off);
+    const uint64_t g0 = (uint64_t)it * (EPT / 8);          // first Philox counter
+    if constexpr (FMT == SNIP_MXFP4) {
+      float x[32], h0[16], h1[16];
+      unpack16(src[0], src[1], h0);
+      unpack16(src[2], src[3], h1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = h0[i];
+        x[16 + i] = h1[i];
+      }
+      Words4 d[4];
+      if (SR) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) d[q] = draws8(J.seed, J.tensor_id, g0 + q);
+      }
+      uint32_t out[4], sc;
+      double be2, bx2;
+      float bx2f;
+      mx_block<SR>(x, d, out, sc, be2, bx2, bx2f);
+      if (!(bx2f <= 3.0e38f)) {
+        uint32_t bnf;
+        double rx2;
+        nonfinite_stats<32>(x, bnf, rx2, amax_bits);
+        nf += bnf;
+        x2r += rx2;
+      } else {
+        e2r += be2;
+        x2r += bx2;
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
+        amax_bits = __float_as_uint(am) > amax_bits ? __float_as_uint(am) : amax_bits;
+      }
+      *reinterpret_cast<uint4*>(J.codes + it * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+      J.scales[it] = (uint8_t)sc;
+    } else {
+      float x[16];
+      unpack16(src[0], src[1], x);
+      Words4 d0, d1;
+      if (SR) {
+        d0 = draws8(J.seed, J.tensor_id, g0);
+        d1 = draws8(J.seed, J.tensor_id, g0 + 1);
+      }
+      float be2, bx2;
+      if constexpr (FMT == SNIP_NVFP4) {
+        uint32_t lo, hi, sc;
+        nvfp4_block<SR>(x, eS, d0, d1, lo, hi, sc, be2, bx2);
+        *reinterpret_cast<uint2*>(J.codes + it * 8) = make_uint2(lo, hi);
+        J.scales[it] = (uint8_t)sc;
+      } else {
+        uint32_t out[4];
+        fp8_chunk<SR>(x, eS, d0, d1, out, be2, bx2);
+        *reinterpret_cast<uint4*>(J.codes + it * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+      }
+      if (!(bx2 <= 3.0e38f)) {
+        uint32_t bnf;
+        double rx2;
+        uint32_t dummy = 0u;
+        nonfinite_stats<16>(x, bnf, rx2, dummy);
+        nf += bnf;
+        x2r += rx2;
+      } else {
+        e2s += (double)be2;
+        x2s += (double)bx2;
+      }
+    }
+  }
+  if (FMT != SNIP_MXFP4) amax_bits = __float_as_uint(A);
+  const double e2 = ldexp(e2s, 2 * eS) + e2r;
+  const double x2 = ldexp(x2s, 2 * eS) + x2r;
+  wg_store_stats(J.part + wg, e2, x2, nf, amax_bits, dred, ured);
+}
+
+// ------------------------------------------------------------ column-wise
+// Source x[R][C] -> output [C][R] with blocks running down the source
+// columns. Tile: kColTileRows x kColTileCols; lane l owns columns c0+2l and
+// c0+2l+1, wave w owns the block rows w, w+4, ...
+template <int FMT, bool SR>
+__global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
+  int32_t wg0[kMaxJobs];
+  for (int i = 0; i < kMaxJobs; ++i) wg0[i] = jobs.j[i].wg0;
+  const QJob J = jobs.j[find_job(wg0, jobs.n)];
+  const int wg = blockIdx.x - J.wg0;
+  __shared__ uint32_t ured[8];
+  __shared__ double dred[8];
+
+  constexpr int BLK = (FMT == SNIP_MXFP4) ? 32 : 16;
+  constexpr int TR = kColTileRows, TC = kColTileCols;
+  constexpr int NB = TR / BLK;                                  // blocks per column per tile
+  constexpr int CB = (FMT == SNIP_NVFP4) ? 8 : 16;              // code bytes per block
+  constexpr int PITCH = NB * CB + 8;                            // LDS bytes per column
+  __shared__ __align__(16) uint8_t lcodes[TC * PITCH];
+  __shared__ uint8_t lsc[TC * NB];
+
+  const float A = (FMT == SNIP_MXFP4) ? 0.0f : wg_tensor_amax(J, ured);
+  const int eS = tensor_exp(A, FMT);
+  if (wg == 0 && threadIdx.x == 0 && J.texp) *J.texp = eS;
+
+  const int64_t R = J.rows, C = J.cols;
+  const int64_t rowbytes = R / BLK * CB;                        // output row length (codes)
+  const int64_t tiles_c = ceil_div(C, TC);
+  const int64_t ntiles = ceil_div(R, TR) * tiles_c;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double e2s = 0.0, x2s = 0.0, e2r = 0.0, x2r = 0.0;
+  uint32_t nf = 0u, amax_bits = 0u;
+
+  for (int64_t tile = wg; tile < ntiles; tile += J.nwg) {
+    const int64_t r0 = (tile / tiles_c) * TR;
+    const int64_t c0 = (tile % tiles_c) * TC;
+    const int nbt = (int)((R - r0) / BLK < NB ? (R - r0) / BLK : NB);
+    const int64_t col = c0 + 2 * lane;
+    if (col < C) {
+#pragma unroll 1
+      for (int t = 0; t < NB / 4; ++t) {
+        const int rb = wave + 4 * t;
+        if (rb >= nbt) break;
+        const uint16_t* src = J.x + (r0 + (int64_t)rb * BLK) * J.ld + col;
+        float xa[BLK], xb[BLK];
+#pragma unroll
+        for (int i = 0; i < BLK; ++i) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (int64_t)i * J.ld);
+          xa[i] = bf16_lo(w);
+          xb[i] = bf16_hi(w);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float(&x)[BLK] = h ? xb : xa;
+          const int cl = 2 * lane + h;
+          const uint64_t g0 = ((uint64_t)(col + h) * (uint64_t)R + (uint64_t)(r0 + rb * BLK)) >> 3;
+          uint8_t* dst = lcodes + cl * PITCH + rb * CB;
+          if constexpr (FMT == SNIP_MXFP4) {
+            Words4 d[4];
+            if (SR) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) d[q] = draws8(J.seed, J.tensor_id, g0 + q);
+            }
+            uint32_t out[4], sc;
+            double be2, bx2;
+            float bx2f;
+            mx_block<SR>(x, d, out, sc, be2, bx2, bx2f);
+            if (!(bx2f <= 3.0e38f)) {
+              uint32_t bnf;
+              double rx2;
+              nonfinite_stats<32>(x, bnf, rx2, amax_bits);
+              nf += bnf;
+              x2r += rx2;
+            } else {
+              e2r += be2;
+              x2r += bx2;
+              float am = 0.0f;
+#pragma unroll
+              for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
+              amax_bits = __float_as_uint(am) > amax_bits ? __float_as_uint(am) : amax_bits;
+            }
+            *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
+            *reinterpret_cast<uint2*>(dst + 8) = make_uint2(out[2], out[3]);
+            lsc[cl * NB + rb] = (uint8_t)sc;
+          } else {
+            Words4 d0, d1;
+            if (SR) {
+              d0 = draws8(J.seed, J.tensor_id, g0);
+              d1 = draws8(J.seed, J.tensor_id, g0 + 1);
+            }
+            float be2, bx2;
+            if constexpr (FMT == SNIP_NVFP4) {
+              uint32_t lo, hi, sc;
+              nvfp4_block<SR>(x, eS, d0, d1, lo, hi, sc, be2, bx2);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+              lsc[cl * NB + rb] = (uint8_t)sc;
+            } else {
+              uint32_t out[4];
+              fp8_chunk<SR>(x, eS, d0, d1, out, be2, bx2);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
+              *reinterpret_cast<uint2*>(dst + 8) = make_uint2(out[2], out[3]);
+            }
+            if (!(bx2 <= 3.0e38f)) {
+              uint32_t bnf, dummy = 0u;
+              double rx2;
+              nonfinite_stats<16>(x, bnf, rx2, dummy);
+              nf += bnf;
+              x2r += rx2;
+            } else {
+              e2s += (double)be2;
+              x2s += (double)bx2;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // write the tile's output row segments: nbt*CB bytes of codes per column
+    constexpr int CH = NB * CB / 8;                              // 8-byte chunks per column
+    const int valid_ch = nbt * CB / 8;
+    for (int q = threadIdx.x; q < TC * CH; q += 256) {
+      const int cl = q / CH, ch = q % CH;
+      if (ch < valid_ch && c0 + cl < C) {
+        *reinterpret_cast<uint2*>(J.codes + (c0 + cl) * rowbytes + r0 / BLK * CB + ch * 8) =
+            *reinterpret_cast<const uint2*>(lcodes + cl * PITCH + ch * 8);
+      }
+    }
+    if constexpr (FMT != SNIP_FP8_E4M3) {
+      for (int q = threadIdx.x; q < TC * NB; q += 256) {
+        const int cl = q / NB, b = q % NB;
+        if (b < nbt && c0 + cl < C) J.scales[(c0 + cl) * (R / BLK) + r0 / BLK + b] = lsc[cl * NB + b];
+      }
+    }
+    __syncthreads();
+  }
+  if (FMT != SNIP_MXFP4) amax_bits = __float_as_uint(A);
+  const double e2 = ldexp(e2s, 2 * eS) + e2r;
+  const double x2 = ldexp(x2s, 2 * eS) + x2r;
+  wg_store_stats(J.part + wg, e2, x2, nf, amax_bits, dred, ured);
+}
+
+// ------------------------------------------------------------ bf16 (unquantized)
+// Row-wise: copy x[rows][cols] (leading dim ld) to a contiguous buffer, or
+// only gather the statistics when no destination is given.
+__global__ __launch_bounds__(256) void bf16_copy_kernel(QJobs jobs) {
+  int32_t wg0[kMaxJobs];
+  for (int i = 0; i < kMaxJobs; ++i) wg0[i] = jobs.j[i].wg0;
+  const QJob J = jobs.j[find_job(wg0, jobs.n)];
+  const int wg = blockIdx.x - J.wg0;
+  __shared__ uint32_t ured[8];
+  __shared__ double dred[8];
+  const int64_t cpr = J.cols >> 3;
+  const int64_t nchunk = J.rows * cpr;
+  const bool flat = J.ld == J.cols;
+  double x2 = 0.0;
+  uint32_t nf = 0u, amax_bits = 0u;
+  for (int64_t c = (int64_t)wg * 256 + threadIdx.x; c < nchunk; c += (int64_t)J.nwg * 256) {
+    const int64_t off = flat ? c * 8 : (c / cpr) * J.ld + (c % cpr) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(J.x + off);
+    if (J.codes) *reinterpret_cast<uint4*>(J.codes + c * 16) = v;   // null: statistics only
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+      if (isfinite(a)) { s = fmaf(a, a, s); amax_bits = max(amax_bits, __float_as_uint(fabsf(a))); } else ++nf;
+      if (isfinite(b)) { s = fmaf(b, b, s); amax_bits = max(amax_bits, __float_as_uint(fabsf(b))); } else ++nf;
+    }
+    x2 += (double)s;
+  }
+  wg_store_stats(J.part + wg, 0.0, x2, nf, amax_bits, dred, ured);
+}
+
+// Column-wise: out[cols][rows] = x^T through 64x64 LDS tiles.
+__global__ __launch_bounds__(256) void bf16_transpose_kernel(QJobs jobs) {
+  int32_t wg0[kMaxJobs];
+  for (int i = 0; i < kMaxJobs; ++i) wg0[i] = jobs.j[i].wg0;
+  const QJob J = jobs.j[find_job(wg0, jobs.n)];
+  const int wg = blockIdx.x - J.wg0;
+  __shared__ uint32_t ured[8];
+  __shared__ double dred[8];
+  __shared__ uint16_t tileb[64][66];
+  const int64_t R = J.rows, C = J.cols;
+  const int64_t tiles_c = ceil_div(C, 64);
+  const int64_t ntiles = ceil_div(R, 64) * tiles_c;
+  const int tr = threadIdx.x >> 2, tq = (threadIdx.x & 3) * 16;
+  double x2 = 0.0;
+  uint32_t nf = 0u, amax_bits = 0u;
+  for (int64_t tile = wg; tile < ntiles; tile += J.nwg) {
+    const int64_t r0 = (tile / tiles_c) * 64, c0 = (tile % tiles_c) * 64;
+    // load: thread reads 16 consecutive elements of source row r0+tr
+    if (r0 + tr < R && c0 + tq < C) {
+      const uint4* s = reinterpret_cast<const uint4*>(J.x + (r0 + tr) * J.ld + c0 + tq);
+      const uint4 v0 = s[0], v1 = s[1];
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      float s2 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        tileb[tr][tq + 2 * i] = (uint16_t)(w[i] & 0xFFFFu);
+        tileb[tr][tq + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+        const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+        if (isfinite(a)) { s2 = fmaf(a, a, s2); amax_bits = max(amax_bits, __float_as_uint(fabsf(a))); } else ++nf;
+        if (isfinite(b)) { s2 = fmaf(b, b, s2); amax_bits = max(amax_bits, __float_as_uint(fabsf(b))); } else ++nf;
+      }
+      x2 += (double)s2;
+    }
+    __syncthreads();
+    // store: thread writes 16 consecutive elements of output row c0+tr
+    if (c0 + tr < C && r0 + tq < R) {
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[i] = (uint32_t)tileb[tq + 2 * i][tr] | ((uint32_t)tileb[tq + 2 * i + 1][tr] << 16);
+      uint4* d = reinterpret_cast<uint4*>(J.codes + ((c0 + tr) * R + r0 + tq) * 2);
+      d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+    __syncthreads();
+  }
+  wg_store_stats(J.part + wg, 0.0, x2, nf, amax_bits, dred, ured);
+}
+
+// ------------------------------------------------------------ finalisation
+// One workgroup per tensor: fixed-order sum of the partials.
+__global__ __launch_bounds__(256) void finalize_kernel(FJobs jobs) {
+  const FJob J = jobs.j[blockIdx.x];
+  double e2 = 0.0, x2 = 0.0;
+  uint32_t nf = 0u, am = 0u;
+  for (int i = threadIdx.x; i < J.nwg; i += 256) {
+    const StatPart p = J.part[i];
+    e2 += p.e2;
+    x2 += p.x2;
+    nf += p.nf;
+    am = p.amax_bits > am ? p.amax_bits : am;
+  }
+  __shared__ uint32_t ured[8];
+  __shared__ double dred[8];
+  e2 = wave_sum(e2);
+  x2 = wave_sum(x2);
+  nf = wave_sum_u(nf);
+  am = wave_max_u(am);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    dred[2 * wave] = e2;
+    dred[2 * wave + 1] = x2;
+    ured[2 * wave] = nf;
+    ured[2 * wave + 1] = am;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    snip_stats s{0.0, 0.0, 0.0f, 0u};
+    uint32_t m = 0u;
+    for (int w = 0; w < 4; ++w) {
+      s.sum_err2 += dred[2 * w];
+      s.sum_x2 += dred[2 * w + 1];
+      s.n_nonfinite += ured[2 * w];
+      m = ured[2 * w + 1] > m ? ured[2 * w + 1] : m;
+    }
+    s.amax = __uint_as_float(m);
+    *J.out = s;
+  }
+}
+
+// ------------------------------------------------------------ launchers
+hipError_t launch_amax(const AJobs& jobs, int total_wg, hipStream_t s) {
+  hipLaunchKernelGGL(amax_kernel, dim3(total_wg), dim3(256), 0, s, jobs);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t quant_row_fmt(bool sr, const QJobs& jobs, int total_wg, hipStream_t s) {
+  if (sr) hipLaunchKernelGGL((quant_row_kernel<FMT, true>), dim3(total_wg), dim3(256), 0, s, jobs);
+  else hipLaunchKernelGGL((quant_row_kernel<FMT, false>), dim3(total_wg), dim3(256), 0, s, jobs);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t quant_col_fmt(bool sr, const QJobs& jobs, int total_wg, hipStream_t s) {
+  if (sr) hipLaunchKernelGGL((quant_col_kernel<FMT, true>), dim3(total_wg), dim3(256), 0, s, jobs);
+  else hipLaunchKernelGGL((quant_col_kernel<FMT, false>), dim3(total_wg), dim3(256), 0, s, jobs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_row(int format, bool sr, const QJobs& jobs, int total_wg, hipStream_t s) {
+  switch (format) {
+    case SNIP_NVFP4: return quant_row_fmt<SNIP_NVFP4>(sr, jobs, total_wg, s);
+    case SNIP_FP8_E4M3: return quant_row_fmt<SNIP_FP8_E4M3>(sr, jobs, total_wg, s);
+    case SNIP_MXFP4: return quant_row_fmt<SNIP_MXFP4>(sr, jobs, total_wg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_quant_col(int format, bool sr, const QJobs& jobs, int total_wg, hipStream_t s) {
+  switch (format) {
+    case SNIP_NVFP4: return quant_col_fmt<SNIP_NVFP4>(sr, jobs, total_wg, s);
+    case SNIP_FP8_E4M3: return quant_col_fmt<SNIP_FP8_E4M3>(sr, jobs, total_wg, s);
+    case SNIP_MXFP4: return quant_col_fmt<SNIP_MXFP4>(sr, jobs, total_wg, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bf16_copy(const QJobs& jobs, int total_wg, hipStream_t s) {
+  hipLaunchKernelGGL(bf16_copy_kernel, dim3(total_wg), dim3(256), 0, s, jobs);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_transpose(const QJobs& jobs, int total_wg, hipStream_t s) {
+  hipLaunchKernelGGL(bf16_transpose_kernel, dim3(total_wg), dim3(256), 0, s, jobs);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FJobs& jobs, hipStream_t s) {
+  if (jobs.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3(jobs.n), dim3(256), 0, s, jobs);
+  return hipGetLastError();
+}
+
+}  // namespace snip

@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/snip.h declares, sizes buffers, and rejects bad arguments with the
+documented status codes before any HIP call (so these calls are safe on a
+machine without a GPU: the fake device addresses below are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sub_byte_mixed_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "snip.h")
+
+# fake, 256-byte-aligned device addresses: validation must reject before use
+P = 0x7F0000000000
+P2 = P + 0x100000
+P3 = P + 0x200000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(S.LIB_PATH):
+        from sub_byte_mixed_amd import build
+        build.build()
+    return S.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(snip_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(L, n), n
+    # and nothing else is exported under the snip_ prefix
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r"\bT (snip_[a-z0-9_]+)", out)))
+    assert exported == names
+
+
+def test_version_and_sizes(L):
+    assert L.snip_version() == 100
+    assert L.snip_qtensor_bytes(S.NVFP4, 4, 32, 0) == 64
+    assert L.snip_qtensor_bytes(S.NVFP4, 4, 32, 1) == 8
+    assert L.snip_qtensor_bytes(S.MXFP4, 4, 64, 1) == 8
+    assert L.snip_qtensor_bytes(S.FP8, 4, 32, 0) == 128
+    assert L.snip_qtensor_bytes(S.FP8, 4, 32, 1) == 0
+    assert L.snip_qtensor_bytes(S.BF16, 4, 32, 0) == 256
+    assert L.snip_qtensor_bytes(S.MXFP4, 4, 48, 0) == -1       # k % 32
+    assert L.snip_qtensor_bytes(9, 4, 32, 0) == -1
+    assert L.snip_quantize_workspace(16, 16, S.ROWWISE, S.NVFP4) > 0
+    assert L.snip_quantize_workspace(0, 16, S.ROWWISE, S.NVFP4) == 0
+    f = L.snip_linear_fwd_workspace(256, 512, 512, S.NVFP4)
+    # quantized X and W: codes + scales at least
+    assert f >= 256 * 512 // 2 + 256 * 512 // 16 + 512 * 512 // 2 + 512 * 512 // 16
+    b = L.snip_linear_bwd_workspace(256, 512, 512, S.NVFP4, S.FP8)
+    assert b >= 2 * (256 * 512 // 2) + 2 * 256 * 512
+    assert L.snip_linear_bwd_workspace(256, 512, 512, 7, S.FP8) == 0
+
+
+def qdesc(fmt, rows, k, codes=P2, scales=P3, texp=P3 + 0x1000):
+    return S.QTensorDesc(fmt, 0, rows, k, codes, scales, texp)
+
+
+def err(L):
+    return L.snip_last_error().decode()
+
+
+def quant(L, x=P, rows=64, cols=64, ld=64, layout=0, fmt=S.NVFP4, rnd=0, out=None, ws=P + 0x400000,
+          ws_bytes=1 << 20, amax=None, stats=None):
+    if out is None:
+        R, K = (rows, cols) if layout == 0 else (cols, rows)
+        out = qdesc(fmt, R, K)
+    return L.snip_quantize(x, rows, cols, ld, layout, fmt, rnd, 0, 0, amax, ctypes.byref(out), stats,
+                           ws, ws_bytes, None)
+
+
+def test_quantize_validation(L):
+    assert quant(L, x=None) == -1 and "x is NULL" in err(L)
+    assert quant(L, fmt=7) == -4
+    assert quant(L, rnd=3) == -4
+    assert quant(L, layout=2) == -4
+    assert quant(L, cols=40, ld=40) == -2                       # cols % 16
+    assert quant(L, ld=60) == -2                                # ld < cols
+    assert quant(L, rows=0) == -2
+    assert quant(L, layout=1, rows=40) == -2                    # K = rows % 16
+    assert quant(L, fmt=S.MXFP4, cols=48, ld=48) == -2          # MX K % 32
+    assert quant(L, out=qdesc(S.FP8, 64, 64)) == -4             # format mismatch
+    assert quant(L, out=qdesc(S.NVFP4, 64, 32)) == -2           # shape mismatch
+    assert quant(L, layout=1, rows=64, cols=32, ld=32, out=qdesc(S.NVFP4, 64, 32)) == -2
+    assert quant(L, out=qdesc(S.NVFP4, 64, 64, scales=None)) == -1
+    assert quant(L, out=qdesc(S.NVFP4, 64, 64, texp=None)) == -1
+    assert quant(L, x=P + 2) == -3
+    assert quant(L, out=qdesc(S.NVFP4, 64, 64, codes=P2 + 8)) == -3
+    assert quant(L, ws=None) == -5
+    assert quant(L, ws_bytes=1024) == -5 and "workspace" in err(L)
+
+
+def test_qgemm_validation(L):
+    a, b = qdesc(S.NVFP4, 64, 256), qdesc(S.NVFP4, 32, 256)
+    c = P + 0x800000
+    assert L.snip_qgemm(None, ctypes.byref(b), c, 32, None, 0, None) == -1
+    assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(b), None, 32, None, 0, None) == -1
+    b8 = qdesc(S.FP8, 32, 256, scales=None)
+    assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(b8), c, 32, None, 0, None) == -4
+    bk = qdesc(S.NVFP4, 32, 128)
+    assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(bk), c, 32, None, 0, None) == -2
+    a96, b96 = qdesc(S.NVFP4, 64, 96), qdesc(S.NVFP4, 32, 96)
+    assert L.snip_qgemm(ctypes.byref(a96), ctypes.byref(b96), c, 32, None, 0, None) == -2
+    assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(b), c, 16, None, 0, None) == -2   # ldc < N
+    assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(b), c + 4, 32, None, 0, None) == -3
+    bad = qdesc(5, 32, 256)
+    assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(bad), c, 32, None, 0, None) == -4
+
+
+def test_linear_validation(L):
+    ws, y = P + 0x1000000, P + 0x2000000
+    assert L.snip_linear_fwd(None, P2, 64, 128, 64, S.NVFP4, 0, 0, y, None, ws, 1 << 30, None) == -1
+    assert L.snip_linear_fwd(P, P2, 64, 96, 64, S.NVFP4, 0, 0, y, None, ws, 1 << 30, None) == -2
+    assert L.snip_linear_fwd(P, P2, 64, 128, 64, 11, 0, 0, y, None, ws, 1 << 30, None) == -4
+    assert L.snip_linear_fwd(P, P2, 64, 128, 64, S.NVFP4, 0, 0, y, None, ws, 100, None) == -5
+    assert L.snip_linear_fwd(P, P2 + 1, 64, 128, 64, S.NVFP4, 0, 0, y, None, ws, 1 << 30, None) == -3
+    # backward: dgrad needs out % 128, wgrad needs T % 128
+    dx, dw = P + 0x3000000, P + 0x4000000
+    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 96, S.NVFP4, S.NVFP4, 0, 0, dx, None, None, ws,
+                             1 << 30, None) == -2
+    assert L.snip_linear_bwd(P, P2, P3, 96, 64, 128, S.NVFP4, S.NVFP4, 0, 0, None, dw, None, ws,
+                             1 << 30, None) == -2
+    assert L.snip_linear_bwd(P, None, P3, 128, 64, 128, S.NVFP4, S.NVFP4, 0, 0, dx, dw, None, ws,
+                             1 << 30, None) == -1
+    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 128, S.NVFP4, 9, 0, 0, dx, dw, None, ws,
+                             1 << 30, None) == -4
+    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 128, S.NVFP4, S.FP8, 0, 0, dx, dw, None, ws,
+                             64, None) == -5
+
+
+def test_layer_stats_validation(L):
+    rep = (S.TensorReport * 2)()
+    assert L.snip_layer_stats(None, 2, rep, None) == -1
+    assert L.snip_layer_stats(P, 0, rep, None) == -2
+    assert L.snip_layer_stats(P, 2, None, None) == -1
+
+
+def test_binding_requires_gpu_tensors():
+    import torch
+    x = torch.zeros((16, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        S.quantize(x, S.ROWWISE, S.NVFP4)

@@ -1,0 +1,69 @@
+"""GPU parity: the block-scaled MFMA GEMMs against the oracle's fp64 product
+of the dequantized operands, within 1e-5 * sum_k |a_k||b_k| per element.
+
+The operands are quantized by the oracle and uploaded, so this isolates the
+GEMM from the GPU quantizers; shapes span several 128x128 output tiles and
+ragged M / N tails."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import sub_byte_mixed_amd as S
+from parity import check_gemm, oracle_quant, say, upload_oracle_q
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(128, 128, 128), (200, 72, 256), (16, 16, 128), (384, 256, 512), (1, 1, 128),
+          (257, 129, 384), (64, 520, 1024)]
+
+
+def run(fmt, M, N, K, seed, dist="normal", rnd_b=S.SR):
+    say(f"gemm case fmt={fmt} M={M} N={N} K={K} seed={seed} dist={dist}")
+    a = synth.gen_matrix((M, K), seed=seed, dist=dist)
+    b = synth.gen_matrix((N, K), seed=seed + 1000, std=0.02, dist=dist)
+    oa = oracle_quant(a, S.ROWWISE, fmt, S.RNE, 0, 0)
+    ob = oracle_quant(b, S.ROWWISE, fmt, rnd_b, 1, 1)
+    qa, qb = upload_oracle_q(oa, fmt), upload_oracle_q(ob, fmt)
+    c = S.qgemm(qa, qb)
+    torch.cuda.synchronize()
+    return check_gemm(c.cpu().numpy().astype(np.float64), oa["xhat"], ob["xhat"],
+                      what=f"fmt={fmt} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", [S.NVFP4, S.FP8, S.MXFP4, S.BF16])
+def test_gemm_parity(fmt):
+    for i, (M, N, K) in enumerate(SHAPES):
+        run(fmt, M, N, K, seed=100 + i)
+
+
+@pytest.mark.parametrize("fmt", [S.NVFP4, S.FP8, S.MXFP4])
+def test_gemm_wide_range(fmt):
+    run(fmt, 128, 96, 256, seed=7, dist="lognormal_mixed")
+    run(fmt, 96, 128, 384, seed=8, dist="student_t")
+
+
+def test_gemm_tensor_scale_epilogue():
+    # tensors whose tensor exponents are far from 0 in both directions
+    for fmt in (S.NVFP4, S.FP8):
+        a = synth.gen_matrix((64, 256), seed=1, std=3e4)
+        b = synth.gen_matrix((48, 256), seed=2, std=1e-6)
+        oa = oracle_quant(a, S.ROWWISE, fmt, S.RNE)
+        ob = oracle_quant(b, S.ROWWISE, fmt, S.SR, 3, 3)
+        assert oa["texp"] > 0 and ob["texp"] < -20
+        c = S.qgemm(upload_oracle_q(oa, fmt), upload_oracle_q(ob, fmt))
+        torch.cuda.synchronize()
+        check_gemm(c.cpu().numpy().astype(np.float64), oa["xhat"], ob["xhat"], what=f"epilogue fmt={fmt}")
+
+
+def test_gemm_ldc_and_overwrite():
+    fmt = S.NVFP4
+    a = synth.gen_matrix((64, 128), seed=3)
+    b = synth.gen_matrix((40, 128), seed=4)
+    oa, ob = oracle_quant(a, S.ROWWISE, fmt, S.RNE), oracle_quant(b, S.ROWWISE, fmt, S.RNE)
+    big = torch.full((64, 64), 7.0, dtype=torch.float32, device="cuda")
+    S.qgemm(upload_oracle_q(oa, fmt), upload_oracle_q(ob, fmt), out=big[:, :40])
+    torch.cuda.synchronize()
+    h = big.cpu().numpy()
+    assert np.all(h[:, 40:] == 7.0)                          # untouched beyond N
+    check_gemm(h[:, :40].astype(np.float64), oa["xhat"], ob["xhat"], what="ldc")

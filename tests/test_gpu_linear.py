@@ -1,0 +1,98 @@
+"""GPU parity of the quantized linear layer (forward RTN, backward SR) against
+the oracle: every element of Y, dX and dW within 1e-5 * sum|a||b|, the
+statistics of each quantized operand within 1e-5, on the 512x512 layer
+(T = 256) workload and on ragged shapes in every format combination."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import sub_byte_mixed_amd as S
+from oracle import linear as OL
+from parity import TOL, check_gemm, compare_stats, f32, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_layer(x, w, dy, fmt_f, fmt_d, fmt_w, seed=0, layer_id=0):
+    say(f"linear case T={x.shape[0]} in={x.shape[1]} out={w.shape[0]} fmts=({fmt_f},{fmt_d},{fmt_w}) "
+        f"seed={seed} layer={layer_id}")
+    xd, wd, dyd = x.cuda(), w.cuda(), dy.cuda()
+    y, st_f = S.linear_fwd(xd, wd, fmt_f, seed, layer_id)
+    dx, dw, st_b = S.linear_bwd(dyd, xd, wd, fmt_d, fmt_w, seed, layer_id)
+    torch.cuda.synchronize()
+    x32, w32, dy32 = f32(x), f32(w), f32(dy)
+    of = OL.linear_fwd(x32, w32, fmt_f, seed, layer_id)
+    ob = OL.linear_bwd(dy32, x32, w32, fmt_d, fmt_w, seed, layer_id)
+    check_gemm(y.cpu().numpy().astype(np.float64), of["qx"]["xhat"], of["qw"]["xhat"], what="Y")
+    qdy, qwt, qdyt, qxt = ob["q"]
+    check_gemm(dx.cpu().numpy().astype(np.float64), qdy["xhat"], qwt["xhat"], what="dX")
+    check_gemm(dw.cpu().numpy().astype(np.float64), qdyt["xhat"], qxt["xhat"], what="dW")
+    gf = S.decode_stats(st_f)
+    gb = S.decode_stats(st_b)
+    for i, n in enumerate(["X", "W"]):
+        compare_stats(gf[i], of["stats"][i], what=f"fwd stats {n}")
+    for i, n in enumerate(["dY", "W^T", "dY^T", "X^T"]):
+        compare_stats(gb[i], ob["stats"][i], what=f"bwd stats {n}")
+    return y, dx, dw, gf, gb
+
+
+def test_linear512_workload_nvfp4():
+    wl = synth.WORKLOADS["linear512"]
+    x, w, dy = synth.gen_layer(wl, 0)
+    run_layer(x, w, dy, S.NVFP4, S.NVFP4, S.NVFP4, seed=0, layer_id=0)
+
+
+@pytest.mark.parametrize("fmts", [(S.FP8, S.FP8, S.FP8), (S.MXFP4, S.MXFP4, S.MXFP4),
+                                  (S.BF16, S.BF16, S.BF16), (S.NVFP4, S.FP8, S.NVFP4),
+                                  (S.FP8, S.NVFP4, S.MXFP4), (S.BF16, S.NVFP4, S.BF16)])
+def test_linear_formats_ragged(fmts):
+    T, din, dout = 384, 256, 256
+    x = synth.gen_matrix((T, din), seed=1)
+    w = synth.gen_matrix((dout, din), seed=2, std=0.02)
+    dy = synth.gen_matrix((T, dout), seed=3, std=1e-3)
+    run_layer(x, w, dy, *fmts, seed=5, layer_id=3)
+
+
+def test_linear_ragged_out_and_skips():
+    # forward with out not a multiple of the tile; backward with dx only / dw only
+    T, din, dout = 256, 384, 144
+    x = synth.gen_matrix((T, din), seed=4)
+    w = synth.gen_matrix((dout, din), seed=5, std=0.02)
+    y, st = S.linear_fwd(x.cuda(), w.cuda(), S.NVFP4, 0, 1)
+    torch.cuda.synchronize()
+    of = OL.linear_fwd(f32(x), f32(w), S.NVFP4, 0, 1)
+    check_gemm(y.cpu().numpy().astype(np.float64), of["qx"]["xhat"], of["qw"]["xhat"], what="Y ragged")
+    dout = 256
+    w = synth.gen_matrix((dout, din), seed=6, std=0.02)
+    dy = synth.gen_matrix((T, dout), seed=7, std=1e-3)
+    dx, dw, st = S.linear_bwd(dy.cuda(), x.cuda(), w.cuda(), S.NVFP4, S.NVFP4, 2, 4,
+                              need_dx=True, need_dw=False)
+    torch.cuda.synchronize()
+    assert dw is None
+    ob = OL.linear_bwd(f32(dy), f32(x), f32(w), S.NVFP4, S.NVFP4, 2, 4)
+    check_gemm(dx.cpu().numpy().astype(np.float64), ob["q"][0]["xhat"], ob["q"][1]["xhat"], what="dX only")
+    dx, dw, st = S.linear_bwd(dy.cuda(), x.cuda(), w.cuda(), S.NVFP4, S.NVFP4, 2, 4,
+                              need_dx=False, need_dw=True)
+    torch.cuda.synchronize()
+    assert dx is None
+    check_gemm(dw.cpu().numpy().astype(np.float64), ob["q"][2]["xhat"], ob["q"][3]["xhat"], what="dW only")
+
+
+def test_layer_stats_report():
+    wl = synth.WORKLOADS["linear512"]
+    x, w, dy = synth.gen_layer(wl, 0)
+    _, _, st = S.linear_bwd(dy.cuda(), x.cuda(), w.cuda(), S.NVFP4, S.NVFP4, 0, 0)
+    reps, nonfinite = S.layer_stats(st)
+    assert not nonfinite
+    raw = S.decode_stats(st)
+    for r, s in zip(reps, raw):
+        assert r["rel_mse"] == pytest.approx(s["sum_err2"] / s["sum_x2"], rel=1e-12)
+        assert r["below_sqrt3"] == int(s["sum_x2"] < 3 * s["sum_err2"])
+    # NVFP4 noise is well below the gradient norm for Gaussian dY
+    assert reps[0]["below_sqrt3"] == 0
+    bad = dy.clone()
+    bad[0, 0] = float("nan")
+    _, _, st = S.linear_bwd(bad.cuda(), x.cuda(), w.cuda(), S.NVFP4, S.NVFP4, 0, 0)
+    reps, nonfinite = S.layer_stats(st)
+    assert nonfinite and reps[0]["n_nonfinite"] == 1
