@@ -90,7 +90,7 @@ def main():
         for li, d in enumerate(layers):
             S.linear_fwd(d["x"], d["w"], d["fmt"], seed, li, y=d["y"], stats=d["st_f"], ws=d["ws_f"])
             S.linear_bwd(d["dy"], d["x"], d["w"], d["fmt"], d["fmt"], seed, li, dx=d["dx"], dw=d["dw"],
-                         stats=d["st_b"], ws=d["ws_b"])
+                         stats=d["st_b"], ws=d["ws_b"], fwd_stats=d["st_f"])
 
     gemm_flops = sum(3 * 2 * T * d["din"] * d["dout"] for d in layers)
 

@@ -207,6 +207,9 @@ int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t
  *   in % 16 == 0, out % 16 == 0 when dw is computed.
  *   tensor ids 8*layer_id + {2: dY row-wise, 3: W column-wise,
  *              4: dY column-wise, 5: X column-wise}.
+ *   fwd_stats2 device snip_stats[2] = {X, W} written by snip_linear_fwd on the
+ *              same x and w, or NULL. When given, their amax fields serve as
+ *              max|x| and max|w| and the two tensors are not re-read for it.
  *   dx, dw     device fp32 or NULL (NULL skips that GEMM and its operands).
  *   stats4     device snip_stats[4] = {dY, W^T, dY^T, X^T} or NULL
  *              (entries of a skipped GEMM are left untouched).
@@ -215,7 +218,7 @@ int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t
 int snip_linear_bwd(const void* dy, const void* x, const void* w,
                     int64_t T, int64_t in, int64_t out,
                     int fmt_dgrad, int fmt_wgrad, uint64_t seed, uint32_t layer_id,
-                    float* dx, float* dw, snip_stats* stats4,
+                    const snip_stats* fwd_stats2, float* dx, float* dw, snip_stats* stats4,
                     void* ws, size_t ws_bytes, void* stream);
 
 /* Synchronise `stream`, copy n device statistics records to the host and

@@ -73,7 +73,7 @@ _SIGS = {
                                    _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "snip_linear_bwd": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64,
                                    _c.c_int64, _c.c_int, _c.c_int, _c.c_uint64, _c.c_uint32,
-                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                   _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                    _c.c_size_t, _c.c_void_p]),
     "snip_layer_stats": (_c.c_int, [_c.c_void_p, _c.c_int, _c.POINTER(TensorReport), _c.c_void_p]),
     "snip_quantize_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
@@ -226,9 +226,11 @@ def linear_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, fmt_dgrad: in
                seed: int = 0, layer_id: int = 0, need_dx: bool = True, need_dw: bool = True,
                dx: Optional[torch.Tensor] = None, dw: Optional[torch.Tensor] = None,
                stats: Optional[torch.Tensor] = None, with_stats: bool = True,
-               ws: Optional[torch.Tensor] = None, stream=None):
+               ws: Optional[torch.Tensor] = None, fwd_stats: Optional[torch.Tensor] = None,
+               stream=None):
     """snip_linear_bwd: dx [T, in] = Q_sr(dy) . Q_sr(w^T)^T, dw [out, in] =
-    Q_sr(dy^T) . Q_sr(x^T)^T."""
+    Q_sr(dy^T) . Q_sr(x^T)^T. fwd_stats: the stats of linear_fwd on the same
+    x and w, whose max|x| and max|w| are then reused."""
     for t, n in ((dy, "dy"), (x, "x"), (w, "w")):
         _require_cuda_bf16(t, n)
     L = lib()
@@ -243,8 +245,9 @@ def linear_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, fmt_dgrad: in
     if ws is None:
         ws = _workspace(L.snip_linear_bwd_workspace(T, din, dout, fmt_dgrad, fmt_wgrad), x.device)
     _check(L.snip_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), T, din, dout, fmt_dgrad, fmt_wgrad, seed,
-                             layer_id, _ptr(dx) if need_dx else None, _ptr(dw) if need_dw else None,
-                             _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)))
+                             layer_id, _ptr(fwd_stats), _ptr(dx) if need_dx else None,
+                             _ptr(dw) if need_dw else None, _ptr(stats), _ptr(ws), ws.numel(),
+                             _stream(stream)))
     return dx, dw, stats
 
 

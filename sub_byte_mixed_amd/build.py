@@ -32,6 +32,25 @@ def hipcc_path() -> str:
     return p
 
 
+REPO = os.path.dirname(HERE)
+CHECKER_SRC = os.path.join(REPO, "tests", "helpers", "hw_convert_check.hip")
+CHECKER_BIN = os.path.join(REPO, "tests", "helpers", "hw_convert_check")
+
+
+def build_checker(verbose: bool = False) -> str:
+    """The exhaustive hardware-convert checker used by the GPU tests."""
+    cmd = [hipcc_path(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], "-o",
+           CHECKER_BIN + ".tmp", CHECKER_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed:\n{errs}")
+    os.replace(CHECKER_BIN + ".tmp", CHECKER_BIN)
+    return CHECKER_BIN
+
+
 def build(verbose: bool = False) -> str:
     out_tmp = LIB + ".tmp"
     cmd = [hipcc_path(), *HIPCC_FLAGS, "-o", out_tmp] + [os.path.join(CSRC, s) for s in SOURCES]
@@ -47,3 +66,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if os.path.exists(CHECKER_SRC):
+        print(build_checker(verbose="-v" in sys.argv))

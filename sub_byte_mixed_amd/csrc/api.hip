@@ -6,6 +6,7 @@
 // two backward GEMMs of a linear layer, each in the layer's plan format) and
 // "FP4 All the Way" summary, Outline (round-to-nearest forward operands,
 // stochastic rounding for back-propagation and update operands).
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -95,7 +96,7 @@ int quant_wg(int layout, int f, int64_t rows, int64_t cols) {
   if (f == SNIP_BF16) {
     wg = layout == SNIP_ROWWISE ? ceil_div(rows * cols / 8, 256 * 2) : ceil_div(rows, 64) * ceil_div(cols, 64);
   } else if (layout == SNIP_ROWWISE) {
-    wg = ceil_div(rows * cols / (f == SNIP_MXFP4 ? 32 : 16), 256);
+    wg = ceil_div(rows * cols / (f == SNIP_MXFP4 ? 32 : 16), 512);     // two items per thread
   } else {
     wg = ceil_div(rows, kColTileRows) * ceil_div(cols, kColTileCols);
   }
@@ -265,20 +266,23 @@ size_t snip_quantize_workspace(int64_t rows, int64_t cols, int layout, int forma
 }
 
 size_t snip_qgemm_workspace(int64_t M, int64_t N, int64_t K, int format) {
-  (void)M; (void)N; (void)K; (void)format;
-  return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || !valid_format(format)) return 0;
+  return gemm_partial_bytes(format, M, N, K);
 }
 
 size_t snip_linear_fwd_workspace(int64_t T, int64_t in, int64_t out, int format) {
   if (T <= 0 || in <= 0 || out <= 0 || !valid_format(format)) return 0;
-  return 2 * kQuantWS + qtensor_ws_bytes(format, T, in) + qtensor_ws_bytes(format, out, in);
+  return 2 * kQuantWS + qtensor_ws_bytes(format, T, in) + qtensor_ws_bytes(format, out, in) +
+         align_up(gemm_partial_bytes(format, T, out, in), kAlign);
 }
 
 size_t snip_linear_bwd_workspace(int64_t T, int64_t in, int64_t out, int fmt_dgrad, int fmt_wgrad) {
   if (T <= 0 || in <= 0 || out <= 0 || !valid_format(fmt_dgrad) || !valid_format(fmt_wgrad)) return 0;
+  const size_t split = std::max(gemm_partial_bytes(fmt_dgrad, T, in, out),
+                                gemm_partial_bytes(fmt_wgrad, out, in, T));
   return 3 * kAmaxBytes + 4 * kPartBytes + qtensor_ws_bytes(fmt_dgrad, T, out) +
          qtensor_ws_bytes(fmt_dgrad, in, out) + qtensor_ws_bytes(fmt_wgrad, out, T) +
-         qtensor_ws_bytes(fmt_wgrad, in, T);
+         qtensor_ws_bytes(fmt_wgrad, in, T) + align_up(split, kAlign);
 }
 
 int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int layout, int format,
@@ -353,8 +357,6 @@ int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int lay
 
 int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t ldc, void* ws,
                size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int rc = validate_qtensor(a, "snip_qgemm: a");
   if (rc) return rc;
   rc = validate_qtensor(b, "snip_qgemm: b");
@@ -380,6 +382,10 @@ int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t l
   g.N = b->rows;
   g.K = a->k;
   g.ldc = ldc;
+  if (ws && !aligned(ws, 16)) return fail(SNIP_E_ALIGN, "snip_qgemm: workspace must be 16-byte aligned");
+  const size_t need = gemm_partial_bytes(a->format, g.M, g.N, g.K);
+  // a split-K plan needs its scratch; without it the GEMM runs unsplit
+  g.partial = (need > 0 && ws && ws_bytes >= need) ? static_cast<float*>(ws) : nullptr;
   rc = hip_check(launch_gemm(a->format, g, static_cast<hipStream_t>(stream)), "gemm launch");
   if (rc) return rc;
   return ok();
@@ -406,7 +412,8 @@ QBuf carve_q(Carver& cv, int f, int64_t rows, int64_t k) {
   return q;
 }
 
-int gemm_q(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, hipStream_t s) {
+int gemm_q(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, float* partial,
+           hipStream_t s) {
   GemmArgs g;
   g.a = static_cast<const uint8_t*>(a.codes);
   g.b = static_cast<const uint8_t*>(b.codes);
@@ -419,6 +426,7 @@ int gemm_q(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, 
   g.N = b.rows;
   g.K = a.k;
   g.ldc = ldc;
+  g.partial = partial;
   return hip_check(launch_gemm(a.format, g, s), "gemm launch");
 }
 
@@ -453,6 +461,8 @@ int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t
     qx = carve_q(cv, format, T, in);
     qw = carve_q(cv, format, out, in);
   }
+  const size_t split_bytes = gemm_partial_bytes(format, T, out, in);
+  float* split = split_bytes ? reinterpret_cast<float*>(cv.take(split_bytes)) : nullptr;
   auto fill = [&](QPlan& p, const uint16_t* src, int64_t rows, QBuf& q, uint32_t role) {
     p.x = src;
     p.rows = rows;
@@ -490,9 +500,9 @@ int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t
   if (bf) {
     snip_qtensor ax{SNIP_BF16, 0, T, in, const_cast<void*>(x), nullptr, nullptr};
     snip_qtensor aw{SNIP_BF16, 0, out, in, const_cast<void*>(w), nullptr, nullptr};
-    r = gemm_q(ax, aw, y, out, s);
+    r = gemm_q(ax, aw, y, out, split, s);
   } else {
-    r = gemm_q(qx.t, qw.t, y, out, s);
+    r = gemm_q(qx.t, qw.t, y, out, split, s);
   }
   if (r) return r;
   if (stats2) {
@@ -504,8 +514,9 @@ int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t
 }
 
 int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int64_t in, int64_t out,
-                    int fmt_dgrad, int fmt_wgrad, uint64_t seed, uint32_t layer_id, float* dx, float* dw,
-                    snip_stats* stats4, void* ws, size_t ws_bytes, void* stream) {
+                    int fmt_dgrad, int fmt_wgrad, uint64_t seed, uint32_t layer_id,
+                    const snip_stats* fwd_stats2, float* dx, float* dw, snip_stats* stats4, void* ws,
+                    size_t ws_bytes, void* stream) {
   if (!dy || !x || !w) return fail(SNIP_E_NULL, "snip_linear_bwd: dy, x and w must be non-NULL");
   if (!valid_format(fmt_dgrad) || !valid_format(fmt_wgrad))
     return fail(SNIP_E_FORMAT, "snip_linear_bwd: unknown format (%d, %d)", fmt_dgrad, fmt_wgrad);
@@ -519,7 +530,7 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int
     if (in % 16 || out % 16) return fail(SNIP_E_SHAPE, "snip_linear_bwd: in and out must be multiples of 16");
   }
   if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w, 16) || !aligned(dx, 16) || !aligned(dw, 16) ||
-      !aligned(stats4, 8) || !aligned(ws, 16))
+      !aligned(stats4, 8) || !aligned(fwd_stats2, 8) || !aligned(ws, 16))
     return fail(SNIP_E_ALIGN, "snip_linear_bwd: misaligned pointer");
   const size_t need = snip_linear_bwd_workspace(T, in, out, fmt_dgrad, fmt_wgrad);
   if (!ws || ws_bytes < need) return fail(SNIP_E_WORKSPACE, "snip_linear_bwd: workspace of %zu bytes needed", need);
@@ -571,12 +582,17 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int
     p[i].nwg = quant_wg(lay[i], fmt[i], rows[i], cols[i]);
     p[i].stats = stats4 ? stats4 + i : nullptr;
   }
-  // amax passes: dY (shared by both of its quantizations), W, X
+  // amax passes: dY (shared by both of its quantizations), W, X -- the
+  // forward pass's statistics, when given, already hold max|w| and max|x|
+  if (fwd_stats2) {
+    p[1].amax_in = &fwd_stats2[1].amax;
+    p[3].amax_in = &fwd_stats2[0].amax;
+  }
   APlan a[3];
   int na = 0;
   const bool need_dy = (use[0] && needs_amax(fmt[0])) || (use[2] && needs_amax(fmt[2]));
-  const bool need_w = use[1] && needs_amax(fmt[1]);
-  const bool need_x = use[3] && needs_amax(fmt[3]);
+  const bool need_w = use[1] && needs_amax(fmt[1]) && !fwd_stats2;
+  const bool need_x = use[3] && needs_amax(fmt[3]) && !fwd_stats2;
   if (need_dy) a[na++] = APlan{dys, T, out, out, ap_dy, amax_wg(T, out)};
   if (need_w) a[na++] = APlan{wsrc, out, in, in, ap_w, amax_wg(out, in)};
   if (need_x) a[na++] = APlan{xs, T, in, in, ap_x, amax_wg(T, in)};
@@ -598,12 +614,15 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int
   }
   r = run_quant_all(todo, nt, s);
   if (r) return r;
+  const size_t split_bytes = std::max(gemm_partial_bytes(fmt_dgrad, T, in, out),
+                                      gemm_partial_bytes(fmt_wgrad, out, in, T));
+  float* split = split_bytes ? reinterpret_cast<float*>(cv.take(split_bytes)) : nullptr;
   if (dx) {
-    r = gemm_q(q[0].t, q[1].t, dx, in, s);       // [T][out] . ([in][out])^T
+    r = gemm_q(q[0].t, q[1].t, dx, in, split, s);       // [T][out] . ([in][out])^T
     if (r) return r;
   }
   if (dw) {
-    r = gemm_q(q[2].t, q[3].t, dw, in, s);       // [out][T] . ([in][T])^T
+    r = gemm_q(q[2].t, q[3].t, dw, in, split, s);       // [out][T] . ([in][T])^T
     if (r) return r;
   }
   if (stats4) {

@@ -112,6 +112,90 @@ __device__ __forceinline__ float e4m3_val(uint32_t c) {
   return __uint_as_float(c << 20) * 1.32922799578491587e+36f /* 2^120 */;
 }
 
+// ---------------------------------------------------------------- hardware converts
+// gfx950 conversion instructions with unit scale:
+//   v_cvt_scalef32_pk_fp4_f32     E2M1, round to nearest even, saturating;
+//   v_cvt_scalef32_sr_pk_fp4_f32  E2M1, stochastic: the 32-bit random operand,
+//                                 shifted right to align with the discarded
+//                                 mantissa bits, is added and the result
+//                                 truncated;
+//   v_cvt_scalef32_pk_fp8_f32, v_cvt_scalef32_sr_fp8_f32  E4M3 likewise, but
+//                                 not saturating: inputs are clamped to +-448;
+//   v_cvt_scalef32_pk_f32_fp4 / _fp8  decoders.
+// With R16 in the top half of the random operand the stochastic rule is
+// exactly that of e2m1_sr / e4m3_sr above. The stochastic FP4 convert shares
+// its random word between its two lanes and does not keep the other bytes of
+// its destination, so it is issued once per element (lane 0, byte 0) and the
+// nibble is placed by hand. Every helper below is checked against the
+// software encoders over all fp32 inputs (tests/helpers/hw_convert_check.hip).
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef short s2_t __attribute__((ext_vector_type(2)));
+
+// R16 of element i of a Philox block (i in 0..7) in the top half of a word.
+__device__ __forceinline__ uint32_t sr_seed(const Words4& d, int i) {
+  const uint32_t w = d.w[(i >> 1) & 3];
+  return (i & 1) ? (w & 0xFFFF0000u) : (w << 16);
+}
+
+// 8 scaled values -> 8 E2M1 codes in one word (element i in nibble i), RNE.
+__device__ __forceinline__ uint32_t fp4x8_rne(const float* r) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[0], r[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[2], r[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[4], r[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[6], r[7], 1.0f, 3);
+  return w;
+}
+
+// 8 scaled values -> 8 E2M1 codes, stochastic, element i drawing R16 from d.
+__device__ __forceinline__ uint32_t fp4x8_sr(const float* r, const Words4& d) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, f2_t{r[i], 0.0f},
+                                                                   sr_seed(d, i), 1.0f, 0);
+    w |= (c & 0xFu) << (4 * i);
+  }
+  return w;
+}
+
+// Decoded (signed) E2M1 values of the 8 codes of a word.
+__device__ __forceinline__ void fp4x8_dec(uint32_t w, float* q) {
+  const f2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  q[0] = v0[0]; q[1] = v0[1]; q[2] = v1[0]; q[3] = v1[1];
+  q[4] = v2[0]; q[5] = v2[1]; q[6] = v3[0]; q[7] = v3[1];
+}
+
+// 4 values clamped to +-448 -> 4 E4M3 codes (byte b = element b), RNE.
+__device__ __forceinline__ uint32_t fp8x4_rne(const float* c) {
+  s2_t w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c[0], c[1], 1.0f, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c[2], c[3], 1.0f, true);
+  return __builtin_bit_cast(uint32_t, w);
+}
+
+// 4 values clamped to +-448 -> 4 E4M3 codes, stochastic; element b draws
+// R16 of element (first + b) of the Philox block d.
+__device__ __forceinline__ uint32_t fp8x4_sr(const float* c, const Words4& d, int first) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t v = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0u, c[b], sr_seed(d, first + b), 1.0f, 0);
+    w |= (v & 0xFFu) << (8 * b);
+  }
+  return w;
+}
+
+// Decoded (signed) E4M3 values of the 4 codes of a word.
+__device__ __forceinline__ void fp8x4_dec(uint32_t w, float* q) {
+  const f2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+  const f2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+  q[0] = a[0]; q[1] = a[1]; q[2] = b[0]; q[3] = b[1];
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll

@@ -76,7 +76,21 @@ struct GemmArgs {
   const int32_t* eb;
   float* c;
   int64_t M, N, K, ldc;
+  float* partial;          // split-K scratch [ksplit][M][N] or null (no split)
+  int32_t tiles_m, tiles_n;
+  int64_t kchunk;          // K elements per split (set by launch_gemm)
 };
+
+// Tile shape and K split chosen on the host for one GEMM.
+struct GemmPlan {
+  int bm;                  // square tile edge: 256 or 128
+  int bk;                  // K per LDS stage
+  int64_t tiles;
+  int ksplit;
+  int64_t kchunk;
+};
+GemmPlan plan_gemm(int format, int64_t M, int64_t N, int64_t K);
+size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K);
 
 // Launchers (all asynchronous on `s`); they return the hipError_t of the launch.
 hipError_t launch_amax(const AJobs& jobs, int total_wg, hipStream_t s);

@@ -126,6 +126,9 @@ __global__ __launch_bounds__(256) void amax_kernel(AJobs jobs) {
 }
 
 // ------------------------------------------------------------ block codecs
+// Element encoding and the decode for the statistics use the gfx950
+// conversion instructions through the packed helpers of device.h.
+
 // NVFP4: 16 raw values x -> 16 packed nibbles (lo: elements 0..7, hi: 8..15),
 // the E4M3 block scale and the block's stats in the tensor-scaled domain.
 template <bool SR>
@@ -141,34 +144,27 @@ __device__ __forceinline__ void nvfp4_block(const float (&x)[16], int eS, const 
   }
   sc = e4m3_rne(am / 6.0f);
   const float shat = e4m3_val(sc);
-  lo = 0u;
-  hi = 0u;
+  const float inv = sc ? 1.0f / shat : 0.0f;      // a zero block keeps signed-zero codes
+  float r[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = xs[i] * inv;
+  if (SR) {
+    lo = fp4x8_sr(r, d0);
+    hi = fp4x8_sr(r + 8, d1);
+  } else {
+    lo = fp4x8_rne(r);
+    hi = fp4x8_rne(r + 8);
+  }
+  float q[16];
+  fp4x8_dec(lo, q);
+  fp4x8_dec(hi, q + 8);
   be2 = 0.0f;
   bx2 = 0.0f;
-  if (sc != 0u) {
-    const float inv = 1.0f / shat;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float a = fabsf(xs[i] * inv);
-      uint32_t m;
-      if (SR) m = e2m1_sr(a, r16_of(i < 8 ? d0 : d1, i & 7));
-      else m = e2m1_rne(a);
-      const uint32_t code = m | ((__float_as_uint(x[i]) >> 28) & 8u);
-      if (i < 8) lo |= code << (4 * i);
-      else hi |= code << (4 * (i - 8));
-      const float err = e2m1_val(m) * shat - fabsf(xs[i]);
-      be2 = fmaf(err, err, be2);
-      bx2 = fmaf(xs[i], xs[i], bx2);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t code = (__float_as_uint(x[i]) >> 28) & 8u;
-      if (i < 8) lo |= code << (4 * i);
-      else hi |= code << (4 * (i - 8));
-      bx2 = fmaf(xs[i], xs[i], bx2);
-    }
-    be2 = bx2;
+  for (int i = 0; i < 16; ++i) {
+    const float err = fmaf(q[i], shat, -xs[i]);
+    be2 = fmaf(err, err, be2);
+    bx2 = fmaf(xs[i], xs[i], bx2);
   }
 }
 
@@ -177,23 +173,29 @@ template <bool SR>
 __device__ __forceinline__ void fp8_chunk(const float (&x)[16], int eS, const Words4& d0,
                                           const Words4& d1, uint32_t (&out)[4], float& be2,
                                           float& bx2) {
+  float r[16], c[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    r[i] = ldexpf(x[i], -eS);
+    c[i] = __builtin_amdgcn_fmed3f(r[i], -448.0f, 448.0f);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    out[k] = SR ? fp8x4_sr(c + 4 * k, k < 2 ? d0 : d1, (4 * k) & 7) : fp8x4_rne(c + 4 * k);
   be2 = 0.0f;
   bx2 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = 0u;
+  for (int k = 0; k < 4; ++k) {
+    float q[4];
+    fp8x4_dec(out[k], q);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float r = ldexpf(x[i], -eS);
-    const float a = fabsf(r);
-    uint32_t m;
-    if (SR) m = e4m3_sr(a, r16_of(i < 8 ? d0 : d1, i & 7));
-    else m = e4m3_rne(a);
-    const uint32_t code = m | ((__float_as_uint(x[i]) >> 24) & 0x80u);
-    out[i >> 2] |= code << (8 * (i & 3));
-    const float err = e4m3_val(m) - a;
-    be2 = fmaf(err, err, be2);
-    bx2 = fmaf(r, r, bx2);
+    for (int b = 0; b < 4; ++b) {
+      const float e = q[b] - r[4 * k + b];
+      be2 = fmaf(e, e, be2);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bx2 = fmaf(r[i], r[i], bx2);
 }
 
 // MX-FP4: 32 raw values -> 32 nibbles (4 words), E8M0 scale; stats are
@@ -201,39 +203,34 @@ __device__ __forceinline__ void fp8_chunk(const float (&x)[16], int eS, const Wo
 template <bool SR>
 __device__ __forceinline__ void mx_block(const float (&x)[32], const Words4 (&d)[4],
                                          uint32_t (&out)[4], uint32_t& sc, double& e2,
-                                         double& x2, float& bx2_scaled) {
-  float am = 0.0f;
+                                         double& x2, float& bx2_scaled, float& am) {
+  am = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
-  int X;
+  int X = -127;
   if (am > 0.0f) {
     const int e = (int)(__float_as_uint(am) >> 23);      // biased exponent (0: subnormal)
     X = e - 129;                                          // floor(log2 am) - 2
     X = X < -127 ? -127 : X;
-  } else {
-    X = -127;
   }
   sc = (uint32_t)(X + 127);
-  const float pw = exp2i(-X);                             // exact power of two
+  const float pw = am > 0.0f ? exp2i(-X) : 0.0f;          // exact power of two (0: zero block)
+  float r[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) r[i] = x[i] * pw;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = SR ? fp4x8_sr(r + 8 * k, d[k]) : fp4x8_rne(r + 8 * k);
   float be2 = 0.0f, bx2 = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = 0u;
-  if (am > 0.0f) {
+  for (int k = 0; k < 4; ++k) {
+    float q[8];
+    fp4x8_dec(out[k], q);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float r = x[i] * pw;
-      const float a = fabsf(r);
-      uint32_t m;
-      if (SR) m = e2m1_sr(a, r16_of(d[i >> 3], i & 7));
-      else m = e2m1_rne(a);
-      out[i >> 3] |= (m | ((__float_as_uint(x[i]) >> 28) & 8u)) << (4 * (i & 7));
-      const float err = e2m1_val(m) - a;
+    for (int i = 0; i < 8; ++i) {
+      const float err = q[i] - r[8 * k + i];
       be2 = fmaf(err, err, be2);
-      bx2 = fmaf(r, r, bx2);
+      bx2 = fmaf(r[8 * k + i], r[8 * k + i], bx2);
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) out[i >> 3] |= ((__float_as_uint(x[i]) >> 28) & 8u) << (4 * (i & 7));
   }
   e2 = ldexp((double)be2, 2 * X);
   x2 = ldexp((double)bx2, 2 * X);
@@ -271,7 +268,82 @@ __device__ __forceinline__ void unpack16(const uint4& v0, const uint4& v1, float
 
 // ------------------------------------------------------------ row-wise
 // One thread item = one 16-element NVFP4 block, 16 FP8 elements, or one
-// 32-element MX block; item `it` covers output elements it*EPT .. +EPT.
+// 32-element MX block; item `it` covers output elements it*EPT .. +EPT. Each
+// thread handles two items per iteration (both loads issued first).
+template <int FMT, bool SR>
+struct RowAcc {
+  double e2s = 0.0, x2s = 0.0;      // tensor-scaled domain (NVFP4, FP8)
+  double e2r = 0.0, x2r = 0.0;      // raw domain (MX, non-finite blocks)
+  uint32_t nf = 0u, amax_bits = 0u;
+};
+
+template <int FMT, bool SR>
+__device__ __forceinline__ void row_item(const QJob& J, int eS, int64_t it,
+                                         const uint4 (&v)[FMT == SNIP_MXFP4 ? 4 : 2],
+                                         RowAcc<FMT, SR>& acc) {
+  constexpr int EPT = (FMT == SNIP_MXFP4) ? 32 : 16;
+  const uint64_t g0 = (uint64_t)it * (EPT / 8);           // first Philox counter of the item
+  if constexpr (FMT == SNIP_MXFP4) {
+    float x[32], h0[16], h1[16];
+    unpack16(v[0], v[1], h0);
+    unpack16(v[2], v[3], h1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = h0[i];
+      x[16 + i] = h1[i];
+    }
+    Words4 d[4];
+    if (SR) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] = draws8(J.seed, J.tensor_id, g0 + q);
+    }
+    uint32_t out[4], sc;
+    double be2, bx2;
+    float bx2f, am;
+    mx_block<SR>(x, d, out, sc, be2, bx2, bx2f, am);
+    const bool bad = !(bx2f <= 3.0e38f);
+    uint32_t bnf = 0u, bam = __float_as_uint(am);
+    double rx2 = bx2;
+    if (bad) {
+      bam = 0u;
+      nonfinite_stats<32>(x, bnf, rx2, bam);
+    }
+    acc.nf += bnf;
+    acc.x2r += rx2;
+    acc.e2r += bad ? 0.0 : be2;
+    acc.amax_bits = max(acc.amax_bits, bam);
+    *reinterpret_cast<uint4*>(J.codes + it * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+    J.scales[it] = (uint8_t)sc;
+  } else {
+    float x[16];
+    unpack16(v[0], v[1], x);
+    Words4 d0, d1;
+    if (SR) {
+      d0 = draws8(J.seed, J.tensor_id, g0);
+      d1 = draws8(J.seed, J.tensor_id, g0 + 1);
+    }
+    float be2, bx2;
+    if constexpr (FMT == SNIP_NVFP4) {
+      uint32_t lo, hi, sc;
+      nvfp4_block<SR>(x, eS, d0, d1, lo, hi, sc, be2, bx2);
+      *reinterpret_cast<uint2*>(J.codes + it * 8) = make_uint2(lo, hi);
+      J.scales[it] = (uint8_t)sc;
+    } else {
+      uint32_t out[4];
+      fp8_chunk<SR>(x, eS, d0, d1, out, be2, bx2);
+      *reinterpret_cast<uint4*>(J.codes + it * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+    const bool bad = !(bx2 <= 3.0e38f);
+    uint32_t bnf = 0u, dummy = 0u;
+    double rx2 = 0.0;
+    if (bad) nonfinite_stats<16>(x, bnf, rx2, dummy);
+    acc.nf += bnf;
+    acc.x2r += rx2;
+    acc.e2s += bad ? 0.0 : (double)be2;
+    acc.x2s += bad ? 0.0 : (double)bx2;
+  }
+}
+
 template <int FMT, bool SR>
 __global__ __launch_bounds__(256) void quant_row_kernel(QJobs jobs) {
   int32_t wg0[kMaxJobs];
@@ -281,98 +353,55 @@ __global__ __launch_bounds__(256) void quant_row_kernel(QJobs jobs) {
   __shared__ uint32_t ured[8];
   __shared__ double dred[8];
 
+  constexpr int EPT = (FMT == SNIP_MXFP4) ? 32 : 16;
+  constexpr int NV = EPT / 8;                             // 16-byte loads per item
+  const int64_t tpr = J.cols / EPT;
+  const int64_t nitems = J.rows * tpr;
+  const bool flat = J.ld == J.cols;
+  const int64_t stride = (int64_t)J.nwg * 512;
+  int64_t it = (int64_t)wg * 512 + threadIdx.x;
+
+  // first loads before the tensor-max reduction, to overlap its latency
+  uint4 v[2][NV];
+  auto load = [&](int64_t item, uint4 (&dst)[NV]) {
+    if (item < nitems) {
+      const int64_t off = flat ? item * EPT : (item / tpr) * J.ld + (item % tpr) * EPT;
+      const uint4* src = reinterpret_cast<const uint4*>(J.x + off);
+#pragma unroll
+      for (int q = 0; q < NV; ++q) dst[q] = src[q];
+    }
+  };
+  load(it, v[0]);
+  load(it + 256, v[1]);
+
   const float A = (FMT == SNIP_MXFP4) ? 0.0f : wg_tensor_amax(J, ured);
   const int eS = tensor_exp(A, FMT);
   if (wg == 0 && threadIdx.x == 0 && J.texp) *J.texp = eS;
 
-  constexpr int EPT = (FMT == SNIP_MXFP4) ? 32 : 16;
-  const int64_t tpr = J.cols / EPT;
-  const int64_t nitems = J.rows * tpr;
-  const bool flat = J.ld == J.cols;
-  double e2s = 0.0, x2s = 0.0;      // tensor-scaled domain (NVFP4, FP8)
-  double e2r = 0.0, x2r = 0.0;      // raw domain (MX, non-finite blocks)
-  uint32_t nf = 0u, amax_bits = 0u;
-
-  for (int64_t it = (int64_t)wg * 256 + threadIdx.x; it < nitems; it += (int64_t)J.nwg * 256) {
-    const int64_t off = flat ? it * EPT : (it / tpr) * J.ld + (it % tpr) * EPT;
-    const uint4* src = reinterpret_cast<const uint4*>(J.x + off);
-    const uint64_t g0 = (uint64_t)it * (EPT / 8);          // first Philox counter
-    if constexpr (FMT == SNIP_MXFP4) {
-      float x[32], h0[16], h1[16];
-      unpack16(src[0], src[1], h0);
-      unpack16(src[2], src[3], h1);
+  RowAcc<FMT, SR> acc;
+  for (; it < nitems; it += stride) {
+    uint4 cur[2][NV];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = h0[i];
-        x[16 + i] = h1[i];
-      }
-      Words4 d[4];
-      if (SR) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) d[q] = draws8(J.seed, J.tensor_id, g0 + q);
-      }
-      uint32_t out[4], sc;
-      double be2, bx2;
-      float bx2f;
-      mx_block<SR>(x, d, out, sc, be2, bx2, bx2f);
-      if (!(bx2f <= 3.0e38f)) {
-        uint32_t bnf;
-        double rx2;
-        nonfinite_stats<32>(x, bnf, rx2, amax_bits);
-        nf += bnf;
-        x2r += rx2;
-      } else {
-        e2r += be2;
-        x2r += bx2;
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
-        amax_bits = __float_as_uint(am) > amax_bits ? __float_as_uint(am) : amax_bits;
-      }
-      *reinterpret_cast<uint4*>(J.codes + it * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-      J.scales[it] = (uint8_t)sc;
-    } else {
-      float x[16];
-      unpack16(src[0], src[1], x);
-      Words4 d0, d1;
-      if (SR) {
-        d0 = draws8(J.seed, J.tensor_id, g0);
-        d1 = draws8(J.seed, J.tensor_id, g0 + 1);
-      }
-      float be2, bx2;
-      if constexpr (FMT == SNIP_NVFP4) {
-        uint32_t lo, hi, sc;
-        nvfp4_block<SR>(x, eS, d0, d1, lo, hi, sc, be2, bx2);
-        *reinterpret_cast<uint2*>(J.codes + it * 8) = make_uint2(lo, hi);
-        J.scales[it] = (uint8_t)sc;
-      } else {
-        uint32_t out[4];
-        fp8_chunk<SR>(x, eS, d0, d1, out, be2, bx2);
-        *reinterpret_cast<uint4*>(J.codes + it * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-      }
-      if (!(bx2 <= 3.0e38f)) {
-        uint32_t bnf;
-        double rx2;
-        uint32_t dummy = 0u;
-        nonfinite_stats<16>(x, bnf, rx2, dummy);
-        nf += bnf;
-        x2r += rx2;
-      } else {
-        e2s += (double)be2;
-        x2s += (double)bx2;
-      }
-    }
+      for (int q = 0; q < NV; ++q) cur[u][q] = v[u][q];
+    load(it + stride, v[0]);                                // prefetch the next iteration
+    load(it + stride + 256, v[1]);
+    row_item<FMT, SR>(J, eS, it, cur[0], acc);
+    if (it + 256 < nitems) row_item<FMT, SR>(J, eS, it + 256, cur[1], acc);
   }
-  if (FMT != SNIP_MXFP4) amax_bits = __float_as_uint(A);
-  const double e2 = ldexp(e2s, 2 * eS) + e2r;
-  const double x2 = ldexp(x2s, 2 * eS) + x2r;
-  wg_store_stats(J.part + wg, e2, x2, nf, amax_bits, dred, ured);
+  if (FMT != SNIP_MXFP4) acc.amax_bits = __float_as_uint(A);
+  const double e2 = ldexp(acc.e2s, 2 * eS) + acc.e2r;
+  const double x2 = ldexp(acc.x2s, 2 * eS) + acc.x2r;
+  wg_store_stats(J.part + wg, e2, x2, acc.nf, acc.amax_bits, dred, ured);
 }
 
 // ------------------------------------------------------------ column-wise
 // Source x[R][C] -> output [C][R] with blocks running down the source
 // columns. Tile: kColTileRows x kColTileCols; lane l owns columns c0+2l and
-// c0+2l+1, wave w owns the block rows w, w+4, ...
+// c0+2l+1, wave w owns the block rows w, w+4, ... All loads of a tile are
+// issued before its blocks are encoded; codes are staged in LDS and written
+// as contiguous output row segments.
 template <int FMT, bool SR>
 __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
   int32_t wg0[kMaxJobs];
@@ -385,6 +414,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
   constexpr int BLK = (FMT == SNIP_MXFP4) ? 32 : 16;
   constexpr int TR = kColTileRows, TC = kColTileCols;
   constexpr int NB = TR / BLK;                                  // blocks per column per tile
+  constexpr int NBT = NB / 4;                                   // block rows per wave
   constexpr int CB = (FMT == SNIP_NVFP4) ? 8 : 16;              // code bytes per block
   constexpr int PITCH = NB * CB + 8;                            // LDS bytes per column
   __shared__ __align__(16) uint8_t lcodes[TC * PITCH];
@@ -408,21 +438,25 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
     const int nbt = (int)((R - r0) / BLK < NB ? (R - r0) / BLK : NB);
     const int64_t col = c0 + 2 * lane;
     if (col < C) {
-#pragma unroll 1
-      for (int t = 0; t < NB / 4; ++t) {
-        const int rb = wave + 4 * t;
-        if (rb >= nbt) break;
-        const uint16_t* src = J.x + (r0 + (int64_t)rb * BLK) * J.ld + col;
-        float xa[BLK], xb[BLK];
+      uint32_t w[NBT][BLK];
 #pragma unroll
-        for (int i = 0; i < BLK; ++i) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (int64_t)i * J.ld);
-          xa[i] = bf16_lo(w);
-          xb[i] = bf16_hi(w);
+      for (int t = 0; t < NBT; ++t) {
+        const int rb = wave + 4 * t;
+        if (rb < nbt) {
+          const uint16_t* src = J.x + (r0 + (int64_t)rb * BLK) * J.ld + col;
+#pragma unroll
+          for (int i = 0; i < BLK; ++i) w[t][i] = *reinterpret_cast<const uint32_t*>(src + (int64_t)i * J.ld);
         }
+      }
+#pragma unroll
+      for (int t = 0; t < NBT; ++t) {
+        const int rb = wave + 4 * t;
+        if (rb >= nbt) continue;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const float(&x)[BLK] = h ? xb : xa;
+          float x[BLK];
+#pragma unroll
+          for (int i = 0; i < BLK; ++i) x[i] = h ? bf16_hi(w[t][i]) : bf16_lo(w[t][i]);
           const int cl = 2 * lane + h;
           const uint64_t g0 = ((uint64_t)(col + h) * (uint64_t)R + (uint64_t)(r0 + rb * BLK)) >> 3;
           uint8_t* dst = lcodes + cl * PITCH + rb * CB;
@@ -434,22 +468,19 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
             }
             uint32_t out[4], sc;
             double be2, bx2;
-            float bx2f;
-            mx_block<SR>(x, d, out, sc, be2, bx2, bx2f);
-            if (!(bx2f <= 3.0e38f)) {
-              uint32_t bnf;
-              double rx2;
-              nonfinite_stats<32>(x, bnf, rx2, amax_bits);
-              nf += bnf;
-              x2r += rx2;
-            } else {
-              e2r += be2;
-              x2r += bx2;
-              float am = 0.0f;
-#pragma unroll
-              for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
-              amax_bits = __float_as_uint(am) > amax_bits ? __float_as_uint(am) : amax_bits;
+            float bx2f, am;
+            mx_block<SR>(x, d, out, sc, be2, bx2, bx2f, am);
+            const bool bad = !(bx2f <= 3.0e38f);
+            uint32_t bnf = 0u, bam = __float_as_uint(am);
+            double rx2 = bx2;
+            if (bad) {
+              bam = 0u;
+              nonfinite_stats<32>(x, bnf, rx2, bam);
             }
+            nf += bnf;
+            x2r += rx2;
+            e2r += bad ? 0.0 : be2;
+            amax_bits = max(amax_bits, bam);
             *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
             *reinterpret_cast<uint2*>(dst + 8) = make_uint2(out[2], out[3]);
             lsc[cl * NB + rb] = (uint8_t)sc;
@@ -471,16 +502,14 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
               *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
               *reinterpret_cast<uint2*>(dst + 8) = make_uint2(out[2], out[3]);
             }
-            if (!(bx2 <= 3.0e38f)) {
-              uint32_t bnf, dummy = 0u;
-              double rx2;
-              nonfinite_stats<16>(x, bnf, rx2, dummy);
-              nf += bnf;
-              x2r += rx2;
-            } else {
-              e2s += (double)be2;
-              x2s += (double)bx2;
-            }
+            const bool bad = !(bx2 <= 3.0e38f);
+            uint32_t bnf = 0u, dummy = 0u;
+            double rx2 = 0.0;
+            if (bad) nonfinite_stats<16>(x, bnf, rx2, dummy);
+            nf += bnf;
+            x2r += rx2;
+            e2s += bad ? 0.0 : (double)be2;
+            x2s += bad ? 0.0 : (double)bx2;
           }
         }
       }

@@ -129,15 +129,15 @@ def test_linear_validation(L):
     assert L.snip_linear_fwd(P, P2 + 1, 64, 128, 64, S.NVFP4, 0, 0, y, None, ws, 1 << 30, None) == -3
     # backward: dgrad needs out % 128, wgrad needs T % 128
     dx, dw = P + 0x3000000, P + 0x4000000
-    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 96, S.NVFP4, S.NVFP4, 0, 0, dx, None, None, ws,
+    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 96, S.NVFP4, S.NVFP4, 0, 0, None, dx, None, None, ws,
                              1 << 30, None) == -2
-    assert L.snip_linear_bwd(P, P2, P3, 96, 64, 128, S.NVFP4, S.NVFP4, 0, 0, None, dw, None, ws,
+    assert L.snip_linear_bwd(P, P2, P3, 96, 64, 128, S.NVFP4, S.NVFP4, 0, 0, None, None, dw, None, ws,
                              1 << 30, None) == -2
-    assert L.snip_linear_bwd(P, None, P3, 128, 64, 128, S.NVFP4, S.NVFP4, 0, 0, dx, dw, None, ws,
+    assert L.snip_linear_bwd(P, None, P3, 128, 64, 128, S.NVFP4, S.NVFP4, 0, 0, None, dx, dw, None, ws,
                              1 << 30, None) == -1
-    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 128, S.NVFP4, 9, 0, 0, dx, dw, None, ws,
+    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 128, S.NVFP4, 9, 0, 0, None, dx, dw, None, ws,
                              1 << 30, None) == -4
-    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 128, S.NVFP4, S.FP8, 0, 0, dx, dw, None, ws,
+    assert L.snip_linear_bwd(P, P2, P3, 128, 64, 128, S.NVFP4, S.FP8, 0, 0, None, dx, dw, None, ws,
                              64, None) == -5
 
 
