@@ -41,8 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="tinyllama1b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
-    ap.add_argument("--kernel-reps", type=int, default=10)
     return ap.parse_args()
 
 
@@ -124,74 +124,67 @@ def main():
     value = gemm_flops / (ms_step * 1e-3) / 1e12
 
     # ---------------------------------------------------- per-kernel timing
-    # The same GEMMs and quantize passes, launched one call at a time between
-    # HIP events on the stream they run on.
-    stream = torch.cuda.current_stream()
-    R = args.kernel_reps
-
-    def timed(fn):
-        fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(R):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        return a.elapsed_time(b) / R * 1e-3    # seconds per call
-
+    # The same steps again, eagerly, with every kernel launch of the library
+    # bracketed by HIP events on the stream it is launched on.
+    S.timing_start(len(layers) * 40 * args.steps + 64)
+    for _ in range(args.steps):
+        step()
+    recs, untimed = S.timing_read()
+    if untimed:
+        raise RuntimeError(f"{untimed} launches were not timed")
     gemm_by_fmt = {}
-    quant = {"bytes": 0.0, "sec": 0.0, "passes": 0}
-    amax_sec = 0.0
-    for li, d in enumerate(layers):
-        fmt = d["fmt"]
-        # operands exactly as the step builds them
-        qx, _ = S.quantize(d["x"], S.ROWWISE, fmt, S.RNE, seed, 8 * li + 0, with_stats=False)
-        qw, _ = S.quantize(d["w"], S.ROWWISE, fmt, S.RNE, seed, 8 * li + 1, with_stats=False)
-        qdy, _ = S.quantize(d["dy"], S.ROWWISE, fmt, S.SR, seed, 8 * li + 2, with_stats=False)
-        qwt, _ = S.quantize(d["w"], S.COLWISE, fmt, S.SR, seed, 8 * li + 3, with_stats=False)
-        qdyt, _ = S.quantize(d["dy"], S.COLWISE, fmt, S.SR, seed, 8 * li + 4, with_stats=False)
-        qxt, _ = S.quantize(d["x"], S.COLWISE, fmt, S.SR, seed, 8 * li + 5, with_stats=False)
-        for a, b, out in ((qx, qw, d["y"]), (qdy, qwt, d["dx"]), (qdyt, qxt, d["dw"])):
-            sec = timed(lambda: S.qgemm(a, b, out=out))
-            g = gemm_by_fmt.setdefault(fmt, {"sec": 0.0, "flops": 0.0, "launches": 0})
-            g["sec"] += sec
-            g["flops"] += 2.0 * a.rows * b.rows * a.k
+    quant = {"bytes": 0.0, "ms": 0.0, "launches": 0}
+    other_ms = {}
+    for r in recs:
+        if r["kind"] == "gemm":
+            g = gemm_by_fmt.setdefault(r["format"], {"ms": 0.0, "flops": 0.0, "launches": 0})
+            g["ms"] += r["ms"]
+            g["flops"] += r["work"]
             g["launches"] += 1
-        # quantize passes with the tensor max supplied: kernel alone
-        for src, lay, rnd, qt in ((d["x"], S.ROWWISE, S.RNE, qx), (d["w"], S.ROWWISE, S.RNE, qw),
-                                  (d["dy"], S.ROWWISE, S.SR, qdy), (d["w"], S.COLWISE, S.SR, qwt),
-                                  (d["dy"], S.COLWISE, S.SR, qdyt), (d["x"], S.COLWISE, S.SR, qxt)):
-            amax = src.abs().max().float().reshape(1)
-            sec = timed(lambda: S.quantize(src, lay, fmt, rnd, seed, 1, amax=amax, out=qt,
-                                           with_stats=False))
-            quant["sec"] += sec
-            quant["bytes"] += src.numel() * QBYTES[fmt]
-            quant["passes"] += 1
-    dom_fmt = max(gemm_by_fmt, key=lambda f: gemm_by_fmt[f]["sec"])
+        elif r["kind"] == "quantize":
+            quant["ms"] += r["ms"]
+            quant["bytes"] += r["work"] * QBYTES[r["format"]]
+            quant["launches"] += 1
+        else:
+            other_ms[r["kind"]] = other_ms.get(r["kind"], 0.0) + r["ms"]
+    dom_fmt = max(gemm_by_fmt, key=lambda f: gemm_by_fmt[f]["ms"])
+    # algorithmic HBM bytes of the dominant format's GEMMs: both operands'
+    # codes and scales read once, the fp32 product written once
+    ebytes = {S.BF16: 2.0, S.FP8: 1.0, S.NVFP4: 0.5 + 1 / 16, S.MXFP4: 0.5 + 1 / 32}[dom_fmt]
+    shapes = [(T, d["dout"], d["din"]) for d in layers if d["fmt"] == dom_fmt]
+    shapes = [s_ for (t, o, i) in shapes for s_ in ((t, o, i), (t, i, o), (o, i, t))]
+    alg_bytes = sum((m * k + n * k) * ebytes + 4.0 * m * n for m, n, k in shapes) / len(shapes)
     dom = gemm_by_fmt[dom_fmt]
-    avg_launch = dom["sec"] / dom["launches"]
+    avg_launch_s = dom["ms"] / dom["launches"] * 1e-3
     flops_per_launch = dom["flops"] / dom["launches"]
-    achieved = flops_per_launch / avg_launch / 1e12
+    achieved = flops_per_launch / avg_launch_s / 1e12
+    kernel_prefix = f"void snip::gemm_kernel<{dom_fmt},"
+    from sub_byte_mixed_amd import profiling
+    tr = profiling.load_traffic(wl.name, kernel_prefix)
     roofline = {
         "bound": "mfma",
         "kernel": f"gemm_kernel<{S.FORMAT_NAMES[dom_fmt]}> (fp16 MFMA after exact decode)"
         if dom_fmt in (S.NVFP4, S.FP8) else f"gemm_kernel<{S.FORMAT_NAMES[dom_fmt]}>",
         "achieved": round(achieved, 2), "peak": PEAK["fp16_tflops"], "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK["fp16_tflops"], 4), "traffic": None,
-        "avg_launch_us": round(avg_launch * 1e6, 2), "flops_per_launch": flops_per_launch,
-        "launches_per_step": dom["launches"],
+        "frac": round(achieved / PEAK["fp16_tflops"], 4),
+        "traffic": tr["traffic_bytes_per_launch"] if tr else None,
+        "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+        "algorithmic_bytes_per_launch": round(alg_bytes),
+        "avg_launch_us": round(avg_launch_s * 1e6, 2), "flops_per_launch": flops_per_launch,
+        "launches_per_step": dom["launches"] // args.steps,
         "frac_of_native_peak": round(achieved / (PEAK["fp4_tflops"] if dom_fmt in (S.NVFP4, S.MXFP4)
                                                  else PEAK["fp8_tflops"]), 4),
     }
-    gemm_detail = {S.FORMAT_NAMES[f]: {"tflops": round(g["flops"] / g["sec"] / 1e12, 2),
-                                       "ms_per_step": round(g["sec"] * 1e3, 3), "launches": g["launches"]}
+    gemm_detail = {S.FORMAT_NAMES[f]: {"tflops": round(g["flops"] / (g["ms"] * 1e-3) / 1e12, 2),
+                                       "ms_per_step": round(g["ms"] / args.steps, 4),
+                                       "launches_per_step": g["launches"] // args.steps}
                    for f, g in gemm_by_fmt.items()}
-    quant_gbs = quant["bytes"] / quant["sec"] / 1e9
+    quant_gbs = quant["bytes"] / (quant["ms"] * 1e-3) / 1e9
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl)
+        cpu = cpu_baseline(wl, args.cpu_tokens)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -203,16 +196,21 @@ def main():
                    "plan": [S.FORMAT_NAMES[d["fmt"]] for d in layers], "graph": bool(graph)},
         "gemm": gemm_detail,
         "quantize": {"gbs": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / PEAK["hbm_gbs"], 4),
-                     "ms_per_step": round(quant["sec"] * 1e3, 3), "passes": quant["passes"]},
+                     "ms_per_step": round(quant["ms"] / args.steps, 4),
+                     "launches_per_step": quant["launches"] // args.steps},
+        "other_kernels_ms_per_step": {k: round(v / args.steps, 4) for k, v in other_ms.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl):
-    """The oracle as it stands on a bounded sample: forward + backward of the
-    first layer (Q) at the workload's format, on the first 256 tokens."""
+def cpu_baseline(wl, tokens=None):
+    """The oracle as it stands on a bounded sample of the workload: forward +
+    backward of the Gate layer (the first layer if there is none), all six
+    quantize passes and the three GEMMs in the layer's format, on the first
+    `tokens` tokens (default: the whole layer when it holds at most 4096
+    tokens)."""
     import synth
     from oracle import linear as OL
     try:
@@ -220,9 +218,10 @@ def cpu_baseline(wl):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    li = 0
+    names = [l.name for l in wl.layers]
+    li = names.index("Gate") if "Gate" in names else 0
     layer = wl.layers[li]
-    Ts = min(256, wl.tokens)
+    Ts = min(tokens or 4096, wl.tokens)
     x, w, dy = synth.gen_x(wl, li, rows=Ts), synth.gen_w(wl, li), synth.gen_dy(wl, li, rows=Ts)
     x32, w32, dy32 = (synth.bf16_to_f32(t) for t in (x, w, dy))
     fmt = wl.plan[li]
@@ -231,10 +230,11 @@ def cpu_baseline(wl):
     OL.linear_bwd(dy32, x32, w32, fmt, fmt, 0, li)
     sec = time.perf_counter() - t0
     flops = 3 * 2 * Ts * layer.d_in * layer.d_out
+    import sub_byte_mixed_amd as S
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"layer {layer.name} {layer.d_in}->{layer.d_out}, T={Ts} of {wl.tokens}, "
-                      f"fwd+bwd incl. all six quantize passes, format {fmt}"}
+            "sample": f"layer {layer.name} {layer.d_in}->{layer.d_out}, T={Ts} of {wl.tokens} tokens, "
+                      f"fwd+bwd incl. all six quantize passes, {S.FORMAT_NAMES[fmt]}"}
 
 
 if __name__ == "__main__":

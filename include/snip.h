@@ -31,8 +31,9 @@
  *               any HIP call, so a rejected call has enqueued nothing.
  *               snip_last_error() returns a thread-local message for the
  *               last failure. No C++ exception crosses this interface.
- *   Threads     Calls hold no global mutable state and may be made from
- *               several threads; work enqueued on one stream is ordered.
+ *   Threads     Calls hold no global mutable state (apart from the launch
+ *               timing switch, snip_timing_*) and may be made from several
+ *               threads; work enqueued on one stream is ordered.
  *   Workspace   Caller-provided device scratch of at least the size the
  *               matching snip_*_workspace() returns; its contents need no
  *               initialisation and are clobbered. Calls that overlap in time
@@ -242,6 +243,45 @@ size_t snip_linear_bwd_workspace(int64_t T, int64_t in, int64_t out,
 /* Bytes of one part of a quantized operand: part 0 = codes, 1 = scales.
  * Returns -1 on invalid arguments. */
 int64_t snip_qtensor_bytes(int format, int64_t rows, int64_t k, int part);
+
+/* ---- launch timing (measurement support) -------------------------------- */
+
+/* Kinds of kernel launch that the library makes. */
+#define SNIP_LAUNCH_AMAX      0  /* tensor-max pre-pass                         */
+#define SNIP_LAUNCH_QUANTIZE  1  /* quantize (or bf16 copy / transpose) pass    */
+#define SNIP_LAUNCH_GEMM      2  /* block-scaled GEMM main kernel               */
+#define SNIP_LAUNCH_SPLITK    3  /* split-K partial-sum reduction               */
+#define SNIP_LAUNCH_FINALIZE  4  /* statistics finalisation                     */
+
+/* One timed launch. `work` is the launch's algorithmic work: GEMM 2*M*N*K
+ * flop; quantize and amax: source elements read (all tensors of the
+ * launch); split-K: output elements; finalize: tensors. `ms` is the time
+ * between HIP events recorded on the launch's stream right before and
+ * right after it. */
+typedef struct snip_launch_record {
+  int32_t kind;       /* SNIP_LAUNCH_*                                      */
+  int32_t format;     /* SNIP_BF16.. for quantize / GEMM / split-K, else -1 */
+  int32_t layout;     /* quantize: SNIP_ROWWISE / SNIP_COLWISE, else -1     */
+  int32_t rounding;   /* quantize: SNIP_RNE / SNIP_SR, else -1              */
+  double work;
+  double ms;
+} snip_launch_record;   /* 32 bytes */
+
+/* Start timing: creates `capacity` (1 .. 1<<20) event pairs on the current
+ * device and, until snip_timing_read, brackets every kernel launch of the
+ * library with an event pair (launches beyond `capacity` are counted, not
+ * timed; launches on a stream under graph capture are not timed). Adds a
+ * few microseconds per launch: for measurement runs, not for production.
+ * Process-global: do not time from several threads at once.
+ * Errors: SHAPE (capacity), HIP. */
+int snip_timing_start(int capacity);
+
+/* Stop timing, wait for the recorded events, copy up to `max` records
+ * (host array, in launch order) and release the events. Returns the number
+ * of records written (>= 0); *n_untimed (host, may be NULL) receives the
+ * number of launches that exceeded the capacity. Errors: HIP, FORMAT
+ * (timing was not started). */
+int snip_timing_read(snip_launch_record* out, int max, int64_t* n_untimed);
 
 /* Thread-local message for the last failed call ("" if none). */
 const char* snip_last_error(void);

@@ -11,6 +11,7 @@ the C entry points (include/snip.h):
   linear_fwd(x, w, fmt, ...)               -> y, stats[2]
   linear_bwd(dy, x, w, fmt_d, fmt_w, ...)  -> dx, dw, stats[4]
   layer_stats(stats)                       -> list of per-tensor reports
+  timing_start(capacity), timing_read()    -> per-launch kernel times
 
 The library is built in-tree by `python -m sub_byte_mixed_amd.build`. If it is
 missing, importing works but every call raises: there is no CPU fallback.
@@ -56,6 +57,14 @@ class TensorReport(ctypes.Structure):
                 ("below_sqrt3", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class LaunchRecord(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("format", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("work", ctypes.c_double), ("ms", ctypes.c_double)]
+
+
+LAUNCH_KINDS = {0: "amax", 1: "quantize", 2: "gemm", 3: "splitk", 4: "finalize"}
+
 STATS_BYTES = 24     # sizeof(snip_stats)
 
 _lib = None
@@ -82,6 +91,8 @@ _SIGS = {
     "snip_linear_bwd_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                                 _c.c_int]),
     "snip_qtensor_bytes": (_c.c_int64, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int]),
+    "snip_timing_start": (_c.c_int, [_c.c_int]),
+    "snip_timing_read": (_c.c_int, [_c.POINTER(LaunchRecord), _c.c_int, _c.POINTER(_c.c_int64)]),
     "snip_last_error": (_c.c_char_p, []),
     "snip_version": (_c.c_int, []),
 }
@@ -273,3 +284,24 @@ def workspace_bytes(op: str, *args) -> int:
 
 def version() -> int:
     return lib().snip_version()
+
+
+def timing_start(capacity: int = 4096) -> None:
+    """snip_timing_start: bracket every following kernel launch of the
+    library with a pair of HIP events (measurement runs only)."""
+    _check(lib().snip_timing_start(int(capacity)))
+
+
+def timing_read() -> Tuple[List[dict], int]:
+    """snip_timing_read: stop timing and return ([{kind, format, layout,
+    rounding, work, ms}, ...] in launch order, launches left untimed)."""
+    L = lib()
+    cap = 1 << 20
+    buf = (LaunchRecord * cap)()
+    untimed = ctypes.c_int64(0)
+    n = L.snip_timing_read(buf, cap, ctypes.byref(untimed))
+    if n < 0:
+        _check(n)
+    recs = [{"kind": LAUNCH_KINDS.get(r.kind, str(r.kind)), "format": r.format, "layout": r.layout,
+             "rounding": r.rounding, "work": r.work, "ms": r.ms} for r in buf[:n]]
+    return recs, int(untimed.value)

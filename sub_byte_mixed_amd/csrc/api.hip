@@ -18,6 +18,42 @@
 
 using namespace snip;
 
+// ================================================================ launch timing
+// Process-global recorder behind snip_timing_*: event pairs created up front,
+// handed out in launch order while enabled.
+namespace {
+struct TimingState {
+  bool on = false;
+  std::vector<hipEvent_t> ev;          // 2 per slot: start, stop
+  std::vector<LaunchTag> tag;
+  int used = 0;
+  int64_t untimed = 0;
+};
+TimingState g_timing;
+}  // namespace
+
+namespace snip {
+int timing_begin(const LaunchTag& t, hipStream_t s) {
+  if (!g_timing.on) return -1;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return -1;
+  if (g_timing.used >= (int)g_timing.tag.size()) {
+    ++g_timing.untimed;
+    return -1;
+  }
+  const int slot = g_timing.used++;
+  g_timing.tag[slot] = t;
+  if (hipEventRecord(g_timing.ev[2 * slot], s) != hipSuccess) {
+    g_timing.tag[slot].kind = -1;       // dropped on read
+  }
+  return slot;
+}
+void timing_end(int slot, hipStream_t s) {
+  if (slot < 0) return;
+  if (hipEventRecord(g_timing.ev[2 * slot + 1], s) != hipSuccess) g_timing.tag[slot].kind = -1;
+}
+}  // namespace snip
+
 namespace {
 
 thread_local std::string g_err;
@@ -166,6 +202,10 @@ int run_quant_group(const QPlan* const* ps, int n, hipStream_t s) {
   for (int i = n; i < kMaxJobs; ++i) jobs.j[i].wg0 = 1 << 30;
   jobs.n = n;
   const QPlan& p = *ps[0];
+  double elems = 0.0;
+  for (int i = 0; i < n; ++i) elems += (double)ps[i]->rows * (double)ps[i]->cols;
+  const int slot = timing_begin(LaunchTag{SNIP_LAUNCH_QUANTIZE, p.format, p.layout, p.sr ? SNIP_SR : SNIP_RNE,
+                                          elems}, s);
   hipError_t e;
   if (p.format == SNIP_BF16) {
     e = p.layout == SNIP_ROWWISE ? launch_bf16_copy(jobs, wg, s) : launch_bf16_transpose(jobs, wg, s);
@@ -174,6 +214,7 @@ int run_quant_group(const QPlan* const* ps, int n, hipStream_t s) {
   } else {
     e = launch_quant_col(p.format, p.sr, jobs, wg, s);
   }
+  timing_end(slot, s);
   return hip_check(e, "quantize launch");
 }
 
@@ -196,7 +237,12 @@ int run_amax(const APlan* ps, int n, hipStream_t s) {
   }
   for (int i = n; i < kMaxJobs; ++i) jobs.j[i].wg0 = 1 << 30;
   jobs.n = n;
-  return hip_check(launch_amax(jobs, wg, s), "amax launch");
+  double elems = 0.0;
+  for (int i = 0; i < n; ++i) elems += (double)ps[i].rows * (double)ps[i].cols;
+  const int slot = timing_begin(LaunchTag{SNIP_LAUNCH_AMAX, -1, -1, -1, elems}, s);
+  const hipError_t e = launch_amax(jobs, wg, s);
+  timing_end(slot, s);
+  return hip_check(e, "amax launch");
 }
 
 int run_finalize(const QPlan* const* ps, int n, hipStream_t s) {
@@ -206,7 +252,10 @@ int run_finalize(const QPlan* const* ps, int n, hipStream_t s) {
     if (!ps[i] || !ps[i]->stats) continue;
     f.j[f.n++] = FJob{ps[i]->part, ps[i]->nwg, ps[i]->stats};
   }
-  return hip_check(launch_finalize(f, s), "finalize launch");
+  const int slot = f.n ? timing_begin(LaunchTag{SNIP_LAUNCH_FINALIZE, -1, -1, -1, (double)f.n}, s) : -1;
+  const hipError_t e = launch_finalize(f, s);
+  timing_end(slot, s);
+  return hip_check(e, "finalize launch");
 }
 
 // Group passes by (layout, format, rounding) and launch each group once.
@@ -252,6 +301,59 @@ extern "C" {
 const char* snip_last_error(void) { return g_err.c_str(); }
 
 int snip_version(void) { return 100; }
+
+namespace {
+void timing_release() {
+  for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+  g_timing.ev.clear();
+  g_timing.tag.clear();
+  g_timing.used = 0;
+  g_timing.on = false;
+}
+}  // namespace
+
+int snip_timing_start(int capacity) {
+  if (capacity < 1 || capacity > (1 << 20))
+    return fail(SNIP_E_SHAPE, "snip_timing_start: capacity %d outside 1 .. 2^20", capacity);
+  timing_release();
+  g_timing.ev.reserve(2 * (size_t)capacity);
+  for (int i = 0; i < 2 * capacity; ++i) {
+    hipEvent_t e;
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      timing_release();
+      return hip_check(r, "snip_timing_start: hipEventCreate");
+    }
+    g_timing.ev.push_back(e);
+  }
+  g_timing.tag.assign((size_t)capacity, LaunchTag{-1, -1, -1, -1, 0.0});
+  g_timing.untimed = 0;
+  g_timing.on = true;
+  return ok();
+}
+
+int snip_timing_read(snip_launch_record* out, int max, int64_t* n_untimed) {
+  if (g_timing.ev.empty()) return fail(SNIP_E_FORMAT, "snip_timing_read: timing was not started");
+  if (max > 0 && !out) return fail(SNIP_E_NULL, "snip_timing_read: out is NULL");
+  g_timing.on = false;
+  int n = 0;
+  int rc = SNIP_OK;
+  for (int i = 0; i < g_timing.used; ++i) {
+    const LaunchTag& t = g_timing.tag[i];
+    if (t.kind < 0) continue;
+    hipError_t r = hipEventSynchronize(g_timing.ev[2 * i + 1]);
+    float ms = 0.0f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]);
+    if (r != hipSuccess) {
+      rc = hip_check(r, "snip_timing_read: event");
+      break;
+    }
+    if (n < max) out[n++] = snip_launch_record{t.kind, t.format, t.layout, t.rounding, t.work, (double)ms};
+  }
+  if (n_untimed) *n_untimed = g_timing.untimed;
+  timing_release();
+  return rc ? rc : (ok(), n);
+}
 
 int64_t snip_qtensor_bytes(int format, int64_t rows, int64_t k, int part) {
   if (!valid_format(format) || rows <= 0 || k <= 0 || (part != 0 && part != 1)) return -1;

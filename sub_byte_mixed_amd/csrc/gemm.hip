@@ -457,19 +457,24 @@ hipError_t launch_gemm(int format, const GemmArgs& g_in, hipStream_t s) {
   g.tiles_m = (int)ceil_div(g.M, p.bm);
   g.tiles_n = (int)ceil_div(g.N, p.bm);
   g.kchunk = p.kchunk;
+  if (format < SNIP_BF16 || format > SNIP_MXFP4) return hipErrorInvalidValue;
+  int slot = timing_begin(LaunchTag{SNIP_LAUNCH_GEMM, format, -1, -1, 2.0 * g.M * g.N * g.K}, s);
   switch (format) {
     case SNIP_NVFP4: launch_fmt<SNIP_NVFP4>(p, g, s); break;
     case SNIP_FP8_E4M3: launch_fmt<SNIP_FP8_E4M3>(p, g, s); break;
     case SNIP_MXFP4: launch_fmt<SNIP_MXFP4>(p, g, s); break;
-    case SNIP_BF16: launch_fmt<SNIP_BF16>(p, g, s); break;
-    default: return hipErrorInvalidValue;
+    default: launch_fmt<SNIP_BF16>(p, g, s); break;
   }
   hipError_t e = hipGetLastError();
+  timing_end(slot, s);
   if (e != hipSuccess || p.ksplit == 1) return e;
   int64_t wg = ceil_div(g.M * g.N, 256);
   if (wg > 4096) wg = 4096;
+  slot = timing_begin(LaunchTag{SNIP_LAUNCH_SPLITK, format, -1, -1, (double)(g.M * g.N)}, s);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)wg), dim3(256), 0, s, g, p.ksplit);
-  return hipGetLastError();
+  e = hipGetLastError();
+  timing_end(slot, s);
+  return e;
 }
 
 }  // namespace snip

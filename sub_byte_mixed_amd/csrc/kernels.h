@@ -101,6 +101,16 @@ hipError_t launch_bf16_transpose(const QJobs& jobs, int total_wg, hipStream_t s)
 hipError_t launch_finalize(const FJobs& jobs, hipStream_t s);
 hipError_t launch_gemm(int format, const GemmArgs& g, hipStream_t s);
 
+// Launch timing (snip_timing_*): when enabled, each launch is bracketed by
+// a pair of HIP events. timing_begin returns the slot to close with
+// timing_end (-1: not timed).
+struct LaunchTag {
+  int kind, format, layout, rounding;
+  double work;
+};
+int timing_begin(const LaunchTag& t, hipStream_t s);
+void timing_end(int slot, hipStream_t s);
+
 // Work decomposition helpers shared by host and kernels.
 constexpr int kColTileRows = 256;   // column-wise quantizer: source rows per tile
 constexpr int kColTileCols = 128;   // source columns per tile (2 per lane)

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     # and nothing else is exported under the snip_ prefix
@@ -153,3 +153,11 @@ def test_binding_requires_gpu_tensors():
     x = torch.zeros((16, 16), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         S.quantize(x, S.ROWWISE, S.NVFP4)
+
+
+def test_timing_argument_errors(L):
+    assert L.snip_timing_start(0) == -2
+    assert L.snip_timing_start((1 << 20) + 1) == -2
+    n = ctypes.c_int64(-1)
+    assert L.snip_timing_read(None, 0, ctypes.byref(n)) == -4     # not started
+    assert "not started" in err(L)

@@ -96,3 +96,33 @@ def test_layer_stats_report():
     _, _, st = S.linear_bwd(bad.cuda(), x.cuda(), w.cuda(), S.NVFP4, S.NVFP4, 0, 0)
     reps, nonfinite = S.layer_stats(st)
     assert nonfinite and reps[0]["n_nonfinite"] == 1
+
+
+def test_launch_timing_records():
+    """snip_timing_*: every launch of a forward + backward is recorded in
+    order with its kind, format and algorithmic work, and outputs are the
+    same as untimed."""
+    wl = synth.WORKLOADS["linear512"]
+    x, w, dy = (t.cuda() for t in synth.gen_layer(wl, 0))
+    T, din, dout = x.shape[0], x.shape[1], w.shape[0]
+    say("timing case linear512 NVFP4")
+    y0, _ = S.linear_fwd(x, w, S.NVFP4, 0, 0)
+    torch.cuda.synchronize()
+    S.timing_start(64)
+    y1, st_f = S.linear_fwd(x, w, S.NVFP4, 0, 0)
+    S.linear_bwd(dy, x, w, S.NVFP4, S.NVFP4, 0, 0, fwd_stats=st_f)
+    recs, untimed = S.timing_read()
+    assert untimed == 0
+    assert torch.equal(y0, y1)
+    kinds = [r["kind"] for r in recs]
+    gemms = [r for r in recs if r["kind"] == "gemm"]
+    assert [g["work"] for g in gemms] == [2.0 * T * din * dout] * 3
+    assert all(g["format"] == S.NVFP4 for g in gemms)
+    assert kinds[0] == "amax" and "quantize" in kinds and "finalize" in kinds
+    q = [r for r in recs if r["kind"] == "quantize"]
+    # forward: X, W; backward: dY, W^T, dY^T, X^T (elements read)
+    assert sum(r["work"] for r in q) == float(2 * T * din + 2 * dout * din + 2 * T * dout)
+    assert all(r["ms"] > 0.0 for r in recs)
+    # timing is off again: a further read is an error
+    with pytest.raises(S.SnipError):
+        S.timing_read()
