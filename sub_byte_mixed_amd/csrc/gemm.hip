@@ -9,98 +9,103 @@
 //   NVFP4  code x E4M3 scale is decoded exactly into fp16 (a product of a
 //          2-significant-bit E2M1 value and a 4-bit E4M3 scale spans at most
 //          6 significant bits within [2^-10, 2688]) and multiplied on
-//          v_mfma_f32_16x16x32_f16. Decoding: v_cvt_scalef32_pk_f16_fp4 with
-//          the power-of-two part of the scale, then v_pk_mul_f16 by the
-//          mantissa part. The gfx950 FP4 MFMA takes only power-of-two scales
-//          per 32 elements, which cannot represent E4M3 scales per 16.
+//          v_mfma_f32_16x16x32_f16. Decoding: v_cvt_scalef32_pk_f16_fp4 of
+//          the codes and v_cvt_scalef32_pk_f16_fp8 of the two scale bytes a
+//          lane needs, then v_pk_mul_f16. The gfx950 FP4 MFMA takes only
+//          power-of-two scales per 32 elements, which cannot represent E4M3
+//          scales per 16.
 //   FP8    E4M3 codes are decoded exactly into fp16 (v_cvt_scalef32_pk_f16_fp8)
-//          and multiplied on v_mfma_f32_16x16x32_f16. The gfx950 8-bit MFMA
-//          (v_mfma_*_f8f6f4) sums its 128 products with only ~12 bits below
-//          the largest product, measured at up to 1e-4 of sum|a||b|: outside
-//          the 1e-5 bound, so it is not used for E4M3 x E4M3.
+//          and multiplied on v_mfma_f32_16x16x32_f16. The gfx950 8-bit MFMAs
+//          (v_mfma_*_f8f6f4, and v_mfma_f32_16x16x32_fp8_fp8 as well) align
+//          their products to the largest one with too few bits: measured up
+//          to 4e-4 of sum|a||b| on E4M3 data of full range, outside the 1e-5
+//          bound, so they are not used for E4M3 x E4M3.
 //   MXFP4  E2M1 codes and E8M0 scales go straight into
 //          v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 operands, one scale per row
 //          and 32-element K block).
 //   BF16   v_mfma_f32_16x16x32_bf16.
 //
-// Tiling: a workgroup of 256 threads (2x2 waves) owns a BM x BN output tile
-// (256x256 for large problems, 128x128 otherwise) and walks K in stages of
-// BK elements (64; 128 for MX). Stages are double-buffered in LDS: the global
-// loads of stage s+1 are issued into registers before the MFMAs of stage s,
-// and written to the other LDS buffer afterwards, so one barrier per stage
-// suffices. NVFP4 block scales are split into (2^e as fp32, mantissa as
-// fp16x2) once, when they are staged in LDS. Within a stage, lane group
-// g = lane/16 owns the K slice [g*BK/4, (g+1)*BK/4) of its row; A and B use
-// the same K assignment, so every dot product is a permutation of the K sum.
+// Data movement. Operands are staged in LDS by direct global-to-LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane),
+// so staging takes no VGPRs and no LDS write instructions. The unit of
+// staging is 16 rows x 64 bytes of one operand (1 KiB): lane l fetches the
+// 16 bytes of row l % 16 at byte offset 16 * (l / 16) of the row's 64. The
+// MFMA-side read of a unit is then one ds_read_b128 per lane at 16 * lane:
+// lane (r16 = l % 16, grp = l / 16) gets exactly the K slice grp of row r16
+// that the 16x16 MFMA operand layout asks for (measured free of LDS bank
+// conflicts on MI355X; the row-pitched layouts it replaces were not). A and
+// B use the same K slices, so every dot product is a permutation of the
+// K sum. A unit covers K = 32 (BF16), 64 (FP8) or 128 (FP4) elements, and
+// one K stage is one unit per 16-row block; block scales travel with it
+// (8 E4M3 bytes or 4 E8M0 bytes per row and unit, dword DMA).
 //
-// Tile order: the hardware hands workgroups to the 8 XCDs round-robin; tile
-// ids are remapped so each XCD works on a contiguous range, and tiles are
-// ordered in groups of 8 tile-rows so that concurrently running tiles share
-// A and B panels in that XCD's L2. Skinny problems split K across
+// Pipeline: S stages in a ring. The loads of stage k + S - 1 are issued
+// right after the barrier that opens stage k, so S - 1 stages are in flight
+// while one is multiplied. Before the barrier each wave waits (vmcnt) only
+// for its own loads of stage k; the barrier then makes every wave's loads
+// visible and guarantees that the ring slot about to be refilled is no
+// longer read.
+//
+// Tiling: a workgroup of 256 threads (2x2 waves) owns a BM x BN output tile:
+// 256x256 (one workgroup per CU) or 128x128 (two per CU), as plan_gemm
+// decides from the problem's tile rounds. Tile order: the hardware hands workgroups to the 8 XCDs
+// round-robin; tile ids are remapped so each XCD works on a contiguous range,
+// and tiles are ordered in groups of 8 tile-rows so that concurrently running
+// tiles share A and B panels in that XCD's L2. Skinny problems split K across
 // workgroups into fp32 partials that a second kernel sums in a fixed order.
-#include "device.h"
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace snip {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef int intx8_t __attribute__((ext_vector_type(8)));
-
 constexpr int NT = 256;
 
-// Code bytes per row for BK elements of K, and scale bytes per row.
-template <int FMT, int BK> struct KStage;
-template <int BK> struct KStage<SNIP_NVFP4, BK>    { static constexpr int CB = BK / 2, NS = BK / 16; };
-template <int BK> struct KStage<SNIP_FP8_E4M3, BK> { static constexpr int CB = BK,     NS = 0; };
-template <int BK> struct KStage<SNIP_BF16, BK>     { static constexpr int CB = BK * 2, NS = 0; };
-template <int BK> struct KStage<SNIP_MXFP4, BK>    { static constexpr int CB = BK / 2, NS = BK / 32; };
+// Staging unit per format: K elements per 64-byte row segment (UE), MFMAs
+// per fragment pair and unit (NQ), block-scale bytes per row and unit (SB).
+template <int FMT> struct Unit;
+template <> struct Unit<SNIP_BF16>     { static constexpr int UE = 32,  NQ = 1, SB = 0; };
+template <> struct Unit<SNIP_FP8_E4M3> { static constexpr int UE = 64,  NQ = 2, SB = 0; };
+template <> struct Unit<SNIP_NVFP4>    { static constexpr int UE = 128, NQ = 4, SB = 8; };
+template <> struct Unit<SNIP_MXFP4>    { static constexpr int UE = 128, NQ = 1, SB = 4; };
 
-// Per-format kernel configuration, chosen from measured sweeps on MI355X:
-//   NVFP4  256x256 tiles (one workgroup per CU) halve the in-register decode
-//          per MFMA; 128x128 for problems with fewer than 192 big tiles.
-//   FP8    decode is half as costly, so 128x128 tiles with two workgroups per
-//          CU (better latency hiding) win at every size.
-//   MX     no decode: 128x128 tiles, two per CU, K stage of 256.
-//   BF16   as NVFP4 (256x256 when the problem is large).
-
-// K per LDS stage: 64, except MX-FP4 (one MFMA covers K = 128), which takes
-// 256 when K allows it and 128 otherwise. The API guarantees K % 128 == 0.
-static int stage_k(int format, int64_t K) {
-  if (format == SNIP_MXFP4) return (K % 256 == 0) ? 256 : 128;
-  return 64;
-}
-static bool big_tiles_allowed(int format) { return format == SNIP_NVFP4 || format == SNIP_BF16; }
-
-
-// E4M3 scale code -> {fp32 bits of its power-of-two part, fp16x2 bits of its
-// mantissa part} with value = p2 * m exactly; subnormal codes are c * 2^-9.
-__device__ __forceinline__ uint2 split_e4m3(uint32_t c) {
-  uint32_t p2, m;
-  if (c >= 8u) {
-    p2 = ((c >> 3) + 120u) << 23;                 // 2^((c>>3) - 7)
-    m = 0x3C00u | ((c & 7u) << 7);                 // fp16 1 + (c&7)/8
-  } else {
-    p2 = 118u << 23;                               // 2^-9
-    m = __builtin_bit_cast(uint16_t, (_Float16)(float)c);
-  }
-  return make_uint2(p2, m | (m << 16));
+static int unit_k(int format) {
+  return format == SNIP_BF16 ? 32 : format == SNIP_FP8_E4M3 ? 64 : 128;
 }
 
-// 8 E2M1 nibbles (one 32-bit word) -> 8 fp16 values code * p2 * m.
-__device__ __forceinline__ half8_t decode8(uint32_t w, uint2 s) {
-  const float p2 = __uint_as_float(s.x);
-  const half2_t m = __builtin_bit_cast(half2_t, s.y);
-  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 0) * m;
-  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 1) * m;
-  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 2) * m;
-  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, p2, 3) * m;
+// Direct global -> LDS loads: lane l's 16 (4) bytes land at LDS byte
+// address lds + 16 * l (4 * l); `lds` is wave-uniform (it goes to M0).
+// Issued as asm so that the compiler, which cannot tell the ring slots
+// apart, does not drain every load in flight before each LDS read; the
+// waits for these loads are the explicit vmcnt waits of the main loop. One
+// wait state separates the M0 write from the load that reads it.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// and all its LDS reads have returned, then barrier. One asm statement with
+// a memory clobber, so that no LDS access moves across it and no implicit
+// full drain of the loads in flight is added.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// 8 E2M1 nibbles (one word) times an fp16 scale pair {s, s}: 8 exact fp16.
+__device__ __forceinline__ half8_t decode_fp4(uint32_t w, half2_t s) {
+  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
   return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-// 8 E4M3 codes (two 32-bit words) -> 8 fp16 values (exact).
+// 8 E4M3 codes (two words) -> 8 fp16 values (exact).
 __device__ __forceinline__ half8_t fp8x8_to_half8(uint32_t w0, uint32_t w1) {
   const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
   const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
@@ -109,115 +114,127 @@ __device__ __forceinline__ half8_t fp8x8_to_half8(uint32_t w0, uint32_t w1) {
   return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-// Tile id -> (tile row, tile column).
-__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  constexpr int GM = 8;
-  const int group = id / (GM * tiles_n);
-  const int first = group * GM;
-  const int gm = (tiles_m - first) < GM ? (tiles_m - first) : GM;
-  const int r = id - group * GM * tiles_n;
-  tm = first + r % gm;
-  tn = r / gm;
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
+  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-template <int FMT, int BM, int BN, int BK>
+template <int FMT, int BM, int BN, int S, int UK>
 __global__ __launch_bounds__(NT, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs g) {
-  constexpr int CB = KStage<FMT, BK>::CB, NS = KStage<FMT, BK>::NS;
-  constexpr int KG = BK / 4;                                    // K per lane group per stage
-  constexpr int NSUB = (FMT == SNIP_MXFP4) ? KG / 32 : KG / 8;  // MFMAs along K per stage
-  constexpr int WM = BM / 2, WN = BN / 2;            // wave tile
-  constexpr int TM = WM / 16, TN = WN / 16;          // 16x16 MFMA tiles per wave
-  constexpr int PITCH = CB + 16;                     // LDS bytes per row (codes)
-  constexpr int CPA = BM * CB / 16 / NT;             // 16-byte chunks per thread (A)
-  constexpr int CPB = BN * CB / 16 / NT;
-  static_assert(CPA >= 1 && CPB >= 1, "tile too small");
-  // NVFP4 scales are staged decoded (8 bytes each), MX scales raw (1 byte)
-  constexpr int SBYTES = (FMT == SNIP_NVFP4) ? 8 : 1;
-  constexpr int LA = BM * PITCH, LB = BN * PITCH;
-  constexpr int LSA = NS ? BM * NS * SBYTES : 0, LSB = NS ? BN * NS * SBYTES : 0;
+  using U = Unit<FMT>;
+  constexpr int UE = U::UE, NQ = U::NQ, SB = U::SB;
+  constexpr int RBA = BM / 16, RBB = BN / 16;              // 16-row blocks per tile
+  constexpr int NUA = RBA * UK, NUB = RBB * UK;            // code units per stage
+  constexpr int LA = NUA * 1024, LB = NUB * 1024;          // code bytes per stage
+  constexpr int LSA = NUA * 16 * SB, LSB = NUB * 16 * SB;  // scale bytes per stage
   constexpr int STAGE = LA + LB + LSA + LSB;
-  __shared__ __align__(16) uint8_t smem[2 * STAGE];
-  // E4M3 code -> (2^e, mantissa) table for NVFP4 scales, built once
-  __shared__ uint2 lut[FMT == SNIP_NVFP4 ? 256 : 1];
-  if constexpr (FMT == SNIP_NVFP4) {
-    lut[threadIdx.x] = split_e4m3(threadIdx.x);
-    __syncthreads();
-  }
+  // DMA instructions per stage and wave: code units of A and of B, then
+  // scale instructions (a dword per lane covers 256 bytes of scales)
+  constexpr int NSA = LSA / 256, NSB = LSB / 256;
+  constexpr int IA = NUA / 4, IB = NUB / 4, IS = (NSA + NSB) / 4;
+  constexpr int NIW = IA + IB + IS;
+  static_assert(NUA % 4 == 0 && NUB % 4 == 0 && (NSA + NSB) % 4 == 0, "DMA split over 4 waves");
+  static_assert(LSA % 256 == 0 && LSB % 256 == 0, "scale staging granularity");
+  static_assert(S >= 2 && NIW * (S > 2 ? S - 2 : 0) <= 63, "ring depth");
+  constexpr int WM = BM / 2, WN = BN / 2;                  // wave tile
+  constexpr int TM = WM / 16, TN = WN / 16;                // 16x16 MFMA tiles per wave
+  constexpr int KS = UE * UK;                              // K elements per stage
+  __shared__ __align__(1024) uint8_t smem[S * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int r16 = lane & 15, grp = lane >> 4;
   int tm, tn;
   tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t rowbytes = (int64_t)g.K * CB / BK;
-  const int kt0 = blockIdx.y * g.kchunk / BK;
-  const int kt1 = min((int)(g.K / BK), (int)((blockIdx.y + 1) * g.kchunk / BK));
+  const int64_t rowbytes = g.K / UE * 64;                  // code bytes per row
+  const int64_t srow = SB ? g.K / UE * SB : 0;             // scale bytes per row
+  const int kt0 = (int)(blockIdx.y * g.kchunk / KS);
+  const int kt1 = min((int)(g.K / KS), (int)((blockIdx.y + 1) * g.kchunk / KS));
   const int nk = kt1 - kt0;
 
-  uint4 ra[CPA], rb[CPB];
-  uint2 sa = make_uint2(0u, 0u), sb = make_uint2(0u, 0u);
-
-  auto gload = [&](int kt) {
+  // Per-lane DMA sources of this wave's instructions: wave w loads the code
+  // units w, w + 4, ... of A and of B (unit index = row block * UK + unit
+  // of the stage), and scale instructions w, w + 4, ... of the list
+  // [A scales, B scales]. Offsets are 32-bit (the host keeps every operand
+  // below 4 GiB). Rows past M or N load row M-1 / N-1 instead (in bounds);
+  // their products are never stored.
+  uint32_t offa[IA], offb[IB], offs[IS > 0 ? IS : 1];
 #pragma unroll
-    for (int i = 0; i < CPA; ++i) {
-      const int c = tid + i * NT, row = c / (CB / 16), cc = c % (CB / 16);
-      ra[i] = (m0 + row < g.M)
-                  ? *reinterpret_cast<const uint4*>(g.a + (m0 + row) * rowbytes + (int64_t)kt * CB + cc * 16)
-                  : make_uint4(0u, 0u, 0u, 0u);
-    }
+  for (int t = 0; t < IA; ++t) {
+    const int idx = wave + 4 * t;
+    offa[t] = (uint32_t)(min(m0 + (idx / UK) * 16 + r16, g.M - 1) * rowbytes) + (idx % UK) * 64 + grp * 16;
+  }
 #pragma unroll
-    for (int i = 0; i < CPB; ++i) {
-      const int c = tid + i * NT, row = c / (CB / 16), cc = c % (CB / 16);
-      rb[i] = (n0 + row < g.N)
-                  ? *reinterpret_cast<const uint4*>(g.b + (n0 + row) * rowbytes + (int64_t)kt * CB + cc * 16)
-                  : make_uint4(0u, 0u, 0u, 0u);
-    }
-    if constexpr (NS == 4) {          // 4 scale bytes per row per stage
-      const int64_t srow = g.K / (FMT == SNIP_NVFP4 ? 16 : 32);
-      if (tid < BM) sa.x = (m0 + tid < g.M) ? *reinterpret_cast<const uint32_t*>(g.as + (m0 + tid) * srow + kt * 4) : 0u;
-      if (tid < BN) sb.x = (n0 + tid < g.N) ? *reinterpret_cast<const uint32_t*>(g.bs + (n0 + tid) * srow + kt * 4) : 0u;
-    } else if constexpr (NS == 8) {   // 8 scale bytes per row per stage
-      const int64_t srow = g.K / (FMT == SNIP_NVFP4 ? 16 : 32);
-      if (tid < BM) sa = (m0 + tid < g.M) ? *reinterpret_cast<const uint2*>(g.as + (m0 + tid) * srow + kt * 8) : make_uint2(0u, 0u);
-      if (tid < BN) sb = (n0 + tid < g.N) ? *reinterpret_cast<const uint2*>(g.bs + (n0 + tid) * srow + kt * 8) : make_uint2(0u, 0u);
+  for (int t = 0; t < IB; ++t) {
+    const int idx = wave + 4 * t;
+    offb[t] = (uint32_t)(min(n0 + (idx / UK) * 16 + r16, g.N - 1) * rowbytes) + (idx % UK) * 64 + grp * 16;
+  }
+#pragma unroll
+  for (int t = 0; t < IS; ++t) {
+    const int pp = wave + 4 * t;
+    const bool isa = pp < NSA;
+    const int p = isa ? pp : pp - NSA;
+    // scale blocks [16 rows][SB bytes], one per code unit: NVFP4 2 blocks
+    // per instruction, MX 4
+    const int blk = SB == 8 ? 2 * p + (lane >> 5) : 4 * p + (lane >> 4);
+    const int r = SB == 8 ? (lane & 31) >> 1 : lane & 15;
+    const int part = SB == 8 ? (lane & 1) * 4 : 0;
+    const int64_t row = isa ? min(m0 + (blk / UK) * 16 + r, g.M - 1) : min(n0 + (blk / UK) * 16 + r, g.N - 1);
+    offs[t] = (uint32_t)(row * srow) + (blk % UK) * SB + part;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto issue = [&](int kt, int slot) {
+    const uint32_t base = lds0 + slot * STAGE;
+#pragma unroll
+    for (int t = 0; t < IA; ++t) dma16(g.a + (int64_t)kt * UK * 64 + offa[t], base + (wave + 4 * t) * 1024);
+#pragma unroll
+    for (int t = 0; t < IB; ++t)
+      dma16(g.b + (int64_t)kt * UK * 64 + offb[t], base + LA + (wave + 4 * t) * 1024);
+#pragma unroll
+    for (int t = 0; t < IS; ++t) {
+      const int pp = wave + 4 * t;                       // wave-uniform
+      if (pp < NSA) dma4(g.as + (int64_t)kt * UK * SB + offs[t], base + LA + LB + pp * 256);
+      else dma4(g.bs + (int64_t)kt * UK * SB + offs[t], base + LA + LB + LSA + (pp - NSA) * 256);
     }
   };
-  auto sstore = [&](int buf) {
-    uint8_t* la = smem + buf * STAGE;
-    uint8_t* lb = la + LA;
+
+  // Fragments of one unit in registers: A and B code slices (16 bytes per
+  // lane) and the lane's block scales (NVFP4: two per fragment as fp16).
+  struct Frags {
+    uint4 a[TM], b[TN];
+    half2_t sa[SB == 8 ? TM : 1], sb[SB == 8 ? TN : 1];
+    int xa[SB == 4 ? TM : 1], xb[SB == 4 ? TN : 1];
+  };
+  auto load = [&](Frags& f, int slot, int u) {        // B first: decoded first
+    const uint8_t* base = smem + slot * STAGE;
+    const uint8_t* la = base + ((wm * TM) * UK + u) * 1024 + lane * 16;
+    const uint8_t* lb = base + LA + ((wn * TN) * UK + u) * 1024 + lane * 16;
 #pragma unroll
-    for (int i = 0; i < CPA; ++i) {
-      const int c = tid + i * NT, row = c / (CB / 16), cc = c % (CB / 16);
-      *reinterpret_cast<uint4*>(la + row * PITCH + cc * 16) = ra[i];
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const uint4*>(lb + j * UK * 1024);
+    if constexpr (SB == 8) {        // lane (r16, grp): blocks 2grp, 2grp+1 of its row
+      const uint8_t* sb = base + LA + LB + LSA + (((wn * TN) * UK + u) * 16 + r16) * 8 + grp * 2;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        f.sb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+            (uint32_t)*reinterpret_cast<const uint16_t*>(sb + j * UK * 128), 1.0f, false);
+    } else if constexpr (SB == 4) { // lane (r16, grp): block grp of its row
+      const uint8_t* sb = base + LA + LB + LSA + (((wn * TN) * UK + u) * 16 + r16) * 4 + grp;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) f.xb[j] = sb[j * UK * 64];
     }
 #pragma unroll
-    for (int i = 0; i < CPB; ++i) {
-      const int c = tid + i * NT, row = c / (CB / 16), cc = c % (CB / 16);
-      *reinterpret_cast<uint4*>(lb + row * PITCH + cc * 16) = rb[i];
-    }
-    if constexpr (FMT == SNIP_NVFP4) {
-      uint2* lsa = reinterpret_cast<uint2*>(lb + LB);
-      uint2* lsb = reinterpret_cast<uint2*>(lb + LB + LSA);
-      if (tid < BM) {
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const uint4*>(la + i * UK * 1024);
+    if constexpr (SB == 8) {
+      const uint8_t* sa = base + LA + LB + (((wm * TM) * UK + u) * 16 + r16) * 8 + grp * 2;
 #pragma unroll
-        for (int q = 0; q < NS; ++q) lsa[tid * NS + q] = lut[((q < 4 ? sa.x : sa.y) >> (8 * (q & 3))) & 0xFFu];
-      }
-      if (tid < BN) {
+      for (int i = 0; i < TM; ++i)
+        f.sa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+            (uint32_t)*reinterpret_cast<const uint16_t*>(sa + i * UK * 128), 1.0f, false);
+    } else if constexpr (SB == 4) {
+      const uint8_t* sa = base + LA + LB + (((wm * TM) * UK + u) * 16 + r16) * 4 + grp;
 #pragma unroll
-        for (int q = 0; q < NS; ++q) lsb[tid * NS + q] = lut[((q < 4 ? sb.x : sb.y) >> (8 * (q & 3))) & 0xFFu];
-      }
-    } else if constexpr (FMT == SNIP_MXFP4) {
-      if (tid < BM) {
-        if constexpr (NS == 4) *reinterpret_cast<uint32_t*>(lb + LB + tid * 4) = sa.x;
-        else *reinterpret_cast<uint2*>(lb + LB + tid * 8) = sa;
-      }
-      if (tid < BN) {
-        if constexpr (NS == 4) *reinterpret_cast<uint32_t*>(lb + LB + LSA + tid * 4) = sb.x;
-        else *reinterpret_cast<uint2*>(lb + LB + LSA + tid * 8) = sb;
-      }
+      for (int i = 0; i < TM; ++i) f.xa[i] = sa[i * UK * 64];
     }
   };
 
@@ -227,164 +244,82 @@ __global__ __launch_bounds__(NT, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs g)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) {
-    gload(kt0);
-    sstore(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nk) gload(kt0 + it + 1);
-    const uint8_t* la = smem + buf * STAGE;
-    const uint8_t* lb = la + LA;
-
+  // Decoded fp16 fragments (NVFP4, FP8): A_i or B_j for K slice q.
+  auto dec_a = [&](const Frags& f, int q, int i) -> half8_t {
     if constexpr (FMT == SNIP_NVFP4) {
-      // lane group g: K slice [g*KG, (g+1)*KG): KG/2 code bytes, KG/16 blocks
-      constexpr int W = KG / 8;                        // code words per lane per tile
-      const uint2* lsa = reinterpret_cast<const uint2*>(lb + LB);
-      const uint2* lsb = reinterpret_cast<const uint2*>(lb + LB + LSA);
-      uint32_t ca[TM][W], cbv[TN][W];
-      uint2 sca[TM][W / 2], scb[TN][W / 2];
+      const _Float16 s = q < 2 ? f.sa[i][0] : f.sa[i][1];
+      return decode_fp4(word_of(f.a[i], q), half2_t{s, s});
+    } else {
+      return fp8x8_to_half8(word_of(f.a[i], 2 * q), word_of(f.a[i], 2 * q + 1));
+    }
+  };
+  auto dec_b = [&](const Frags& f, int q, int j) -> half8_t {
+    if constexpr (FMT == SNIP_NVFP4) {
+      const _Float16 s = q < 2 ? f.sb[j][0] : f.sb[j][1];
+      return decode_fp4(word_of(f.b[j], q), half2_t{s, s});
+    } else {
+      return fp8x8_to_half8(word_of(f.b[j], 2 * q), word_of(f.b[j], 2 * q + 1));
+    }
+  };
+
+  // One stage's MFMAs, in rows (q, i): fragment A_i against every B_j for
+  // K slice q; the B fragments of a slice are decoded once, at its first row.
+  auto run_stage = [&](const Frags& f) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      half8_t bd[TN];
+      if constexpr (FMT == SNIP_NVFP4 || FMT == SNIP_FP8_E4M3) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bd[j] = dec_b(f, q, j);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 16 + r16;
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(la + row * PITCH + grp * (KG / 2));
-#pragma unroll
-        for (int w = 0; w < W; ++w) ca[i][w] = p[w];
-#pragma unroll
-        for (int q = 0; q < W / 2; ++q) sca[i][q] = lsa[row * NS + grp * (W / 2) + q];
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int row = wn * WN + j * 16 + r16;
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(lb + row * PITCH + grp * (KG / 2));
-#pragma unroll
-        for (int w = 0; w < W; ++w) cbv[j][w] = p[w];
-#pragma unroll
-        for (int q = 0; q < W / 2; ++q) scb[j][q] = lsb[row * NS + grp * (W / 2) + q];
-      }
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        half8_t af[TM], bf[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = decode8(ca[i][s], sca[i][s / 2]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = decode8(cbv[j][s], scb[j][s / 2]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
+        if constexpr (FMT == SNIP_NVFP4 || FMT == SNIP_FP8_E4M3) {
+          const half8_t ad = dec_a(f, q, i);
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
-    } else if constexpr (FMT == SNIP_FP8_E4M3) {
-      // lane group g: K slice [g*KG, (g+1)*KG): KG code bytes
-      constexpr int W = KG / 4;
-      uint32_t ca[TM][W], cbv[TN][W];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(la + (wm * WM + i * 16 + r16) * PITCH + grp * KG);
-#pragma unroll
-        for (int w = 0; w < W; ++w) ca[i][w] = p[w];
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(lb + (wn * WN + j * 16 + r16) * PITCH + grp * KG);
-#pragma unroll
-        for (int w = 0; w < W; ++w) cbv[j][w] = p[w];
-      }
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        half8_t af[TM], bf[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = fp8x8_to_half8(ca[i][2 * s], ca[i][2 * s + 1]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[j] = fp8x8_to_half8(cbv[j][2 * s], cbv[j][2 * s + 1]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ad, bd[j], acc[i][j], 0, 0, 0);
+        } else if constexpr (FMT == SNIP_BF16) {
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
-    } else if constexpr (FMT == SNIP_BF16) {
-      // lane group g: K slice [g*KG, (g+1)*KG): 2*KG bytes
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.a[i]),
+                                                                __builtin_bit_cast(bf16x8_t, f.b[j]),
+                                                                acc[i][j], 0, 0, 0);
+        } else {  // MXFP4: one scaled MFMA (K = 128) per fragment pair
+          const intx8_t av = {(int)f.a[i].x, (int)f.a[i].y, (int)f.a[i].z, (int)f.a[i].w, 0, 0, 0, 0};
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        bf16x8_t af[TM], bf[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(la + (wm * WM + i * 16 + r16) * PITCH + grp * 2 * KG + s * 16);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bf[j] = *reinterpret_cast<const bf16x8_t*>(lb + (wn * WN + j * 16 + r16) * PITCH + grp * 2 * KG + s * 16);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
-    } else {  // MXFP4: lane group g owns NSUB 32-blocks; one scaled MFMA covers K = 128
-      const uint8_t* lsa = lb + LB;
-      const uint8_t* lsb = lb + LB + LSA;
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        intx8_t af[TM], bf[TN];
-        int sva[TM], svb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = wm * WM + i * 16 + r16;
-          const uint4 v = *reinterpret_cast<const uint4*>(la + row * PITCH + s * 64 + grp * 16);
-          af[i] = intx8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          sva[i] = lsa[row * NS + s * 4 + grp];
+          for (int j = 0; j < TN; ++j) {
+            const intx8_t bv = {(int)f.b[j].x, (int)f.b[j].y, (int)f.b[j].z, (int)f.b[j].w, 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0,
+                                                                         f.xa[i], 0, f.xb[j]);
+          }
         }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int row = wn * WN + j * 16 + r16;
-          const uint4 v = *reinterpret_cast<const uint4*>(lb + row * PITCH + s * 64 + grp * 16);
-          bf[j] = intx8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          svb[j] = lsb[row * NS + s * 4 + grp];
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 4, 4,
-                                                                         0, sva[i], 0, svb[j]);
       }
     }
+  };
 
-    if (it + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+  // Stage `it`: wait for this wave's loads of `it` (later stages may still
+  // be in flight: stages up to it+S-2 have been issued), barrier (every
+  // wave's loads of `it` are in LDS, and every wave has finished reading
+  // stage it-1), refill stage it-1's slot with stage it+S-1, read the
+  // fragments and multiply.
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(kt0 + s, s);
+  for (int it = 0; it < nk; ++it) {
+    const int ahead = min(S - 2, nk - 1 - it);         // stages issued after it
+    if (S > 2 && ahead >= S - 2) wait_vm_barrier<NIW * (S > 2 ? S - 2 : 0)>();
+    else if (S > 3 && ahead == 1) wait_vm_barrier<NIW>();
+    else wait_vm_barrier<0>();
+    if (it + S - 1 < nk) issue(kt0 + it + S - 1, (it + S - 1) % S);
+    Frags f[UK];
+#pragma unroll
+    for (int u = 0; u < UK; ++u) load(f[u], it % S, u);
+#pragma unroll
+    for (int u = 0; u < UK; ++u) run_stage(f[u]);
   }
 
-  // epilogue: lane holds rows 4*grp + v, column r16 of each 16x16 tile
-  if (g.kchunk >= g.K) {
-    const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = n0 + wn * WN + j * 16 + r16;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t row = m0 + wm * WM + i * 16 + 4 * grp + v;
-          if (row < g.M && col < g.N) g.c[row * g.ldc + col] = ldexpf(acc[i][j][v], e);
-        }
-      }
-  } else {
-    float* part = g.partial + (int64_t)blockIdx.y * g.M * g.N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t col = n0 + wn * WN + j * 16 + r16;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t row = m0 + wm * WM + i * 16 + 4 * grp + v;
-          if (row < g.M && col < g.N) part[row * g.N + col] = acc[i][j][v];
-        }
-      }
-  }
+  store_tile<TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, r16, grp);
 }
 
 // Split-K reduction: C = 2^(ea+eb) * sum over splits, in split order.
@@ -399,28 +334,57 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nspl
   }
 }
 
-// Host-side plan: tile shape and K split for a problem.
+// Host-side plan: kernel, tile shape and K split for a problem.
+//
+// A CU holds one 256x256 workgroup or two 128x128 ones, so a launch runs in
+// rounds of 256 big or 512 small tiles. Per unit of tile area a round of
+// big tiles is faster by big_tile_gain (measured on MI355X: less decode and
+// operand traffic per MFMA for the LDS-DMA kernel; for MX-FP4 and BF16 the
+// small tiles run on the register-staged kernel, gemm_staged.hip, which
+// nearly matches it). A last, partial round of small tiles costs a full
+// round when more than 256 tiles remain (two per CU) and about 0.6 of one
+// otherwise (one per CU, running faster alone). The plan takes the cheaper
+// shape; problems with fewer than 192 small tiles split K so that about
+// 256 workgroups run.
+static double big_tile_gain(int format) {
+  switch (format) {
+    case SNIP_NVFP4: return 1.06;
+    case SNIP_FP8_E4M3: return 1.15;
+    case SNIP_MXFP4: return 1.03;
+    default: return 1.02;
+  }
+}
+
 GemmPlan plan_gemm(int format, int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
-  const int bk = stage_k(format, K);
-  p.bk = bk;
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
-  if (big_tiles_allowed(format) && t256 >= 192) {
+  const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
+  const int64_t rem = t128 % 512;
+  const double time128 = (double)(t128 / 512) + (rem == 0 ? 0.0 : rem <= 256 ? 0.6 : 1.0);
+  const double time256 = (double)ceil_div(t256, 256) * 2.0 / big_tile_gain(format);
+  p.staged = 0;
+  if (t128 >= 192 && time256 < time128) {
     p.bm = 256;
+    p.bk = unit_k(format);
     p.tiles = t256;
     p.ksplit = 1;
     p.kchunk = K;
     return p;
   }
   p.bm = 128;
-  p.tiles = ceil_div(M, 128) * ceil_div(N, 128);
+  p.tiles = t128;
+  p.staged = (format == SNIP_MXFP4 || format == SNIP_BF16) ? 1 : 0;
   int64_t split = p.tiles >= 192 ? 1 : 256 / p.tiles;
-  const int64_t max_split = K / (4 * bk);                 // keep >= 4 stages per split
+  // split in whole stages (the staged MX kernel then runs 128-element
+  // stages), at least 4 per split
+  const int64_t gran = p.staged ? (format == SNIP_MXFP4 ? 128 : 64) : unit_k(format);
+  const int64_t max_split = K / (4 * gran);
   if (split > max_split) split = max_split;
   if (split < 1) split = 1;
-  const int64_t chunk = ceil_div(ceil_div(K, split), bk) * bk;
+  const int64_t chunk = ceil_div(ceil_div(K, split), gran) * gran;
   p.kchunk = chunk;
   p.ksplit = (int)ceil_div(K, chunk);
+  p.bk = p.ksplit > 1 ? (int)gran : p.staged ? staged_stage_k(format, K) : unit_k(format);
   return p;
 }
 
@@ -432,19 +396,9 @@ size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K) {
 template <int FMT>
 static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles, (unsigned)p.ksplit);
-  if constexpr (FMT == SNIP_MXFP4) {
-    if (p.bk == 256) hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 256>), grid, dim3(NT), 0, s, g);
-    else hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 128>), grid, dim3(NT), 0, s, g);
-    return;
-  } else {
-    if constexpr (FMT == SNIP_NVFP4 || FMT == SNIP_BF16) {
-      if (p.bm == 256) {
-        hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 64>), grid, dim3(NT), 0, s, g);
-        return;
-      }
-    }
-    hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 64>), grid, dim3(NT), 0, s, g);
-  }
+  if (p.bm == 256) hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1>), grid, dim3(NT), 0, s, g);
+  else if (p.staged) launch_staged(FMT, p.bk, g, grid, s);
+  else hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 4, 1>), grid, dim3(NT), 0, s, g);
 }
 
 hipError_t launch_gemm(int format, const GemmArgs& g_in, hipStream_t s) {
@@ -453,6 +407,7 @@ hipError_t launch_gemm(int format, const GemmArgs& g_in, hipStream_t s) {
   if (p.ksplit > 1 && g.partial == nullptr) {      // no scratch: run unsplit
     p.ksplit = 1;
     p.kchunk = g.K;
+    if (p.staged) p.bk = staged_stage_k(format, g.K);
   }
   g.tiles_m = (int)ceil_div(g.M, p.bm);
   g.tiles_n = (int)ceil_div(g.N, p.bm);

@@ -1,0 +1,72 @@
+// Pieces shared by the two GEMM kernel families (gemm.hip: LDS-DMA staged
+// kernel; gemm_staged.hip: register-staged kernel): vector types, the tile
+// order and the epilogue.
+#pragma once
+
+#include "device.h"
+#include "kernels.h"
+
+namespace snip {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef int intx8_t __attribute__((ext_vector_type(8)));
+
+// Tile id -> (tile row, tile column). The hardware hands workgroups to the 8
+// XCDs round-robin; ids are remapped so each XCD works on a contiguous range,
+// and tiles are ordered in groups of 8 tile-rows so that concurrently
+// running tiles share A and B panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  constexpr int GM = 8;
+  const int group = id / (GM * tiles_n);
+  const int first = group * GM;
+  const int gm = (tiles_m - first) < GM ? (tiles_m - first) : GM;
+  const int r = id - group * GM * tiles_n;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+// Epilogue of a 2x2-wave tile: the wave's accumulators (lane holds rows
+// 4*grp + v, column r16 of each 16x16 block) go to C scaled by 2^(ea+eb),
+// or, under split-K, unscaled to this split's fp32 partial.
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const floatx4_t (&acc)[TM][TN], int64_t r0,
+                                           int64_t c0, int r16, int grp) {
+  if (g.kchunk >= g.K) {
+    const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = c0 + j * 16 + r16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t row = r0 + i * 16 + 4 * grp + v;
+          if (row < g.M && col < g.N) g.c[row * g.ldc + col] = ldexpf(acc[i][j][v], e);
+        }
+      }
+  } else {
+    float* part = g.partial + (int64_t)blockIdx.y * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t col = c0 + j * 16 + r16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t row = r0 + i * 16 + 4 * grp + v;
+          if (row < g.M && col < g.N) part[row * g.N + col] = acc[i][j][v];
+        }
+      }
+  }
+}
+
+// Register-staged 128x128 kernel (MX-FP4 and BF16): K per stage and launch.
+int staged_stage_k(int format, int64_t K);
+void launch_staged(int format, int bk, const GemmArgs& g, dim3 grid, hipStream_t s);
+
+}  // namespace snip

@@ -88,6 +88,7 @@ struct GemmPlan {
   int64_t tiles;
   int ksplit;
   int64_t kchunk;
+  int staged;              // 1: register-staged kernel (128x128 MX-FP4, BF16)
 };
 GemmPlan plan_gemm(int format, int64_t M, int64_t N, int64_t K);
 size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K);
