@@ -135,7 +135,17 @@ def main():
     gemm_by_fmt = {}
     quant = {"bytes": 0.0, "ms": 0.0, "launches": 0}
     other_ms = {}
+    by_class = {}
     for r in recs:
+        if r["kind"] in ("quantize", "amax"):
+            fname = S.FORMAT_NAMES.get(r["format"], "any")
+            key = r["kind"] if r["kind"] == "amax" else \
+                f"quantize {fname} {'row' if r['layout'] == 0 else 'col'} {'sr' if r['rounding'] == 1 else 'rne'}"
+            nb = r["work"] * (QBYTES[r["format"]] if r["kind"] == "quantize" else 2.0)
+            c = by_class.setdefault(key, {"ms": 0.0, "bytes": 0.0, "launches": 0})
+            c["ms"] += r["ms"]
+            c["bytes"] += nb
+            c["launches"] += 1
         if r["kind"] == "gemm":
             g = gemm_by_fmt.setdefault(r["format"], {"ms": 0.0, "flops": 0.0, "launches": 0})
             g["ms"] += r["ms"]
@@ -199,6 +209,10 @@ def main():
                      "ms_per_step": round(quant["ms"] / args.steps, 4),
                      "launches_per_step": quant["launches"] // args.steps},
         "other_kernels_ms_per_step": {k: round(v / args.steps, 4) for k, v in other_ms.items()},
+        "memory_kernels": {k: {"ms_per_step": round(c["ms"] / args.steps, 4),
+                               "launches_per_step": c["launches"] // args.steps,
+                               "gbs": round(c["bytes"] / (c["ms"] * 1e-3) / 1e9, 1)}
+                           for k, c in sorted(by_class.items())},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -207,11 +221,12 @@ def main():
 
 def cpu_baseline(wl, tokens=None):
     """The oracle as it stands on a bounded sample of the workload: forward +
-    backward of the Gate layer (the first layer if there is none), all six
-    quantize passes and the three GEMMs in the layer's format, on the first
-    `tokens` tokens (default: the whole layer when it holds at most 4096
-    tokens)."""
+    backward of the Gate and Up layers (the first layer if there are none),
+    all six quantize passes and the three GEMMs of each in the layer's
+    format, on the first `tokens` tokens (default: the whole layer when it
+    holds at most 4096 tokens)."""
     import synth
+    import sub_byte_mixed_amd as S
     from oracle import linear as OL
     try:
         from threadpoolctl import threadpool_info
@@ -219,22 +234,24 @@ def cpu_baseline(wl, tokens=None):
     except Exception:
         threads = os.cpu_count() or 1
     names = [l.name for l in wl.layers]
-    li = names.index("Gate") if "Gate" in names else 0
-    layer = wl.layers[li]
+    picks = [names.index(n) for n in ("Gate", "Up") if n in names] or [0]
     Ts = min(tokens or 4096, wl.tokens)
-    x, w, dy = synth.gen_x(wl, li, rows=Ts), synth.gen_w(wl, li), synth.gen_dy(wl, li, rows=Ts)
-    x32, w32, dy32 = (synth.bf16_to_f32(t) for t in (x, w, dy))
-    fmt = wl.plan[li]
-    t0 = time.perf_counter()
-    OL.linear_fwd(x32, w32, fmt, 0, li)
-    OL.linear_bwd(dy32, x32, w32, fmt, fmt, 0, li)
-    sec = time.perf_counter() - t0
-    flops = 3 * 2 * Ts * layer.d_in * layer.d_out
-    import sub_byte_mixed_amd as S
+    flops, sec = 0, 0.0
+    for li in picks:
+        layer = wl.layers[li]
+        x, w, dy = synth.gen_x(wl, li, rows=Ts), synth.gen_w(wl, li), synth.gen_dy(wl, li, rows=Ts)
+        x32, w32, dy32 = (synth.bf16_to_f32(t) for t in (x, w, dy))
+        fmt = wl.plan[li]
+        t0 = time.perf_counter()
+        OL.linear_fwd(x32, w32, fmt, 0, li)
+        OL.linear_bwd(dy32, x32, w32, fmt, fmt, 0, li)
+        sec += time.perf_counter() - t0
+        flops += 3 * 2 * Ts * layer.d_in * layer.d_out
+    desc = ", ".join(f"{wl.layers[li].name} {wl.layers[li].d_in}->{wl.layers[li].d_out} "
+                     f"({S.FORMAT_NAMES[wl.plan[li]]})" for li in picks)
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"layer {layer.name} {layer.d_in}->{layer.d_out}, T={Ts} of {wl.tokens} tokens, "
-                      f"fwd+bwd incl. all six quantize passes, {S.FORMAT_NAMES[fmt]}"}
+            "sample": f"layers {desc}, T={Ts} of {wl.tokens} tokens, fwd+bwd incl. all six quantize passes"}
 
 
 if __name__ == "__main__":

@@ -106,13 +106,23 @@ __global__ __launch_bounds__(256) void amax_kernel(AJobs jobs) {
   const int64_t nchunk = J.rows * cpr;
   const bool flat = J.ld == J.cols;
   uint32_t m = 0;
-  for (int64_t c = (int64_t)wg * 256 + threadIdx.x; c < nchunk; c += (int64_t)J.nwg * 256) {
-    const int64_t off = flat ? c * 8 : (c / cpr) * J.ld + (c % cpr) * 8;
-    const uint4 v = *reinterpret_cast<const uint4*>(J.x + off);
-    m = pair_max(v.x, m);
-    m = pair_max(v.y, m);
-    m = pair_max(v.z, m);
-    m = pair_max(v.w, m);
+  // kAmaxUnroll independent 16-byte loads per thread in flight
+  for (int64_t c0 = (int64_t)wg * 256 * kAmaxUnroll + threadIdx.x; c0 < nchunk;
+       c0 += (int64_t)J.nwg * 256 * kAmaxUnroll) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t c = c0 + u * 256;
+      const int64_t off = flat ? c * 8 : (c / cpr) * J.ld + (c % cpr) * 8;
+      v[u] = c < nchunk ? *reinterpret_cast<const uint4*>(J.x + off) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      m = pair_max(v[u].x, m);
+      m = pair_max(v[u].y, m);
+      m = pair_max(v[u].z, m);
+      m = pair_max(v[u].w, m);
+    }
   }
   m = wave_max_u(m);
   __shared__ uint32_t red[4];
