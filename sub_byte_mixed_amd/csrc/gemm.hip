@@ -47,8 +47,8 @@
 // longer read.
 //
 // Tiling: a workgroup of 256 threads (2x2 waves) owns a BM x BN output tile:
-// 256x256 (one workgroup per CU) or 128x128 (two per CU), as plan_gemm
-// decides from the problem's tile rounds. Tile order: the hardware hands workgroups to the 8 XCDs
+// 256x256 (one workgroup per CU), 256x128 (FP8, two per CU) or 128x128 (two
+// per CU), as plan_gemm decides from the problem's tile rounds. Tile order: the hardware hands workgroups to the 8 XCDs
 // round-robin; tile ids are remapped so each XCD works on a contiguous range,
 // and tiles are ordered in groups of 8 tile-rows so that concurrently running
 // tiles share A and B panels in that XCD's L2. Skinny problems split K across
@@ -119,7 +119,7 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
 }
 
 template <int FMT, int BM, int BN, int S, int UK>
-__global__ __launch_bounds__(NT, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NT, BM * BN > 256 * 128 ? 1 : 2) void gemm_kernel(GemmArgs g) {
   using U = Unit<FMT>;
   constexpr int UE = U::UE, NQ = U::NQ, SB = U::SB;
   constexpr int RBA = BM / 16, RBB = BN / 16;              // 16-row blocks per tile
@@ -336,16 +336,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nspl
 
 // Host-side plan: kernel, tile shape and K split for a problem.
 //
-// A CU holds one 256x256 workgroup or two 128x128 ones, so a launch runs in
-// rounds of 256 big or 512 small tiles. Per unit of tile area a round of
-// big tiles is faster by big_tile_gain (measured on MI355X: less decode and
-// operand traffic per MFMA for the LDS-DMA kernel; for MX-FP4 and BF16 the
-// small tiles run on the register-staged kernel, gemm_staged.hip, which
-// nearly matches it). A last, partial round of small tiles costs a full
-// round when more than 256 tiles remain (two per CU) and about 0.6 of one
-// otherwise (one per CU, running faster alone). The plan takes the cheaper
-// shape; problems with fewer than 192 small tiles split K so that about
-// 256 workgroups run.
+// A CU holds one 256x256 workgroup or two smaller ones (128x128, or 256x128
+// for FP8), so a launch runs in rounds of 256 big or 512 smaller tiles. Per
+// unit of tile area the bigger tiles run faster by measured factors (less
+// decode and operand traffic per MFMA; for MX-FP4 and BF16 the 128x128
+// tiles run on the register-staged kernel, gemm_staged.hip, which nearly
+// matches). A last, partial round of two-per-CU tiles costs a full round
+// when more than 256 tiles remain and about 0.6 of one otherwise (one per
+// CU, running faster alone). The plan takes the cheapest shape, in units of
+// one round of 128x128 tiles; problems with fewer than 192 small tiles split
+// K so that about 256 workgroups run.
 static double big_tile_gain(int format) {
   switch (format) {
     case SNIP_NVFP4: return 1.06;
@@ -354,24 +354,32 @@ static double big_tile_gain(int format) {
     default: return 1.02;
   }
 }
+constexpr double kRectGainFp8 = 1.17;     // 256x128 over 128x128, FP8
+
+static double rounds2(int64_t tiles) {    // two tiles per CU
+  const int64_t rem = tiles % 512;
+  return (double)(tiles / 512) + (rem == 0 ? 0.0 : rem <= 256 ? 0.6 : 1.0);
+}
 
 GemmPlan plan_gemm(int format, int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
   const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
   const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128);
-  const int64_t rem = t128 % 512;
-  const double time128 = (double)(t128 / 512) + (rem == 0 ? 0.0 : rem <= 256 ? 0.6 : 1.0);
+  const int64_t trect = ceil_div(M, 256) * ceil_div(N, 128);
+  const double time128 = rounds2(t128);
   const double time256 = (double)ceil_div(t256, 256) * 2.0 / big_tile_gain(format);
+  const double timerect = format == SNIP_FP8_E4M3 ? rounds2(trect) * 2.0 / kRectGainFp8 : 1e30;
   p.staged = 0;
-  if (t128 >= 192 && time256 < time128) {
+  p.ksplit = 1;
+  p.kchunk = K;
+  p.bk = unit_k(format);
+  if (t128 >= 192 && (time256 < time128 || timerect < time128)) {
     p.bm = 256;
-    p.bk = unit_k(format);
-    p.tiles = t256;
-    p.ksplit = 1;
-    p.kchunk = K;
+    p.bn = time256 <= timerect ? 256 : 128;
+    p.tiles = p.bn == 256 ? t256 : trect;
     return p;
   }
-  p.bm = 128;
+  p.bm = p.bn = 128;
   p.tiles = t128;
   p.staged = (format == SNIP_MXFP4 || format == SNIP_BF16) ? 1 : 0;
   int64_t split = p.tiles >= 192 ? 1 : 256 / p.tiles;
@@ -396,6 +404,12 @@ size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K) {
 template <int FMT>
 static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)p.tiles, (unsigned)p.ksplit);
+  if constexpr (FMT == SNIP_FP8_E4M3) {
+    if (p.bm == 256 && p.bn == 128) {     // 3-stage ring: 72 KiB, two per CU
+      hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 3, 1>), grid, dim3(NT), 0, s, g);
+      return;
+    }
+  }
   if (p.bm == 256) hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1>), grid, dim3(NT), 0, s, g);
   else if (p.staged) launch_staged(FMT, p.bk, g, grid, s);
   else hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 4, 1>), grid, dim3(NT), 0, s, g);
@@ -410,7 +424,7 @@ hipError_t launch_gemm(int format, const GemmArgs& g_in, hipStream_t s) {
     if (p.staged) p.bk = staged_stage_k(format, g.K);
   }
   g.tiles_m = (int)ceil_div(g.M, p.bm);
-  g.tiles_n = (int)ceil_div(g.N, p.bm);
+  g.tiles_n = (int)ceil_div(g.N, p.bn);
   g.kchunk = p.kchunk;
   if (format < SNIP_BF16 || format > SNIP_MXFP4) return hipErrorInvalidValue;
   int slot = timing_begin(LaunchTag{SNIP_LAUNCH_GEMM, format, -1, -1, 2.0 * g.M * g.N * g.K}, s);

@@ -84,7 +84,7 @@ struct GemmArgs {
 
 // Tile shape and K split chosen on the host for one GEMM.
 struct GemmPlan {
-  int bm;                  // square tile edge: 256 or 128
+  int bm, bn;              // tile: 256x256, 256x128 (FP8) or 128x128
   int bk;                  // K per LDS stage
   int64_t tiles;
   int ksplit;

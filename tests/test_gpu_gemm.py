@@ -67,3 +67,36 @@ def test_gemm_ldc_and_overwrite():
     h = big.cpu().numpy()
     assert np.all(h[:, 40:] == 7.0)                          # untouched beyond N
     check_gemm(h[:, :40].astype(np.float64), oa["xhat"], ob["xhat"], what="ldc")
+
+
+# Shapes that make the planner pick each kernel and tile: FP8 256x128,
+# 256x256 for NVFP4, MX-FP4 and BF16, the register-staged 128x128 kernel for
+# MX-FP4 and BF16, and the LDS-DMA 128x128 kernel for NVFP4 / FP8 -- all
+# with ragged M and N. Sampled output rows (all columns) against the oracle.
+PLAN_CASES = [
+    (S.FP8, 4000, 5600, 1024),      # 256x128
+    (S.NVFP4, 8000, 4000, 512),     # 256x256
+    (S.FP8, 8000, 4000, 512),       # 256x128
+    (S.MXFP4, 8000, 4000, 512),     # 256x256
+    (S.BF16, 8000, 4000, 256),      # 256x256
+    (S.MXFP4, 2000, 1600, 768),     # staged 128x128, 256-element stages
+    (S.MXFP4, 2000, 1600, 384),     # staged 128x128, 128-element stages
+    (S.BF16, 2000, 1600, 384),      # staged 128x128
+    (S.NVFP4, 2000, 1600, 640),     # LDS-DMA 128x128
+    (S.FP8, 2000, 1600, 640),       # LDS-DMA 128x128
+]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", PLAN_CASES)
+def test_gemm_each_plan_ragged(fmt, M, N, K):
+    say(f"gemm plan case fmt={fmt} M={M} N={N} K={K}")
+    a = synth.gen_matrix((M, K), seed=M + K)
+    b = synth.gen_matrix((N, K), seed=N + K, std=0.02)
+    oa = oracle_quant(a, S.ROWWISE, fmt, S.RNE, 0, 0)
+    ob = oracle_quant(b, S.ROWWISE, fmt, S.SR, 1, 1)
+    c = S.qgemm(upload_oracle_q(oa, fmt), upload_oracle_q(ob, fmt))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(K)
+    rows = np.unique(np.concatenate([rng.choice(M, 96, replace=False), [0, 255, 256, M - 1]]))
+    check_gemm(c[rows].cpu().numpy().astype(np.float64), oa["xhat"][rows], ob["xhat"],
+               what=f"fmt={fmt} {M}x{N}x{K}")
