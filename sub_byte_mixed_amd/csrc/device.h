@@ -36,8 +36,9 @@ __device__ __forceinline__ Words4 philox10(uint32_t c0, uint32_t c1, uint32_t c2
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-way xors as one v_bitop3_b32 each (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -126,8 +127,10 @@ __device__ __forceinline__ float e4m3_val(uint32_t c) {
 // exactly that of e2m1_sr / e4m3_sr above. The stochastic FP4 convert shares
 // its random word between its two lanes and does not keep the other bytes of
 // its destination, so it is issued once per element (lane 0, byte 0) and the
-// nibble is placed by hand. Every helper below is checked against the
-// software encoders over all fp32 inputs (tests/helpers/hw_convert_check.hip).
+// nibble is masked and placed by hand (measured: the bits above the nibble
+// are not zero). The stochastic FP8 convert with a zero `old` operand leaves
+// only the code byte set. Every helper below is checked against the software
+// encoders over all fp32 inputs (tests/helpers/hw_convert_check.hip).
 typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef short s2_t __attribute__((ext_vector_type(2)));
 
@@ -184,7 +187,7 @@ __device__ __forceinline__ uint32_t fp8x4_sr(const float* c, const Words4& d, in
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const uint32_t v = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0u, c[b], sr_seed(d, first + b), 1.0f, 0);
-    w |= (v & 0xFFu) << (8 * b);
+    w |= v << (8 * b);             // v holds the code in its low byte only
   }
   return w;
 }

@@ -139,12 +139,19 @@ __global__ __launch_bounds__(256) void amax_kernel(AJobs jobs) {
 // Element encoding and the decode for the statistics use the gfx950
 // conversion instructions through the packed helpers of device.h.
 
+__device__ __forceinline__ void fill_inv_lut(float* lut) {
+  if (threadIdx.x < 128) lut[threadIdx.x] = threadIdx.x ? 1.0f / e4m3_val(threadIdx.x) : 0.0f;
+  __syncthreads();
+}
+
 // NVFP4: 16 raw values x -> 16 packed nibbles (lo: elements 0..7, hi: 8..15),
 // the E4M3 block scale and the block's stats in the tensor-scaled domain.
+// inv_lut[c] = fp32(1 / e4m3(c)) (IEEE division, filled once per workgroup
+// by fill_inv_lut), 0 for c = 0.
 template <bool SR>
 __device__ __forceinline__ void nvfp4_block(const float (&x)[16], int eS, const Words4& d0,
-                                            const Words4& d1, uint32_t& lo, uint32_t& hi,
-                                            uint32_t& sc, float& be2, float& bx2) {
+                                            const Words4& d1, const float* inv_lut, uint32_t& lo,
+                                            uint32_t& hi, uint32_t& sc, float& be2, float& bx2) {
   float xs[16];
   float am = 0.0f;
 #pragma unroll
@@ -154,7 +161,7 @@ __device__ __forceinline__ void nvfp4_block(const float (&x)[16], int eS, const 
   }
   sc = e4m3_rne(am / 6.0f);
   const float shat = e4m3_val(sc);
-  const float inv = sc ? 1.0f / shat : 0.0f;      // a zero block keeps signed-zero codes
+  const float inv = inv_lut[sc];                  // 0 for a zero block: signed-zero codes
   float r[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) r[i] = xs[i] * inv;
@@ -288,7 +295,7 @@ struct RowAcc {
 };
 
 template <int FMT, bool SR>
-__device__ __forceinline__ void row_item(const QJob& J, int eS, int64_t it,
+__device__ __forceinline__ void row_item(const QJob& J, int eS, const float* inv_lut, int64_t it,
                                          const uint4 (&v)[FMT == SNIP_MXFP4 ? 4 : 2],
                                          RowAcc<FMT, SR>& acc) {
   constexpr int EPT = (FMT == SNIP_MXFP4) ? 32 : 16;
@@ -335,7 +342,7 @@ __device__ __forceinline__ void row_item(const QJob& J, int eS, int64_t it,
     float be2, bx2;
     if constexpr (FMT == SNIP_NVFP4) {
       uint32_t lo, hi, sc;
-      nvfp4_block<SR>(x, eS, d0, d1, lo, hi, sc, be2, bx2);
+      nvfp4_block<SR>(x, eS, d0, d1, inv_lut, lo, hi, sc, be2, bx2);
       *reinterpret_cast<uint2*>(J.codes + it * 8) = make_uint2(lo, hi);
       J.scales[it] = (uint8_t)sc;
     } else {
@@ -387,6 +394,8 @@ __global__ __launch_bounds__(256) void quant_row_kernel(QJobs jobs) {
   const float A = (FMT == SNIP_MXFP4) ? 0.0f : wg_tensor_amax(J, ured);
   const int eS = tensor_exp(A, FMT);
   if (wg == 0 && threadIdx.x == 0 && J.texp) *J.texp = eS;
+  __shared__ float inv_lut[FMT == SNIP_NVFP4 ? 128 : 1];
+  if constexpr (FMT == SNIP_NVFP4) fill_inv_lut(inv_lut);
 
   RowAcc<FMT, SR> acc;
   for (; it < nitems; it += stride) {
@@ -397,8 +406,8 @@ __global__ __launch_bounds__(256) void quant_row_kernel(QJobs jobs) {
       for (int q = 0; q < NV; ++q) cur[u][q] = v[u][q];
     load(it + stride, v[0]);                                // prefetch the next iteration
     load(it + stride + 256, v[1]);
-    row_item<FMT, SR>(J, eS, it, cur[0], acc);
-    if (it + 256 < nitems) row_item<FMT, SR>(J, eS, it + 256, cur[1], acc);
+    row_item<FMT, SR>(J, eS, inv_lut, it, cur[0], acc);
+    if (it + 256 < nitems) row_item<FMT, SR>(J, eS, inv_lut, it + 256, cur[1], acc);
   }
   if (FMT != SNIP_MXFP4) acc.amax_bits = __float_as_uint(A);
   const double e2 = ldexp(acc.e2s, 2 * eS) + acc.e2r;
@@ -433,6 +442,8 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
   const float A = (FMT == SNIP_MXFP4) ? 0.0f : wg_tensor_amax(J, ured);
   const int eS = tensor_exp(A, FMT);
   if (wg == 0 && threadIdx.x == 0 && J.texp) *J.texp = eS;
+  __shared__ float inv_lut[FMT == SNIP_NVFP4 ? 128 : 1];
+  if constexpr (FMT == SNIP_NVFP4) fill_inv_lut(inv_lut);
 
   const int64_t R = J.rows, C = J.cols;
   const int64_t rowbytes = R / BLK * CB;                        // output row length (codes)
@@ -503,7 +514,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
             float be2, bx2;
             if constexpr (FMT == SNIP_NVFP4) {
               uint32_t lo, hi, sc;
-              nvfp4_block<SR>(x, eS, d0, d1, lo, hi, sc, be2, bx2);
+              nvfp4_block<SR>(x, eS, d0, d1, inv_lut, lo, hi, sc, be2, bx2);
               *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
               lsc[cl * NB + rb] = (uint8_t)sc;
             } else {

@@ -27,7 +27,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-GEMM_SOURCES = ("csrc/gemm.hip", "csrc/device.h", "csrc/kernels.h")
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/gemm_common.h", "csrc/device.h", "csrc/kernels.h")
 TRAFFIC_TAG = "traffic-json:"
 
 
