@@ -4,13 +4,19 @@ Gate, Up, Down) of a Llama-like block through the quantized linear layer
 stochastic rounding, dgrad and wgrad GEMMs; per-tensor statistics), on
 synthetic bf16 inputs already resident in HBM.
 
+By default each layer runs the saved-operand path (snip_linear_fwd_save /
+snip_linear_bwd_saved): X, W and dY are each read once by a dual quantizer
+that writes both of their layouts; the results are bit-identical to the
+separate calls (--path unfused), which read X and W again in the backward
+pass and dY twice.
+
 Prints one JSON line: whole-step GEMM throughput (TFLOP/s over the step's
 wall time, quantizers and statistics included), the dominant kernel against
 its MFMA roofline, the quantizers' credited HBM bandwidth, and the CPU
 oracle timed on a bounded sample on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--graph]
+                       [--path fused|unfused] [--no-cpu-baseline] [--graph]
 """
 from __future__ import annotations
 
@@ -32,6 +38,8 @@ PEAK = {  # MI355X published dense peaks
 METRIC = "qGEMM TFLOP/s (FP4/FP8) + quantize GB/s per Llama layer fwd+bwd, % of roofline"
 # credited quantizer bytes per element (bf16 read + codes + scales written)
 QBYTES = {1: 2 + 1.0, 2: 2 + 0.5 + 1 / 16, 3: 2 + 0.5 + 1 / 32, 0: 2 + 2.0}
+# a dual pass reads once and writes both layouts
+QBYTES_DUAL = {f: 2 + 2 * (b - 2) for f, b in QBYTES.items()}
 
 
 def parse():
@@ -43,6 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    ap.add_argument("--path", choices=("fused", "unfused"), default="fused",
+                    help="fused: one read of X, W and dY per step (saved-operand calls)")
     return ap.parse_args()
 
 
@@ -67,6 +77,7 @@ def main():
     L = S.lib()
 
     # ---------------------------------------------------------------- inputs
+    fused = args.path == "fused" and all(f != S.BF16 for f in wl.plan)
     layers = []
     for li, layer in enumerate(wl.layers):
         x, w, dy = synth.gen_layer(wl, li)
@@ -83,15 +94,30 @@ def main():
                                 dtype=torch.uint8, device=dev)
         d["ws_b"] = torch.empty(L.snip_linear_bwd_workspace(T, layer.d_in, layer.d_out, fmt, fmt),
                                 dtype=torch.uint8, device=dev)
+        if fused:
+            d["saved"] = S.SavedOperands(fmt, T, layer.d_in, layer.d_out, dev)
+            d["st_f4"], d["st_b2"] = S.new_stats(4, dev), S.new_stats(2, dev)
+            d["ws_fs"] = torch.empty(L.snip_linear_fwd_save_workspace(T, layer.d_in, layer.d_out, fmt),
+                                     dtype=torch.uint8, device=dev)
+            d["ws_bs"] = torch.empty(L.snip_linear_bwd_saved_workspace(T, layer.d_in, layer.d_out, fmt),
+                                     dtype=torch.uint8, device=dev)
         layers.append(d)
     torch.cuda.synchronize()
 
-    def step():
+    def step_fused():
+        for li, d in enumerate(layers):
+            S.linear_fwd_save(d["x"], d["w"], d["fmt"], seed, li, y=d["y"], saved=d["saved"], stats=d["st_f4"],
+                              ws=d["ws_fs"])
+            S.linear_bwd_saved(d["dy"], d["saved"], seed, li, dx=d["dx"], dw=d["dw"], stats=d["st_b2"],
+                               ws=d["ws_bs"])
+
+    def step_unfused():
         for li, d in enumerate(layers):
             S.linear_fwd(d["x"], d["w"], d["fmt"], seed, li, y=d["y"], stats=d["st_f"], ws=d["ws_f"])
             S.linear_bwd(d["dy"], d["x"], d["w"], d["fmt"], d["fmt"], seed, li, dx=d["dx"], dw=d["dw"],
                          stats=d["st_b"], ws=d["ws_b"], fwd_stats=d["st_f"])
 
+    step = step_fused if fused else step_unfused
     gemm_flops = sum(3 * 2 * T * d["din"] * d["dout"] for d in layers)
 
     graph = None
@@ -139,9 +165,15 @@ def main():
     for r in recs:
         if r["kind"] in ("quantize", "amax"):
             fname = S.FORMAT_NAMES.get(r["format"], "any")
-            key = r["kind"] if r["kind"] == "amax" else \
-                f"quantize {fname} {'row' if r['layout'] == 0 else 'col'} {'sr' if r['rounding'] == 1 else 'rne'}"
-            nb = r["work"] * (QBYTES[r["format"]] if r["kind"] == "quantize" else 2.0)
+            rn = {0: "rne", 1: "sr"}
+            if r["kind"] == "amax":
+                key, nb = "amax", 2.0 * r["work"]
+            elif r["layout"] == S.BOTHWISE:     # rounding = row + 2 * column
+                key = f"quantize {fname} dual row-{rn[r['rounding'] & 1]} col-{rn[r['rounding'] >> 1]}"
+                nb = r["work"] * QBYTES_DUAL[r["format"]]
+            else:
+                key = f"quantize {fname} {'row' if r['layout'] == 0 else 'col'} {rn[r['rounding']]}"
+                nb = r["work"] * QBYTES[r["format"]]
             c = by_class.setdefault(key, {"ms": 0.0, "bytes": 0.0, "launches": 0})
             c["ms"] += r["ms"]
             c["bytes"] += nb
@@ -153,7 +185,7 @@ def main():
             g["launches"] += 1
         elif r["kind"] == "quantize":
             quant["ms"] += r["ms"]
-            quant["bytes"] += r["work"] * QBYTES[r["format"]]
+            quant["bytes"] += r["work"] * (QBYTES_DUAL if r["layout"] == S.BOTHWISE else QBYTES)[r["format"]]
             quant["launches"] += 1
         else:
             other_ms[r["kind"]] = other_ms.get(r["kind"], 0.0) + r["ms"]
@@ -203,7 +235,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T,
                    "layers": [f"{d['name']} {d['din']}->{d['dout']}" for d in layers],
-                   "plan": [S.FORMAT_NAMES[d["fmt"]] for d in layers], "graph": bool(graph)},
+                   "plan": [S.FORMAT_NAMES[d["fmt"]] for d in layers], "graph": bool(graph),
+                   "quantizers": "fused: one read of X, W, dY per step" if fused else "separate passes"},
         "gemm": gemm_detail,
         "quantize": {"gbs": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / PEAK["hbm_gbs"], 4),
                      "ms_per_step": round(quant["ms"] / args.steps, 4),

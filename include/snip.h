@@ -90,6 +90,7 @@ extern "C" {
 
 #define SNIP_ROWWISE   0  /* blocks along each row: [R, C] -> [R, C]        */
 #define SNIP_COLWISE   1  /* blocks along each column: [R, C] -> [C, R]     */
+#define SNIP_BOTHWISE  2  /* launch records only: one pass writing both      */
 
 /* ---- descriptors ------------------------------------------------------ */
 
@@ -171,11 +172,11 @@ int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
  * A = dequant(a) [M][K] and B = dequant(b) [N][K]; M = a->rows, N = b->rows,
  * K = a->k = b->k. [SNIP, Fig. 5]: the GEMMs of a linear layer.
  *   a, b       host descriptors; same format; K % 128 == 0; M, N > 0.
- *              NVFP4 runs on fp16 MFMA after exact decoding of
- *              code x block scale; FP8 and MXFP4 on the gfx950 8-bit / 4-bit
- *              MFMA (MXFP4 with its E8M0 block scales in the instruction);
- *              BF16 on bf16 MFMA. Accumulation is fp32; the tensor scales
- *              2^(ea + eb) are applied in the epilogue.
+ *              NVFP4 (code x block scale) and FP8 codes are decoded exactly
+ *              to fp16 and run on the fp16 MFMA; MXFP4 runs on the gfx950
+ *              scaled 4-bit MFMA with its E8M0 block scales in the
+ *              instruction; BF16 on the bf16 MFMA. Accumulation is fp32;
+ *              the tensor scales 2^(ea + eb) are applied in the epilogue.
  *   c          device fp32, ldc >= N.
  *   ws         may be NULL when ws_bytes == 0 (no workspace needed).
  * Errors: NULL, SHAPE, ALIGN, FORMAT, HIP. */
@@ -222,6 +223,72 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w,
                     const snip_stats* fwd_stats2, float* dx, float* dw, snip_stats* stats4,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* ---- fused quantizers: one read of a tensor, both layouts -------------- */
+
+/* Quantize one bf16 tensor x[rows][cols] row-wise and column-wise from a
+ * single read of x: out_row receives exactly what snip_quantize(...,
+ * SNIP_ROWWISE, format, rounding_row, seed, tensor_id_row, ...) writes and
+ * out_col exactly what snip_quantize(..., SNIP_COLWISE, format,
+ * rounding_col, seed, tensor_id_col, ...) writes (same codes, scales and
+ * tensor exponent). [FP4 All the Way, Outline]: a tensor is quantized with
+ * nearest rounding for the forward GEMM and stochastic rounding for the
+ * backward ones; [SNIP, Fig. 5]: X, W and dY each feed two GEMMs, along
+ * different dimensions.
+ *   x          device bf16, 16-byte aligned, ld >= cols, ld % 8 == 0.
+ *   format     SNIP_NVFP4, SNIP_FP8_E4M3 or SNIP_MXFP4 (BF16: FORMAT error).
+ *   rows, cols > 0, both multiples of 16 (MXFP4: of 32).
+ *   amax_in    as for snip_quantize.
+ *   out_row    host descriptor, [rows][cols]; out_col [cols][rows].
+ *   stats2     device snip_stats[2] = {row-wise, column-wise} or NULL.
+ *   ws         device, snip_quantize_dual_workspace() bytes.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
+int snip_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld, int format,
+                       int rounding_row, int rounding_col, uint64_t seed,
+                       uint32_t tensor_id_row, uint32_t tensor_id_col, const float* amax_in,
+                       const snip_qtensor* out_row, const snip_qtensor* out_col,
+                       snip_stats* stats2, void* ws, size_t ws_bytes, void* stream);
+
+/* Forward that also emits the backward operands built from x and w, so
+ * that each of them is read once per training step:
+ *   y[T][out] = Q_rne(x) . Q_rne(w)^T        (as snip_linear_fwd), and
+ *   wt = Q_sr(w) column-wise, [in][out]      (tensor id 8*layer_id + 3),
+ *   xt = Q_sr(x) column-wise, [in][T]        (tensor id 8*layer_id + 5):
+ * byte for byte the operands snip_linear_bwd builds for the B sides of its
+ * dgrad and wgrad GEMMs when fmt_dgrad = fmt_wgrad = format.
+ * [SNIP, Fig. 5]; [FP4 All the Way, Outline].
+ *   x          device bf16 [T][in]; w device bf16 [out][in] (contiguous).
+ *   format     NVFP4, FP8_E4M3 or MXFP4, for all three GEMMs of the layer.
+ *   T, in, out multiples of 128.
+ *   wt, xt     host descriptors of caller-owned device buffers in `format`
+ *              (rows in, k = out; rows in, k = T); the caller keeps them
+ *              until snip_linear_bwd_saved.
+ *   stats4     device snip_stats[4] = {X, W, W^T, X^T} or NULL.
+ *   ws         device, snip_linear_fwd_save_workspace() bytes.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
+int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, int64_t out,
+                         int format, uint64_t seed, uint32_t layer_id, float* y,
+                         const snip_qtensor* wt, const snip_qtensor* xt, snip_stats* stats4,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Backward from the saved operands: dy is read once and quantized both ways
+ * (row-wise SR, tensor id 8*layer_id + 2; column-wise SR, id
+ * 8*layer_id + 4), then
+ *   dx[T][in]   = Q_sr(dy) . (wt)^T      (K = out)
+ *   dw[out][in] = Q_sr(dy^T) . (xt)^T    (K = T)
+ * identical to snip_linear_bwd with fmt_dgrad = fmt_wgrad = wt->format.
+ * [SNIP, Fig. 5]; [FP4 All the Way, Outline].
+ *   dy         device bf16 [T][out].
+ *   wt, xt     as written by snip_linear_fwd_save (same format; wt [in][out],
+ *              xt [in][T]); T, in, out multiples of 128.
+ *   dx, dw     device fp32 or NULL (NULL skips that GEMM).
+ *   stats2     device snip_stats[2] = {dY, dY^T} or NULL.
+ *   ws         device, snip_linear_bwd_saved_workspace() bytes.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
+int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qtensor* xt,
+                          int64_t T, int64_t in, int64_t out, uint64_t seed, uint32_t layer_id,
+                          float* dx, float* dw, snip_stats* stats2,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Synchronise `stream`, copy n device statistics records to the host and
  * derive the report of each. [SNIP, Abstract] (statistics for the precision
  * decision); [FP4 All the Way, Outline] (sqrt(3) threshold).
@@ -239,6 +306,9 @@ size_t snip_qgemm_workspace(int64_t M, int64_t N, int64_t K, int format);
 size_t snip_linear_fwd_workspace(int64_t T, int64_t in, int64_t out, int format);
 size_t snip_linear_bwd_workspace(int64_t T, int64_t in, int64_t out,
                                  int fmt_dgrad, int fmt_wgrad);
+size_t snip_quantize_dual_workspace(int64_t rows, int64_t cols, int format);
+size_t snip_linear_fwd_save_workspace(int64_t T, int64_t in, int64_t out, int format);
+size_t snip_linear_bwd_saved_workspace(int64_t T, int64_t in, int64_t out, int format);
 
 /* Bytes of one part of a quantized operand: part 0 = codes, 1 = scales.
  * Returns -1 on invalid arguments. */
@@ -261,7 +331,8 @@ int64_t snip_qtensor_bytes(int format, int64_t rows, int64_t k, int part);
 typedef struct snip_launch_record {
   int32_t kind;       /* SNIP_LAUNCH_*                                      */
   int32_t format;     /* SNIP_BF16.. for quantize / GEMM / split-K, else -1 */
-  int32_t layout;     /* quantize: SNIP_ROWWISE / SNIP_COLWISE, else -1     */
+  int32_t layout;     /* quantize: SNIP_ROWWISE / SNIP_COLWISE, or
+                         SNIP_BOTHWISE for a dual pass; else -1            */
   int32_t rounding;   /* quantize: SNIP_RNE / SNIP_SR, else -1              */
   double work;
   double ms;

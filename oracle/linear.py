@@ -55,6 +55,36 @@ def linear_bwd(dy, x, w, fmt_dgrad: int, fmt_wgrad: int, seed: int = 0, layer_id
             "stats": [qdy["stats"], qwt["stats"], qdyt["stats"], qxt["stats"]]}
 
 
+def quantize_dual(x, fmt: int, rounding_row: str, rounding_col: str, seed: int, tid_row: int,
+                  tid_col: int, amax=None):
+    """Both layouts of one tensor [SNIP, Fig. 5: X, W and dY each feed two
+    GEMMs, along different dimensions]: by definition the row-wise and the
+    column-wise quantization of x, each with its own rounding and stream."""
+    return (quantize(x, fmt, rounding_row, seed, tid_row, amax=amax),
+            quantize_colwise(x, fmt, rounding_col, seed, tid_col, amax=amax))
+
+
+def linear_fwd_save(x, w, fmt: int, seed: int = 0, layer_id: int = 0):
+    """Forward plus the backward operands built from x and w, in the
+    layer's one format: what linear_fwd computes, and the column-wise SR
+    operands W^T (dgrad B) and X^T (wgrad B) that linear_bwd builds."""
+    f = linear_fwd(x, w, fmt, seed, layer_id)
+    qwt = quantize_colwise(w, fmt, "sr", seed, tid(layer_id, ROLE_WT_DGRAD))
+    qxt = quantize_colwise(x, fmt, "sr", seed, tid(layer_id, ROLE_XT_WGRAD))
+    f.update(qwt=qwt, qxt=qxt, stats=[f["qx"]["stats"], f["qw"]["stats"], qwt["stats"], qxt["stats"]])
+    return f
+
+
+def linear_bwd_saved(dy, qwt: dict, qxt: dict, fmt: int, seed: int = 0, layer_id: int = 0):
+    """Backward from saved W^T and X^T operands: dY quantized both ways."""
+    qdy = quantize(dy, fmt, "sr", seed, tid(layer_id, ROLE_DY_DGRAD))
+    qdyt = quantize_colwise(dy, fmt, "sr", seed, tid(layer_id, ROLE_DYT_WGRAD))
+    dx, bdx = gemm_q(qdy, qwt)
+    dw, bdw = gemm_q(qdyt, qxt)
+    return {"dx": dx, "bound_dx": bdx, "dw": dw, "bound_dw": bdw, "q": [qdy, qdyt],
+            "stats": [qdy["stats"], qdyt["stats"]]}
+
+
 def report(stats: dict) -> dict:
     """Derived per-tensor report from one statistics record."""
     e2, x2 = stats["sum_err2"], stats["sum_x2"]

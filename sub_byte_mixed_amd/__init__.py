@@ -10,6 +10,9 @@ the C entry points (include/snip.h):
   qgemm(a, b)                              -> fp32 [M, N]
   linear_fwd(x, w, fmt, ...)               -> y, stats[2]
   linear_bwd(dy, x, w, fmt_d, fmt_w, ...)  -> dx, dw, stats[4]
+  quantize_dual(x, fmt, rnd_row, rnd_col, ...)  -> row-wise, column-wise, stats[2]
+  linear_fwd_save(x, w, fmt, ...)          -> y, saved (W^T, X^T), stats[4]
+  linear_bwd_saved(dy, saved, ...)         -> dx, dw, stats[2]
   layer_stats(stats)                       -> list of per-tensor reports
   timing_start(capacity), timing_read()    -> per-launch kernel times
 
@@ -31,7 +34,7 @@ LIB_PATH = os.path.join(HERE, "libsnip.so")
 BF16, FP8_E4M3, NVFP4, MXFP4 = 0, 1, 2, 3
 FP8 = FP8_E4M3
 RNE, SR = 0, 1
-ROWWISE, COLWISE = 0, 1
+ROWWISE, COLWISE, BOTHWISE = 0, 1, 2
 FORMAT_NAMES = {BF16: "bf16", FP8_E4M3: "fp8_e4m3", NVFP4: "nvfp4", MXFP4: "mxfp4"}
 ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "FORMAT", -5: "WORKSPACE",
           -6: "HIP", -7: "NONFINITE"}
@@ -84,12 +87,27 @@ _SIGS = {
                                    _c.c_int64, _c.c_int, _c.c_int, _c.c_uint64, _c.c_uint32,
                                    _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                    _c.c_size_t, _c.c_void_p]),
+    "snip_quantize_dual": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
+                                      _c.c_int, _c.c_uint64, _c.c_uint32, _c.c_uint32, _c.c_void_p,
+                                      _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc), _c.c_void_p,
+                                      _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "snip_linear_fwd_save": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
+                                        _c.c_int, _c.c_uint64, _c.c_uint32, _c.c_void_p,
+                                        _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc), _c.c_void_p,
+                                        _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "snip_linear_bwd_saved": (_c.c_int, [_c.c_void_p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
+                                         _c.c_int64, _c.c_int64, _c.c_int64, _c.c_uint64, _c.c_uint32,
+                                         _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
+                                         _c.c_void_p]),
     "snip_layer_stats": (_c.c_int, [_c.c_void_p, _c.c_int, _c.POINTER(TensorReport), _c.c_void_p]),
     "snip_quantize_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "snip_qgemm_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "snip_linear_fwd_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "snip_linear_bwd_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                                 _c.c_int]),
+    "snip_quantize_dual_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int]),
+    "snip_linear_fwd_save_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
+    "snip_linear_bwd_saved_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "snip_qtensor_bytes": (_c.c_int64, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int]),
     "snip_timing_start": (_c.c_int, [_c.c_int]),
     "snip_timing_read": (_c.c_int, [_c.POINTER(LaunchRecord), _c.c_int, _c.POINTER(_c.c_int64)]),
@@ -262,6 +280,93 @@ def linear_bwd(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, fmt_dgrad: in
     return dx, dw, stats
 
 
+def quantize_dual(x: torch.Tensor, fmt: int, rounding_row: int = RNE, rounding_col: int = SR,
+                  seed: int = 0, tensor_id_row: int = 0, tensor_id_col: int = 1,
+                  amax: Optional[torch.Tensor] = None, out_row: Optional[QuantizedTensor] = None,
+                  out_col: Optional[QuantizedTensor] = None, stats: Optional[torch.Tensor] = None,
+                  with_stats: bool = True, stream=None):
+    """snip_quantize_dual: one read of x bf16 [rows, cols] -> (row-wise
+    [rows][cols], column-wise [cols][rows], stats[2])."""
+    _require_cuda_bf16(x, "x")
+    L = lib()
+    rows, cols = x.shape
+    if out_row is None:
+        out_row = QuantizedTensor(fmt, rows, cols, x.device)
+    if out_col is None:
+        out_col = QuantizedTensor(fmt, cols, rows, x.device)
+    if stats is None and with_stats:
+        stats = new_stats(2, x.device)
+    ws = _workspace(L.snip_quantize_dual_workspace(rows, cols, fmt), x.device)
+    dr, dc = out_row.desc(), out_col.desc()
+    _check(L.snip_quantize_dual(_ptr(x), rows, cols, x.stride(0), fmt, rounding_row, rounding_col, seed,
+                                tensor_id_row, tensor_id_col, _ptr(amax), ctypes.byref(dr), ctypes.byref(dc),
+                                _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_row, out_col, stats
+
+
+class SavedOperands:
+    """The backward operands linear_fwd_save writes: W^T [in][out] and
+    X^T [in][T], column-wise quantized with stochastic rounding."""
+
+    def __init__(self, fmt: int, T: int, din: int, dout: int, device):
+        self.format, self.T, self.din, self.dout = fmt, T, din, dout
+        self.wt = QuantizedTensor(fmt, din, dout, device)
+        self.xt = QuantizedTensor(fmt, din, T, device)
+
+
+def linear_fwd_save(x: torch.Tensor, w: torch.Tensor, fmt: int, seed: int = 0, layer_id: int = 0,
+                    y: Optional[torch.Tensor] = None, saved: Optional[SavedOperands] = None,
+                    stats: Optional[torch.Tensor] = None, with_stats: bool = True,
+                    ws: Optional[torch.Tensor] = None, stream=None):
+    """snip_linear_fwd_save: y = Q_rne(x) . Q_rne(w)^T, plus the backward
+    operands W^T and X^T from the same reads. Returns (y, saved, stats[4] =
+    {X, W, W^T, X^T})."""
+    _require_cuda_bf16(x, "x")
+    _require_cuda_bf16(w, "w")
+    L = lib()
+    T, din = x.shape
+    dout = w.shape[0]
+    if y is None:
+        y = torch.empty((T, dout), dtype=torch.float32, device=x.device)
+    if saved is None:
+        saved = SavedOperands(fmt, T, din, dout, x.device)
+    if stats is None and with_stats:
+        stats = new_stats(4, x.device)
+    if ws is None:
+        ws = _workspace(L.snip_linear_fwd_save_workspace(T, din, dout, fmt), x.device)
+    dwt, dxt = saved.wt.desc(), saved.xt.desc()
+    _check(L.snip_linear_fwd_save(_ptr(x), _ptr(w), T, din, dout, fmt, seed, layer_id, _ptr(y),
+                                  ctypes.byref(dwt), ctypes.byref(dxt), _ptr(stats), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
+    return y, saved, stats
+
+
+def linear_bwd_saved(dy: torch.Tensor, saved: SavedOperands, seed: int = 0, layer_id: int = 0,
+                     need_dx: bool = True, need_dw: bool = True, dx: Optional[torch.Tensor] = None,
+                     dw: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
+                     with_stats: bool = True, ws: Optional[torch.Tensor] = None, stream=None):
+    """snip_linear_bwd_saved: dY read once (row-wise and column-wise SR),
+    dx = Q(dy) . W^T-operand, dw = Q(dy^T) . X^T-operand. Returns (dx, dw,
+    stats[2] = {dY, dY^T})."""
+    _require_cuda_bf16(dy, "dy")
+    L = lib()
+    T, dout = dy.shape
+    din = saved.din
+    if need_dx and dx is None:
+        dx = torch.empty((T, din), dtype=torch.float32, device=dy.device)
+    if need_dw and dw is None:
+        dw = torch.empty((dout, din), dtype=torch.float32, device=dy.device)
+    if stats is None and with_stats:
+        stats = new_stats(2, dy.device)
+    if ws is None:
+        ws = _workspace(L.snip_linear_bwd_saved_workspace(T, din, dout, saved.format), dy.device)
+    dwt, dxt = saved.wt.desc(), saved.xt.desc()
+    _check(L.snip_linear_bwd_saved(_ptr(dy), ctypes.byref(dwt), ctypes.byref(dxt), T, din, dout, seed,
+                                   layer_id, _ptr(dx) if need_dx else None, _ptr(dw) if need_dw else None,
+                                   _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)))
+    return dx, dw, stats
+
+
 def layer_stats(stats: torch.Tensor, stream=None) -> Tuple[List[dict], bool]:
     """snip_layer_stats: synchronise, copy and derive the per-tensor reports.
     Returns (reports, any_nonfinite)."""
@@ -279,7 +384,10 @@ def workspace_bytes(op: str, *args) -> int:
     L = lib()
     return {"quantize": L.snip_quantize_workspace, "qgemm": L.snip_qgemm_workspace,
             "linear_fwd": L.snip_linear_fwd_workspace,
-            "linear_bwd": L.snip_linear_bwd_workspace}[op](*args)
+            "linear_bwd": L.snip_linear_bwd_workspace,
+            "quantize_dual": L.snip_quantize_dual_workspace,
+            "linear_fwd_save": L.snip_linear_fwd_save_workspace,
+            "linear_bwd_saved": L.snip_linear_bwd_saved_workspace}[op](*args)
 
 
 def version() -> int:

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -278,6 +279,73 @@ int run_quant_all(QPlan* const* ps, int n, hipStream_t s) {
   return SNIP_OK;
 }
 
+// One planned dual pass (row-wise and column-wise outputs of one tensor).
+struct DPlan {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  int format;
+  bool sr_row, sr_col;
+  uint64_t seed;
+  const float* amax_in;
+  const uint32_t* amax_part;
+  int n_amax_part;
+  DOut row, col;
+  snip_stats* stats_row;
+  snip_stats* stats_col;
+  int nwg;
+};
+
+// Enqueue dual passes sharing (format, sr_row, sr_col) in one launch.
+int run_dual_group(const DPlan* const* ps, int n, hipStream_t s) {
+  if (n == 0) return SNIP_OK;
+  DJobs jobs;
+  std::memset(&jobs, 0, sizeof(jobs));
+  int wg = 0;
+  double elems = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const DPlan& p = *ps[i];
+    jobs.j[i] = DJob{p.x, p.rows, p.cols, p.ld, p.amax_in, p.amax_part, p.n_amax_part, p.seed,
+                     p.row, p.col, wg, p.nwg};
+    wg += p.nwg;
+    elems += (double)p.rows * (double)p.cols;
+  }
+  for (int i = n; i < kMaxJobs; ++i) jobs.j[i].wg0 = 1 << 30;
+  jobs.n = n;
+  const DPlan& p = *ps[0];
+  // launch record: rounding = rounding_row + 2 * rounding_col
+  const int rnd = (p.sr_row ? SNIP_SR : SNIP_RNE) + 2 * (p.sr_col ? SNIP_SR : SNIP_RNE);
+  const int slot = timing_begin(LaunchTag{SNIP_LAUNCH_QUANTIZE, p.format, SNIP_BOTHWISE, rnd, elems}, s);
+  const hipError_t e = launch_quant_dual(p.format, p.sr_row, p.sr_col, jobs, wg, s);
+  timing_end(slot, s);
+  return hip_check(e, "dual quantize launch");
+}
+
+// Statistics finalisation of the dual passes' requested outputs.
+int run_finalize_dual(const DPlan* const* ps, int n, hipStream_t s) {
+  FJobs f;
+  std::memset(&f, 0, sizeof(f));
+  for (int i = 0; i < n; ++i) {
+    if (ps[i]->stats_row) f.j[f.n++] = FJob{ps[i]->row.part, ps[i]->nwg, ps[i]->stats_row};
+    if (ps[i]->stats_col) f.j[f.n++] = FJob{ps[i]->col.part, ps[i]->nwg, ps[i]->stats_col};
+  }
+  const int slot = f.n ? timing_begin(LaunchTag{SNIP_LAUNCH_FINALIZE, -1, -1, -1, (double)f.n}, s) : -1;
+  const hipError_t e = launch_finalize(f, s);
+  timing_end(slot, s);
+  return hip_check(e, "finalize launch");
+}
+
+DOut dout_of(const snip_qtensor& q, StatPart* part, uint32_t tensor_id) {
+  return DOut{static_cast<uint8_t*>(q.codes), static_cast<uint8_t*>(q.scales),
+              has_texp(q.format) ? q.tensor_exp : nullptr, part, tensor_id};
+}
+
+bool dual_format(int f) { return f == SNIP_FP8_E4M3 || f == SNIP_NVFP4 || f == SNIP_MXFP4; }
+
+int dual_wg(int f, int64_t rows, int64_t cols) {
+  const int64_t wg = ceil_div(rows, dual_tile_rows(f)) * ceil_div(cols, kColTileCols);
+  return (int)(wg < 1 ? 1 : wg > kQuantWG ? kQuantWG : wg);
+}
+
 int validate_qtensor(const snip_qtensor* q, const char* name, bool need_codes = true) {
   if (!q) return fail(SNIP_E_NULL, "%s: descriptor is NULL", name);
   if (!valid_format(q->format)) return fail(SNIP_E_FORMAT, "%s: unknown format %d", name, q->format);
@@ -385,6 +453,24 @@ size_t snip_linear_bwd_workspace(int64_t T, int64_t in, int64_t out, int fmt_dgr
   return 3 * kAmaxBytes + 4 * kPartBytes + qtensor_ws_bytes(fmt_dgrad, T, out) +
          qtensor_ws_bytes(fmt_dgrad, in, out) + qtensor_ws_bytes(fmt_wgrad, out, T) +
          qtensor_ws_bytes(fmt_wgrad, in, T) + align_up(split, kAlign);
+}
+
+size_t snip_quantize_dual_workspace(int64_t rows, int64_t cols, int format) {
+  if (rows <= 0 || cols <= 0 || !dual_format(format)) return 0;
+  return kAmaxBytes + 2 * kPartBytes;
+}
+
+size_t snip_linear_fwd_save_workspace(int64_t T, int64_t in, int64_t out, int format) {
+  if (T <= 0 || in <= 0 || out <= 0 || !dual_format(format)) return 0;
+  return 2 * kAmaxBytes + 4 * kPartBytes + qtensor_ws_bytes(format, T, in) + qtensor_ws_bytes(format, out, in) +
+         align_up(gemm_partial_bytes(format, T, out, in), kAlign);
+}
+
+size_t snip_linear_bwd_saved_workspace(int64_t T, int64_t in, int64_t out, int format) {
+  if (T <= 0 || in <= 0 || out <= 0 || !dual_format(format)) return 0;
+  const size_t split = std::max(gemm_partial_bytes(format, T, in, out), gemm_partial_bytes(format, out, in, T));
+  return kAmaxBytes + 2 * kPartBytes + qtensor_ws_bytes(format, T, out) + qtensor_ws_bytes(format, out, T) +
+         align_up(split, kAlign);
 }
 
 int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int layout, int format,
@@ -734,6 +820,265 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int
       if (use[i]) fin[nf++] = &p[i];
     r = run_finalize(fin, nf, s);
     if (r) return r;
+  }
+  return ok();
+}
+
+int snip_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld, int format,
+                       int rounding_row, int rounding_col, uint64_t seed, uint32_t tensor_id_row,
+                       uint32_t tensor_id_col, const float* amax_in, const snip_qtensor* out_row,
+                       const snip_qtensor* out_col, snip_stats* stats2, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (!x) return fail(SNIP_E_NULL, "snip_quantize_dual: x is NULL");
+  if (!dual_format(format))
+    return fail(SNIP_E_FORMAT, "snip_quantize_dual: format %d is not NVFP4, FP8_E4M3 or MXFP4", format);
+  if ((rounding_row != SNIP_RNE && rounding_row != SNIP_SR) || (rounding_col != SNIP_RNE && rounding_col != SNIP_SR))
+    return fail(SNIP_E_FORMAT, "snip_quantize_dual: unknown rounding (%d, %d)", rounding_row, rounding_col);
+  const int blk = block_of(format);
+  if (rows <= 0 || cols <= 0 || rows % blk || cols % blk)
+    return fail(SNIP_E_SHAPE, "snip_quantize_dual: rows=%lld cols=%lld must be positive multiples of %d",
+                (long long)rows, (long long)cols, blk);
+  if (ld < cols || ld % 8)
+    return fail(SNIP_E_SHAPE, "snip_quantize_dual: ld=%lld must be >= cols and a multiple of 8", (long long)ld);
+  int rc = validate_qtensor(out_row, "snip_quantize_dual: out_row");
+  if (rc) return rc;
+  rc = validate_qtensor(out_col, "snip_quantize_dual: out_col");
+  if (rc) return rc;
+  if (out_row->format != format || out_col->format != format)
+    return fail(SNIP_E_FORMAT, "snip_quantize_dual: output formats (%d, %d) != format %d", out_row->format,
+                out_col->format, format);
+  if (out_row->rows != rows || out_row->k != cols || out_col->rows != cols || out_col->k != rows)
+    return fail(SNIP_E_SHAPE, "snip_quantize_dual: out_row must be [%lld][%lld] and out_col [%lld][%lld]",
+                (long long)rows, (long long)cols, (long long)cols, (long long)rows);
+  if (!aligned(x, 16) || !aligned(amax_in, 4) || !aligned(stats2, 8) || !aligned(ws, 16))
+    return fail(SNIP_E_ALIGN, "snip_quantize_dual: misaligned pointer");
+  const size_t need = snip_quantize_dual_workspace(rows, cols, format);
+  if (!ws || ws_bytes < need) return fail(SNIP_E_WORKSPACE, "snip_quantize_dual: workspace of %zu bytes needed", need);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  uint32_t* apart = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  StatPart* prow = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+  StatPart* pcol = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+  DPlan p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.rows = rows;
+  p.cols = cols;
+  p.ld = ld;
+  p.format = format;
+  p.sr_row = rounding_row == SNIP_SR;
+  p.sr_col = rounding_col == SNIP_SR;
+  p.seed = seed;
+  p.amax_in = amax_in;
+  p.row = dout_of(*out_row, prow, tensor_id_row);
+  p.col = dout_of(*out_col, pcol, tensor_id_col);
+  p.stats_row = stats2 ? stats2 + 0 : nullptr;
+  p.stats_col = stats2 ? stats2 + 1 : nullptr;
+  p.nwg = dual_wg(format, rows, cols);
+  if (needs_amax(format) && !amax_in) {
+    APlan a{p.x, rows, cols, ld, apart, amax_wg(rows, cols)};
+    rc = run_amax(&a, 1, s);
+    if (rc) return rc;
+    p.amax_part = apart;
+    p.n_amax_part = a.nwg;
+  }
+  const DPlan* grp[1] = {&p};
+  rc = run_dual_group(grp, 1, s);
+  if (rc) return rc;
+  if (stats2) {
+    rc = run_finalize_dual(grp, 1, s);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, int64_t out, int format,
+                         uint64_t seed, uint32_t layer_id, float* y, const snip_qtensor* wt,
+                         const snip_qtensor* xt, snip_stats* stats4, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!x || !w || !y) return fail(SNIP_E_NULL, "snip_linear_fwd_save: x, w and y must be non-NULL");
+  if (!dual_format(format))
+    return fail(SNIP_E_FORMAT, "snip_linear_fwd_save: format %d is not NVFP4, FP8_E4M3 or MXFP4", format);
+  if (T <= 0 || in <= 0 || out <= 0 || T % 128 || in % 128 || out % 128)
+    return fail(SNIP_E_SHAPE, "snip_linear_fwd_save: T=%lld in=%lld out=%lld must be positive multiples of 128",
+                (long long)T, (long long)in, (long long)out);
+  int rc = validate_qtensor(wt, "snip_linear_fwd_save: wt");
+  if (rc) return rc;
+  rc = validate_qtensor(xt, "snip_linear_fwd_save: xt");
+  if (rc) return rc;
+  if (wt->format != format || xt->format != format)
+    return fail(SNIP_E_FORMAT, "snip_linear_fwd_save: wt/xt formats (%d, %d) != format %d", wt->format,
+                xt->format, format);
+  if (wt->rows != in || wt->k != out || xt->rows != in || xt->k != T)
+    return fail(SNIP_E_SHAPE, "snip_linear_fwd_save: wt must be [%lld][%lld] and xt [%lld][%lld]", (long long)in,
+                (long long)out, (long long)in, (long long)T);
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(stats4, 8) || !aligned(ws, 16))
+    return fail(SNIP_E_ALIGN, "snip_linear_fwd_save: misaligned pointer");
+  const size_t need = snip_linear_fwd_save_workspace(T, in, out, format);
+  if (!ws || ws_bytes < need)
+    return fail(SNIP_E_WORKSPACE, "snip_linear_fwd_save: workspace of %zu bytes needed", need);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  uint32_t* apx = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  uint32_t* apw = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  StatPart* part[4];
+  for (int i = 0; i < 4; ++i) part[i] = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+  QBuf qx = carve_q(cv, format, T, in);
+  QBuf qw = carve_q(cv, format, out, in);
+  const size_t split_bytes = gemm_partial_bytes(format, T, out, in);
+  float* split = split_bytes ? reinterpret_cast<float*>(cv.take(split_bytes)) : nullptr;
+
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* wsrc = static_cast<const uint16_t*>(w);
+  // X: row-wise RNE (forward A, id 8L+0) + column-wise SR (wgrad B, id 8L+5)
+  // W: row-wise RNE (forward B, id 8L+1) + column-wise SR (dgrad B, id 8L+3)
+  DPlan px{}, pw{};
+  px.x = xs;
+  px.rows = T;
+  px.cols = in;
+  px.ld = in;
+  px.row = dout_of(qx.t, part[0], 8u * layer_id + 0u);
+  px.col = dout_of(*xt, part[3], 8u * layer_id + 5u);
+  px.stats_row = stats4 ? stats4 + 0 : nullptr;
+  px.stats_col = stats4 ? stats4 + 3 : nullptr;
+  pw.x = wsrc;
+  pw.rows = out;
+  pw.cols = in;
+  pw.ld = in;
+  pw.row = dout_of(qw.t, part[1], 8u * layer_id + 1u);
+  pw.col = dout_of(*wt, part[2], 8u * layer_id + 3u);
+  pw.stats_row = stats4 ? stats4 + 1 : nullptr;
+  pw.stats_col = stats4 ? stats4 + 2 : nullptr;
+  for (DPlan* p : {&px, &pw}) {
+    p->format = format;
+    p->sr_row = false;
+    p->sr_col = true;
+    p->seed = seed;
+    p->nwg = dual_wg(format, p->rows, p->cols);
+  }
+  if (needs_amax(format)) {
+    APlan a[2] = {{xs, T, in, in, apx, amax_wg(T, in)}, {wsrc, out, in, in, apw, amax_wg(out, in)}};
+    rc = run_amax(a, 2, s);
+    if (rc) return rc;
+    px.amax_part = apx;
+    px.n_amax_part = a[0].nwg;
+    pw.amax_part = apw;
+    pw.n_amax_part = a[1].nwg;
+  }
+  const DPlan* grp[2] = {&px, &pw};
+  rc = run_dual_group(grp, 2, s);
+  if (rc) return rc;
+  rc = gemm_q(qx.t, qw.t, y, out, split, s);
+  if (rc) return rc;
+  if (stats4) {
+    rc = run_finalize_dual(grp, 2, s);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qtensor* xt, int64_t T,
+                          int64_t in, int64_t out, uint64_t seed, uint32_t layer_id, float* dx, float* dw,
+                          snip_stats* stats2, void* ws, size_t ws_bytes, void* stream) {
+  if (!dy) return fail(SNIP_E_NULL, "snip_linear_bwd_saved: dy is NULL");
+  int rc = validate_qtensor(wt, "snip_linear_bwd_saved: wt");
+  if (rc) return rc;
+  rc = validate_qtensor(xt, "snip_linear_bwd_saved: xt");
+  if (rc) return rc;
+  const int format = wt->format;
+  if (!dual_format(format) || xt->format != format)
+    return fail(SNIP_E_FORMAT, "snip_linear_bwd_saved: wt/xt formats (%d, %d) must match and be quantized",
+                wt->format, xt->format);
+  if (T <= 0 || in <= 0 || out <= 0 || T % 128 || in % 128 || out % 128)
+    return fail(SNIP_E_SHAPE, "snip_linear_bwd_saved: T=%lld in=%lld out=%lld must be positive multiples of 128",
+                (long long)T, (long long)in, (long long)out);
+  if (wt->rows != in || wt->k != out || xt->rows != in || xt->k != T)
+    return fail(SNIP_E_SHAPE, "snip_linear_bwd_saved: wt must be [%lld][%lld] and xt [%lld][%lld]", (long long)in,
+                (long long)out, (long long)in, (long long)T);
+  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw, 16) || !aligned(stats2, 8) || !aligned(ws, 16))
+    return fail(SNIP_E_ALIGN, "snip_linear_bwd_saved: misaligned pointer");
+  const size_t need = snip_linear_bwd_saved_workspace(T, in, out, format);
+  if (!ws || ws_bytes < need)
+    return fail(SNIP_E_WORKSPACE, "snip_linear_bwd_saved: workspace of %zu bytes needed", need);
+  if (!dx && !dw) return ok();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  uint32_t* ap = reinterpret_cast<uint32_t*>(cv.take(kAmaxBytes));
+  StatPart* prow = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+  StatPart* pcol = reinterpret_cast<StatPart*>(cv.take(kPartBytes));
+  QBuf qr = carve_q(cv, format, T, out);      // dY row-wise  [T][out]  (dgrad A)
+  QBuf qc = carve_q(cv, format, out, T);      // dY column-wise [out][T] (wgrad A)
+  const size_t split_bytes = std::max(gemm_partial_bytes(format, T, in, out), gemm_partial_bytes(format, out, in, T));
+  float* split = split_bytes ? reinterpret_cast<float*>(cv.take(split_bytes)) : nullptr;
+  const uint16_t* dys = static_cast<const uint16_t*>(dy);
+  int n_ap = 0;
+  if (needs_amax(format)) {
+    APlan a{dys, T, out, out, ap, amax_wg(T, out)};
+    rc = run_amax(&a, 1, s);
+    if (rc) return rc;
+    n_ap = a.nwg;
+  }
+  if (dx && dw) {       // both layouts from one read of dY
+    DPlan p{};
+    p.x = dys;
+    p.rows = T;
+    p.cols = out;
+    p.ld = out;
+    p.format = format;
+    p.sr_row = true;
+    p.sr_col = true;
+    p.seed = seed;
+    p.amax_part = n_ap ? ap : nullptr;
+    p.n_amax_part = n_ap;
+    p.row = dout_of(qr.t, prow, 8u * layer_id + 2u);
+    p.col = dout_of(qc.t, pcol, 8u * layer_id + 4u);
+    p.stats_row = stats2 ? stats2 + 0 : nullptr;
+    p.stats_col = stats2 ? stats2 + 1 : nullptr;
+    p.nwg = dual_wg(format, T, out);
+    const DPlan* grp[1] = {&p};
+    rc = run_dual_group(grp, 1, s);
+    if (rc) return rc;
+    rc = gemm_q(qr.t, *wt, dx, in, split, s);
+    if (rc) return rc;
+    rc = gemm_q(qc.t, *xt, dw, in, split, s);
+    if (rc) return rc;
+    if (stats2) {
+      rc = run_finalize_dual(grp, 1, s);
+      if (rc) return rc;
+    }
+    return ok();
+  }
+  // one GEMM only: the one layout it needs
+  const bool row = dx != nullptr;
+  QPlan p{};
+  p.x = dys;
+  p.rows = T;
+  p.cols = out;
+  p.ld = out;
+  p.layout = row ? SNIP_ROWWISE : SNIP_COLWISE;
+  p.format = format;
+  p.sr = true;
+  p.seed = seed;
+  p.tensor_id = 8u * layer_id + (row ? 2u : 4u);
+  p.amax_part = n_ap ? ap : nullptr;
+  p.n_amax_part = n_ap;
+  const snip_qtensor& q = row ? qr.t : qc.t;
+  p.codes = static_cast<uint8_t*>(q.codes);
+  p.scales = static_cast<uint8_t*>(q.scales);
+  p.texp = has_texp(format) ? q.tensor_exp : nullptr;
+  p.part = row ? prow : pcol;
+  p.nwg = quant_wg(p.layout, format, T, out);
+  p.stats = stats2 ? stats2 + (row ? 0 : 1) : nullptr;
+  const QPlan* grp[1] = {&p};
+  rc = run_quant_group(grp, 1, s);
+  if (rc) return rc;
+  rc = row ? gemm_q(qr.t, *wt, dx, in, split, s) : gemm_q(qc.t, *xt, dw, in, split, s);
+  if (rc) return rc;
+  if (stats2) {
+    rc = run_finalize(grp, 1, s);
+    if (rc) return rc;
   }
   return ok();
 }

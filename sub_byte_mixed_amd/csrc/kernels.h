@@ -56,6 +56,31 @@ struct QJobs {
   int32_t n;
 };
 
+// Dual quantize pass of one tensor: one read of x[rows][cols] gives its
+// row-wise codes ([rows][cols], blocks along cols) and its column-wise codes
+// ([cols][rows], blocks down the columns), in one format.
+struct DOut {
+  uint8_t* codes;
+  uint8_t* scales;
+  int32_t* texp;                 // tensor exponent out (NVFP4/FP8) or null
+  StatPart* part;                // [nwg]
+  uint32_t tensor_id;
+};
+struct DJob {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  const float* amax_in;
+  const uint32_t* amax_part;
+  int32_t n_amax_part;
+  uint64_t seed;
+  DOut row, col;
+  int32_t wg0, nwg;
+};
+struct DJobs {
+  DJob j[kMaxJobs];
+  int32_t n;
+};
+
 // Statistics finalisation of one tensor.
 struct FJob {
   const StatPart* part;
@@ -98,6 +123,8 @@ size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K);
 hipError_t launch_amax(const AJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_quant_row(int format, bool sr, const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_quant_col(int format, bool sr, const QJobs& jobs, int total_wg, hipStream_t s);
+hipError_t launch_quant_dual(int format, bool sr_row, bool sr_col, const DJobs& jobs, int total_wg,
+                             hipStream_t s);
 hipError_t launch_bf16_copy(const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_bf16_transpose(const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_finalize(const FJobs& jobs, hipStream_t s);
@@ -116,6 +143,8 @@ void timing_end(int slot, hipStream_t s);
 // Work decomposition helpers shared by host and kernels.
 constexpr int kColTileRows = 256;   // column-wise quantizer: source rows per tile
 constexpr int kColTileCols = 128;   // source columns per tile (2 per lane)
+// dual quantizer: source rows per tile, one block row (16, MX 32) per wave
+__host__ __device__ constexpr int dual_tile_rows(int format) { return format == SNIP_MXFP4 ? 128 : 64; }
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace snip

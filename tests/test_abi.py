@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     # and nothing else is exported under the snip_ prefix
@@ -139,6 +139,64 @@ def test_linear_validation(L):
                              1 << 30, None) == -4
     assert L.snip_linear_bwd(P, P2, P3, 128, 64, 128, S.NVFP4, S.FP8, 0, 0, None, dx, dw, None, ws,
                              64, None) == -5
+
+
+def dual(L, x=P, rows=64, cols=64, ld=64, fmt=S.NVFP4, rr=0, rc=1, out_row=None, out_col=None,
+         ws=P + 0x400000, ws_bytes=1 << 20, amax=None, stats=None):
+    out_row = out_row or qdesc(fmt, rows, cols)
+    out_col = out_col or qdesc(fmt, cols, rows, codes=P2 + 0x10000)
+    return L.snip_quantize_dual(x, rows, cols, ld, fmt, rr, rc, 0, 0, 1, amax, ctypes.byref(out_row),
+                                ctypes.byref(out_col), stats, ws, ws_bytes, None)
+
+
+def test_quantize_dual_validation(L):
+    assert dual(L, x=None) == -1
+    assert dual(L, fmt=S.BF16) == -4 and "not NVFP4" in err(L)
+    assert dual(L, rr=2) == -4
+    assert dual(L, rc=-1) == -4
+    assert dual(L, rows=40) == -2                               # rows % 16
+    assert dual(L, cols=40, ld=40) == -2                        # cols % 16
+    assert dual(L, fmt=S.MXFP4, rows=48) == -2                  # MX: % 32
+    assert dual(L, ld=60) == -2
+    assert dual(L, out_row=qdesc(S.NVFP4, 64, 32)) == -2        # shape mismatch
+    assert dual(L, out_col=qdesc(S.FP8, 64, 64, scales=None)) == -4
+    assert dual(L, out_col=qdesc(S.NVFP4, 64, 64, texp=None)) == -1
+    assert dual(L, x=P + 2) == -3
+    assert dual(L, ws_bytes=1024) == -5 and "workspace" in err(L)
+    assert L.snip_quantize_dual_workspace(64, 64, S.NVFP4) > 0
+    assert L.snip_quantize_dual_workspace(64, 64, S.BF16) == 0
+
+
+def test_saved_linear_validation(L):
+    ws, y, dx, dw = P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000
+    T, din, dout = 256, 128, 384
+    wt, xt = qdesc(S.NVFP4, din, dout), qdesc(S.NVFP4, din, T, codes=P2 + 0x20000)
+    big = 1 << 30
+
+    def fwd(x=P, w=P2, T=T, din=din, dout=dout, fmt=S.NVFP4, wt=wt, xt=xt, ws_bytes=big):
+        return L.snip_linear_fwd_save(x, w, T, din, dout, fmt, 0, 0, y, ctypes.byref(wt), ctypes.byref(xt),
+                                      None, ws, ws_bytes, None)
+    assert fwd(x=None) == -1
+    assert fwd(fmt=S.BF16) == -4
+    assert fwd(T=200) == -2                                      # T % 128
+    assert fwd(dout=200, wt=qdesc(S.NVFP4, din, 200)) == -2
+    assert fwd(wt=qdesc(S.NVFP4, din, 256)) == -2                # wt shape
+    assert fwd(xt=qdesc(S.FP8, din, T, scales=None)) == -4       # xt format
+    assert fwd(x=P + 4) == -3
+    assert fwd(ws_bytes=64) == -5
+    assert L.snip_linear_fwd_save_workspace(T, din, dout, S.NVFP4) > 0
+
+    def bwd(dy=P, T=T, din=din, dout=dout, wt=wt, xt=xt, dx=dx, dw=dw, ws_bytes=big):
+        return L.snip_linear_bwd_saved(dy, ctypes.byref(wt), ctypes.byref(xt), T, din, dout, 0, 0, dx, dw,
+                                       None, ws, ws_bytes, None)
+    assert bwd(dy=None) == -1
+    assert bwd(xt=qdesc(S.MXFP4, din, T)) == -4                  # formats differ
+    assert bwd(wt=qdesc(S.BF16, din, dout)) == -4
+    assert bwd(T=128) == -2                                      # xt is [in][256]
+    assert bwd(dout=200) == -2
+    assert bwd(dx=dx + 4) == -3
+    assert bwd(ws_bytes=64) == -5
+    assert L.snip_linear_bwd_saved_workspace(T, din, dout, S.BF16) == 0
 
 
 def test_layer_stats_validation(L):
