@@ -14,6 +14,10 @@ except for the `copy` calibration run).
       dispatch), each scaled by the factor that makes the calibration copy
       read and write exactly its known size. The summary records a hash of
       the kernel sources, so a later change of the kernel invalidates it.
+  python -m sub_byte_mixed_amd.profiling vendor --workload NAME --out OUT_MD
+      times the vendor library's fp16 and bf16 GEMM (torch.mm, hipBLASLt) on
+      the workload's forward, dgrad and wgrad shapes: a reference point for
+      what a tuned dense GEMM reaches at these sizes (not part of the path).
 """
 from __future__ import annotations
 
@@ -146,6 +150,49 @@ def cmd_traffic(a):
     print(json.dumps(d))
 
 
+def cmd_vendor(a):
+    import torch
+    sys.path.insert(0, ROOT)
+    import synth
+    wl = synth.WORKLOADS[a.workload]
+    T = wl.tokens
+    shapes = []
+    for l in wl.layers:
+        shapes += [(T, l.d_out, l.d_in), (T, l.d_in, l.d_out), (l.d_out, l.d_in, T)]
+    lines = [f"# Vendor dense GEMM on the {a.workload} GEMM shapes (reference point)", "",
+             "torch.mm(a, b.t()) with a [M][K] and b [N][K] (the library's operand layout), the",
+             "ROCm PyTorch build's hipBLASLt path; 3 warm-up calls, then the mean of "
+             f"{a.reps} back-to-back calls", "timed with HIP events. Command (from the repository root):", "",
+             "```", f"python -m sub_byte_mixed_amd.profiling vendor --workload {a.workload} --out {a.out}", "```",
+             "", "| dtype | M | N | K | us | TFLOP/s |", "|---|---|---|---|---|---|"]
+    summary = {}
+    for dt in (torch.float16, torch.bfloat16):
+        fl, us_tot = 0.0, 0.0
+        for (M, N, K) in shapes:
+            x = torch.randn(M, K, device="cuda").to(dt)
+            y = torch.randn(N, K, device="cuda").to(dt)
+            for _ in range(3):
+                torch.mm(x, y.t())
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(a.reps):
+                torch.mm(x, y.t())
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / a.reps * 1e3
+            fl += 2.0 * M * N * K
+            us_tot += us
+            lines.append(f"| {str(dt)[6:]} | {M} | {N} | {K} | {us:.1f} | {2.0 * M * N * K / us / 1e6:.0f} |")
+        summary[str(dt)[6:]] = round(fl / us_tot / 1e6, 1)
+        print(f"{dt}: {summary[str(dt)[6:]]} TFLOP/s over the step's GEMMs", flush=True)
+    lines += ["", "Aggregate over the step's GEMM shapes (total flops / total time): " +
+              ", ".join(f"{k} {v} TFLOP/s" for k, v in summary.items()), ""]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(a.out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -163,8 +210,12 @@ def main(argv=None):
         f.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     f.add_argument("--copy-kernel", default="MulFunctor", help="substring of the copy kernel's name")
     f.add_argument("--copy-mib", type=int, default=1024)
+    v = sub.add_parser("vendor")
+    v.add_argument("--workload", default="tinyllama1b")
+    v.add_argument("--out", required=True)
+    v.add_argument("--reps", type=int, default=20)
     a = ap.parse_args(argv)
-    {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic}[a.cmd_name](a)
+    {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic, "vendor": cmd_vendor}[a.cmd_name](a)
 
 
 if __name__ == "__main__":
