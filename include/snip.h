@@ -325,7 +325,9 @@ int64_t snip_qtensor_bytes(int format, int64_t rows, int64_t k, int part);
 
 /* One timed launch. `work` is the launch's algorithmic work: GEMM 2*M*N*K
  * flop; quantize and amax: source elements read (all tensors of the
- * launch); split-K: output elements; finalize: tensors. `ms` is the time
+ * launch); split-K: output elements; finalize: tensors (the layer calls
+ * finalise their statistics inside their last GEMM launch, as extra
+ * workgroups, and make no finalize launch). `ms` is the time
  * between HIP events recorded on the launch's stream right before and
  * right after it. */
 typedef struct snip_launch_record {

@@ -246,13 +246,19 @@ int run_amax(const APlan* ps, int n, hipStream_t s) {
   return hip_check(e, "amax launch");
 }
 
-int run_finalize(const QPlan* const* ps, int n, hipStream_t s) {
+// Finalisation jobs of the passes that requested statistics.
+FJobs fjobs_of(const QPlan* const* ps, int n) {
   FJobs f;
   std::memset(&f, 0, sizeof(f));
   for (int i = 0; i < n; ++i) {
     if (!ps[i] || !ps[i]->stats) continue;
     f.j[f.n++] = FJob{ps[i]->part, ps[i]->nwg, ps[i]->stats};
   }
+  return f;
+}
+
+int run_finalize(const QPlan* const* ps, int n, hipStream_t s) {
+  const FJobs f = fjobs_of(ps, n);
   const int slot = f.n ? timing_begin(LaunchTag{SNIP_LAUNCH_FINALIZE, -1, -1, -1, (double)f.n}, s) : -1;
   const hipError_t e = launch_finalize(f, s);
   timing_end(slot, s);
@@ -321,13 +327,18 @@ int run_dual_group(const DPlan* const* ps, int n, hipStream_t s) {
 }
 
 // Statistics finalisation of the dual passes' requested outputs.
-int run_finalize_dual(const DPlan* const* ps, int n, hipStream_t s) {
+FJobs fjobs_of_dual(const DPlan* const* ps, int n) {
   FJobs f;
   std::memset(&f, 0, sizeof(f));
   for (int i = 0; i < n; ++i) {
     if (ps[i]->stats_row) f.j[f.n++] = FJob{ps[i]->row.part, ps[i]->nwg, ps[i]->stats_row};
     if (ps[i]->stats_col) f.j[f.n++] = FJob{ps[i]->col.part, ps[i]->nwg, ps[i]->stats_col};
   }
+  return f;
+}
+
+int run_finalize_dual(const DPlan* const* ps, int n, hipStream_t s) {
+  const FJobs f = fjobs_of_dual(ps, n);
   const int slot = f.n ? timing_begin(LaunchTag{SNIP_LAUNCH_FINALIZE, -1, -1, -1, (double)f.n}, s) : -1;
   const hipError_t e = launch_finalize(f, s);
   timing_end(slot, s);
@@ -559,6 +570,7 @@ int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t l
                                  (long long)b->rows);
   if (!aligned(c, 16)) return fail(SNIP_E_ALIGN, "snip_qgemm: c must be 16-byte aligned");
   GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
   g.a = static_cast<const uint8_t*>(a->codes);
   g.b = static_cast<const uint8_t*>(b->codes);
   g.as = static_cast<const uint8_t*>(a->scales);
@@ -600,9 +612,13 @@ QBuf carve_q(Carver& cv, int f, int64_t rows, int64_t k) {
   return q;
 }
 
+// One GEMM; `fin` (may be null) lists statistics finalisations that the
+// launch runs as extra workgroups after the quantize launches before it.
 int gemm_q(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, float* partial,
-           hipStream_t s) {
+           hipStream_t s, const FJobs* fin = nullptr) {
   GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  if (fin) g.fin = *fin;
   g.a = static_cast<const uint8_t*>(a.codes);
   g.b = static_cast<const uint8_t*>(b.codes);
   g.as = static_cast<const uint8_t*>(a.scales);
@@ -685,19 +701,16 @@ int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t
     r = run_quant_group(grp, 2, s);
     if (r) return r;
   }
+  const QPlan* fin_grp[2] = {&px, &pw};
+  const FJobs fin = fjobs_of(fin_grp, stats2 ? 2 : 0);
   if (bf) {
     snip_qtensor ax{SNIP_BF16, 0, T, in, const_cast<void*>(x), nullptr, nullptr};
     snip_qtensor aw{SNIP_BF16, 0, out, in, const_cast<void*>(w), nullptr, nullptr};
-    r = gemm_q(ax, aw, y, out, split, s);
+    r = gemm_q(ax, aw, y, out, split, s, &fin);
   } else {
-    r = gemm_q(qx.t, qw.t, y, out, split, s);
+    r = gemm_q(qx.t, qw.t, y, out, split, s, &fin);
   }
   if (r) return r;
-  if (stats2) {
-    const QPlan* grp[2] = {&px, &pw};
-    r = run_finalize(grp, 2, s);
-    if (r) return r;
-  }
   return ok();
 }
 
@@ -805,20 +818,18 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int
   const size_t split_bytes = std::max(gemm_partial_bytes(fmt_dgrad, T, in, out),
                                       gemm_partial_bytes(fmt_wgrad, out, in, T));
   float* split = split_bytes ? reinterpret_cast<float*>(cv.take(split_bytes)) : nullptr;
+  // statistics are finalised by the last GEMM launch
+  const QPlan* fin_grp[4];
+  int nfin = 0;
+  for (int i = 0; i < 4 && stats4; ++i)
+    if (use[i]) fin_grp[nfin++] = &p[i];
+  const FJobs fin = fjobs_of(fin_grp, nfin);
   if (dx) {
-    r = gemm_q(q[0].t, q[1].t, dx, in, split, s);       // [T][out] . ([in][out])^T
+    r = gemm_q(q[0].t, q[1].t, dx, in, split, s, dw ? nullptr : &fin);   // [T][out] . ([in][out])^T
     if (r) return r;
   }
   if (dw) {
-    r = gemm_q(q[2].t, q[3].t, dw, in, split, s);       // [out][T] . ([in][T])^T
-    if (r) return r;
-  }
-  if (stats4) {
-    const QPlan* fin[4];
-    int nf = 0;
-    for (int i = 0; i < 4; ++i)
-      if (use[i]) fin[nf++] = &p[i];
-    r = run_finalize(fin, nf, s);
+    r = gemm_q(q[2].t, q[3].t, dw, in, split, s, &fin);                  // [out][T] . ([in][T])^T
     if (r) return r;
   }
   return ok();
@@ -969,12 +980,9 @@ int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, in
   const DPlan* grp[2] = {&px, &pw};
   rc = run_dual_group(grp, 2, s);
   if (rc) return rc;
-  rc = gemm_q(qx.t, qw.t, y, out, split, s);
+  const FJobs fin = fjobs_of_dual(grp, 2);      // empty when stats4 is NULL
+  rc = gemm_q(qx.t, qw.t, y, out, split, s, &fin);
   if (rc) return rc;
-  if (stats4) {
-    rc = run_finalize_dual(grp, 2, s);
-    if (rc) return rc;
-  }
   return ok();
 }
 
@@ -1040,14 +1048,11 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
     const DPlan* grp[1] = {&p};
     rc = run_dual_group(grp, 1, s);
     if (rc) return rc;
+    const FJobs fin = fjobs_of_dual(grp, 1);
     rc = gemm_q(qr.t, *wt, dx, in, split, s);
     if (rc) return rc;
-    rc = gemm_q(qc.t, *xt, dw, in, split, s);
+    rc = gemm_q(qc.t, *xt, dw, in, split, s, &fin);
     if (rc) return rc;
-    if (stats2) {
-      rc = run_finalize_dual(grp, 1, s);
-      if (rc) return rc;
-    }
     return ok();
   }
   // one GEMM only: the one layout it needs
@@ -1074,12 +1079,9 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
   const QPlan* grp[1] = {&p};
   rc = run_quant_group(grp, 1, s);
   if (rc) return rc;
-  rc = row ? gemm_q(qr.t, *wt, dx, in, split, s) : gemm_q(qc.t, *xt, dw, in, split, s);
+  const FJobs fin = fjobs_of(grp, 1);
+  rc = row ? gemm_q(qr.t, *wt, dx, in, split, s, &fin) : gemm_q(qc.t, *xt, dw, in, split, s, &fin);
   if (rc) return rc;
-  if (stats2) {
-    rc = run_finalize(grp, 1, s);
-    if (rc) return rc;
-  }
   return ok();
 }
 

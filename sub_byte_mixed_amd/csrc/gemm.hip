@@ -141,6 +141,7 @@ __global__ __launch_bounds__(NT, BM * BN > 256 * 128 ? 1 : 2) void gemm_kernel(G
   constexpr int TM = WM / 16, TN = WN / 16;                // 16x16 MFMA tiles per wave
   constexpr int KS = UE * UK;                              // K elements per stage
   __shared__ __align__(1024) uint8_t smem[S * STAGE];
+  if (finalize_workgroup(g)) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -405,7 +406,7 @@ size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K) {
 
 template <int FMT>
 static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
-  const dim3 grid((unsigned)p.tiles, (unsigned)p.ksplit);
+  const dim3 grid((unsigned)(p.tiles + g.fin.n), (unsigned)p.ksplit);
   if constexpr (FMT == SNIP_FP8_E4M3) {
     if (p.bm == 256 && p.bn == 128) {     // 3-stage ring: 72 KiB, two per CU
       hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 3, 1>), grid, dim3(NT), 0, s, g);

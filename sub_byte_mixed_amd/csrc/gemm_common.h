@@ -5,6 +5,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "stats_common.h"
 
 namespace snip {
 
@@ -28,6 +29,17 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
   const int r = id - group * GM * tiles_n;
   tm = first + r % gm;
   tn = r / gm;
+}
+
+// Workgroups past the last tile finalise the statistics jobs the launch
+// carries (one job each, on the first K split); the kernel boundary orders
+// them after the quantize launches that wrote the partials. Returns true
+// for such a workgroup, which then does nothing else.
+__device__ __forceinline__ bool finalize_workgroup(const GemmArgs& g) {
+  const int tiles = g.tiles_m * g.tiles_n;
+  if ((int)blockIdx.x < tiles) return false;
+  if (blockIdx.y == 0) finalize_one(g.fin.j[blockIdx.x - tiles]);
+  return true;
 }
 
 // Epilogue of a 2x2-wave tile: the wave's accumulators (lane holds rows

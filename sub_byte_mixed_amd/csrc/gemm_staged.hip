@@ -44,6 +44,7 @@ __global__ __launch_bounds__(NT, 2) void staged_gemm_kernel(GemmArgs g) {
   constexpr int LS = NS ? BMS * NS : 0;
   constexpr int STAGE = 2 * LA + 2 * LS;
   __shared__ __align__(16) uint8_t smem[2 * STAGE];
+  if (finalize_workgroup(g)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;

@@ -105,6 +105,8 @@ struct GemmArgs {
   float* partial;          // split-K scratch [ksplit][M][N] or null (no split)
   int32_t tiles_m, tiles_n;
   int64_t kchunk;          // K elements per split (set by launch_gemm)
+  FJobs fin;               // statistics finalisations run as extra workgroups
+                           // of the launch (fin.n == 0: none)
 };
 
 // Tile shape and K split chosen on the host for one GEMM.

@@ -18,6 +18,7 @@
 // the codes in LDS and writes each output row segment (128 bytes of codes)
 // with 8-byte stores. All kernels are HBM-bound scans.
 #include "quant_common.h"
+#include "stats_common.h"
 
 namespace snip {
 
@@ -430,44 +431,7 @@ __global__ __launch_bounds__(256) void bf16_transpose_kernel(QJobs jobs) {
 
 // ------------------------------------------------------------ finalisation
 // One workgroup per tensor: fixed-order sum of the partials.
-__global__ __launch_bounds__(256) void finalize_kernel(FJobs jobs) {
-  const FJob J = jobs.j[blockIdx.x];
-  double e2 = 0.0, x2 = 0.0;
-  uint32_t nf = 0u, am = 0u;
-  for (int i = threadIdx.x; i < J.nwg; i += 256) {
-    const StatPart p = J.part[i];
-    e2 += p.e2;
-    x2 += p.x2;
-    nf += p.nf;
-    am = p.amax_bits > am ? p.amax_bits : am;
-  }
-  __shared__ uint32_t ured[8];
-  __shared__ double dred[8];
-  e2 = wave_sum(e2);
-  x2 = wave_sum(x2);
-  nf = wave_sum_u(nf);
-  am = wave_max_u(am);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    dred[2 * wave] = e2;
-    dred[2 * wave + 1] = x2;
-    ured[2 * wave] = nf;
-    ured[2 * wave + 1] = am;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    snip_stats s{0.0, 0.0, 0.0f, 0u};
-    uint32_t m = 0u;
-    for (int w = 0; w < 4; ++w) {
-      s.sum_err2 += dred[2 * w];
-      s.sum_x2 += dred[2 * w + 1];
-      s.n_nonfinite += ured[2 * w];
-      m = ured[2 * w + 1] > m ? ured[2 * w + 1] : m;
-    }
-    s.amax = __uint_as_float(m);
-    *J.out = s;
-  }
-}
+__global__ __launch_bounds__(256) void finalize_kernel(FJobs jobs) { finalize_one(jobs.j[blockIdx.x]); }
 
 // ------------------------------------------------------------ launchers
 hipError_t launch_amax(const AJobs& jobs, int total_wg, hipStream_t s) {
