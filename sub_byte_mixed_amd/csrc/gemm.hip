@@ -49,8 +49,8 @@
 // longer read.
 //
 // Tiling: a workgroup of 256 threads (2x2 waves) owns a BM x BN output tile:
-// 256x256 (one workgroup per CU), 256x128 (FP8, two per CU) or 128x128 (two
-// per CU), as plan_gemm decides from the problem's tile rounds. Tile order: the hardware hands workgroups to the 8 XCDs
+// 256x256 (one workgroup per CU), 256x128 (FP8 and NVFP4, two per CU) or
+// 128x128 (two per CU), as plan_gemm decides from the problem's tile rounds. Tile order: the hardware hands workgroups to the 8 XCDs
 // round-robin; tile ids are remapped so each XCD works on a contiguous range,
 // and tiles are ordered in groups of 8 tile-rows so that concurrently running
 // tiles share A and B panels in that XCD's L2. Skinny problems split K across
@@ -340,7 +340,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nspl
 // Host-side plan: kernel, tile shape and K split for a problem.
 //
 // A CU holds one 256x256 workgroup or two smaller ones (128x128, or 256x128
-// for FP8), so a launch runs in rounds of 256 big or 512 smaller tiles. Per
+// for FP8 and NVFP4), so a launch runs in rounds of 256 big or 512 smaller
+// tiles. Per
 // unit of tile area the bigger tiles run faster by measured factors (less
 // decode and operand traffic per MFMA; for MX-FP4 and BF16 the 128x128
 // tiles run on the register-staged kernel, gemm_staged.hip, which nearly
@@ -357,7 +358,12 @@ static double big_tile_gain(int format) {
     default: return 1.02;
   }
 }
-constexpr double kRectGainFp8 = 1.17;     // 256x128 over 128x128, FP8
+// 256x128 over 128x128: FP8 (3-stage ring, 72 KiB) and NVFP4 (2-stage
+// ring, 54 KiB; a wave's 128x64 sub-tile needs 3 decode instructions per
+// MFMA instead of 4), both two workgroups per CU
+static double rect_gain(int format) {
+  return format == SNIP_FP8_E4M3 ? 1.17 : format == SNIP_NVFP4 ? 1.12 : 0.0;
+}
 
 static double rounds2(int64_t tiles) {    // two tiles per CU
   const int64_t rem = tiles % 512;
@@ -371,7 +377,7 @@ GemmPlan plan_gemm(int format, int64_t M, int64_t N, int64_t K) {
   const int64_t trect = ceil_div(M, 256) * ceil_div(N, 128);
   const double time128 = rounds2(t128);
   const double time256 = (double)ceil_div(t256, 256) * 2.0 / big_tile_gain(format);
-  const double timerect = format == SNIP_FP8_E4M3 ? rounds2(trect) * 2.0 / kRectGainFp8 : 1e30;
+  const double timerect = rect_gain(format) > 0.0 ? rounds2(trect) * 2.0 / rect_gain(format) : 1e30;
   p.staged = 0;
   p.ksplit = 1;
   p.kchunk = K;
@@ -410,6 +416,12 @@ static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   if constexpr (FMT == SNIP_FP8_E4M3) {
     if (p.bm == 256 && p.bn == 128) {     // 3-stage ring: 72 KiB, two per CU
       hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 3, 1>), grid, dim3(NT), 0, s, g);
+      return;
+    }
+  }
+  if constexpr (FMT == SNIP_NVFP4) {
+    if (p.bm == 256 && p.bn == 128) {     // 2-stage ring: 54 KiB, two per CU
+      hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 2, 1>), grid, dim3(NT), 0, s, g);
       return;
     }
   }

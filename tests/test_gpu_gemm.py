@@ -75,7 +75,8 @@ def test_gemm_ldc_and_overwrite():
 # with ragged M and N. Sampled output rows (all columns) against the oracle.
 PLAN_CASES = [
     (S.FP8, 4000, 5600, 1024),      # 256x128
-    (S.NVFP4, 8000, 4000, 512),     # 256x256
+    (S.NVFP4, 8000, 4000, 512),     # 256x128, 2-stage ring
+    (S.NVFP4, 4000, 5600, 1024),    # 256x128, 2-stage ring
     (S.FP8, 8000, 4000, 512),       # 256x128
     (S.MXFP4, 8000, 4000, 512),     # 256x256
     (S.BF16, 8000, 4000, 256),      # 256x256
