@@ -63,6 +63,27 @@ def e8m0_decode(codes: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, codes - 127)
 
 
+# ---------------------------------------------------------------- BF16 (as a block scale)
+def bf16_scale_encode(t: np.ndarray) -> np.ndarray:
+    """Round non-negative finite fp32 values to bfloat16, nearest with ties
+    to the even code: the two bf16 neighbours are the fp32 pattern with its
+    low 16 bits cleared and that plus one bf16 step; the nearer one wins, a
+    tie goes to the one whose last kept bit is 0. Returns the 16-bit codes."""
+    t = np.asarray(t, dtype=np.float32)
+    bits = t.view(np.uint32).astype(np.uint64)
+    lo = bits & np.uint64(0xFFFF0000)
+    hi = lo + np.uint64(0x10000)
+    rem = bits - lo                                    # distance above lo, in fp32 ulps
+    half = np.uint64(0x8000)
+    lo_even = (lo >> np.uint64(16)) & np.uint64(1) == 0
+    up = (rem > half) | ((rem == half) & ~lo_even)
+    return (np.where(up, hi, lo) >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_decode(codes: np.ndarray) -> np.ndarray:
+    return (np.asarray(codes, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 # ---------------------------------------------------------------- rounding
 def round_nearest_even(a: np.ndarray, grid: np.ndarray) -> np.ndarray:
     """Index of the grid value nearest to a >= 0; ties go to the even index;

@@ -27,6 +27,14 @@ Readings (the pages do not fix these):
   * MX: per-32 E8M0 scale X_b = floor(log2 a_b) - 2 (OCP rule, E2M1 largest
     exponent 2), clamped to [-127, 127], X_b = -127 for a zero block;
     r = ldexp(x, -X_b); values in (6, 8) saturate to 6.
+  * FP4 design-space variants [FP4 All the Way summary, Outline: block size,
+    scaling format and rounding were explored]: E2M1 codes with a block of
+    16 or 32 and an E4M3, E8M0 or BF16 block scale. E4M3 scales follow the
+    NVFP4 rules with any block (tensor scale, s = E4M3_RNE(a_b / 6)); E8M0
+    scales follow the MX rule with any block; a BF16 scale is
+    s = bf16_RNE(fp32(a_b / 6)) of the raw block max (bf16 has the range, so
+    no tensor scale), then r = fp32(x * fp32(1 / s)). NVFP4 is the (16,
+    E4M3) variant and MX-FP4 the (32, E8M0) one.
   * Non-finite inputs lie outside the contract: they are counted, the tensor
     max ignores them, the statistics sum only finite elements, and the codes
     of a block holding one are unspecified (reported in `bad_blocks`).
@@ -39,7 +47,11 @@ from . import formats as F
 from .philox import r16 as philox_r16
 
 BF16, FP8, NVFP4, MXFP4 = 0, 1, 2, 3
-BLOCK = {NVFP4: 16, MXFP4: 32, FP8: 1, BF16: 1}
+# design-space variants of FP4 (quantizer only): E2M1 with (block, scale)
+FP4_E4M3_B32, FP4_E8M0_B16, FP4_BF16_B16, FP4_BF16_B32 = 4, 5, 6, 7
+FP4_VARIANT = {NVFP4: (16, "e4m3"), MXFP4: (32, "e8m0"), FP4_E4M3_B32: (32, "e4m3"),
+               FP4_E8M0_B16: (16, "e8m0"), FP4_BF16_B16: (16, "bf16"), FP4_BF16_B32: (32, "bf16")}
+BLOCK = {FP8: 1, BF16: 1, **{f: v[0] for f, v in FP4_VARIANT.items()}}
 NVFP4_RANGE = 6.0 * 448.0   # largest E2M1 magnitude x largest E4M3 scale
 FP8_RANGE = 448.0
 
@@ -131,7 +143,8 @@ def quantize(x: np.ndarray, fmt: int, rounding: str = "rne", seed: int = 0,
 
     nb = K // blk
     sign = np.signbit(xc)
-    if fmt == NVFP4:
+    kind = FP4_VARIANT[fmt][1] if fmt in FP4_VARIANT else None
+    if kind == "e4m3":
         eS = pow2_tensor_exp(A, NVFP4_RANGE)
         xs = np.ldexp(xc, -eS).astype(np.float32)                     # x'
         a_b = np.max(np.abs(xs.reshape(R, nb, blk)), axis=2)           # fp32
@@ -144,7 +157,7 @@ def quantize(x: np.ndarray, fmt: int, rounding: str = "rne", seed: int = 0,
         r = (xs.reshape(R, nb, blk) * inv[:, :, None]).astype(np.float32)
         scale_val = s_hat                                              # per block
         texp = eS
-    elif fmt == MXFP4:
+    elif kind == "e8m0":
         a_b = np.max(np.abs(xc.reshape(R, nb, blk)), axis=2).astype(np.float64)
         fl = np.frexp(np.where(a_b > 0, a_b, 1.0))[1] - 1              # floor(log2 a_b)
         X = np.where(a_b > 0, fl - 2, -127)
@@ -153,6 +166,17 @@ def quantize(x: np.ndarray, fmt: int, rounding: str = "rne", seed: int = 0,
         live = a_b > 0
         r = np.ldexp(xc.reshape(R, nb, blk), -X[:, :, None]).astype(np.float32)
         scale_val = np.ldexp(1.0, X)
+        texp = 0
+    elif kind == "bf16":
+        a_b = np.max(np.abs(xc.reshape(R, nb, blk)), axis=2)              # fp32
+        t_b = (a_b / np.float32(6.0)).astype(np.float32)                  # fp32 divide
+        s_code = F.bf16_scale_encode(t_b)
+        s_hat = F.bf16_decode(s_code)                                     # exact
+        live = s_hat > 0
+        s32 = np.where(live, s_hat, 1.0).astype(np.float32)
+        inv = (np.float32(1.0) / s32).astype(np.float32)                  # fp32 reciprocal
+        r = (xc.reshape(R, nb, blk) * inv[:, :, None]).astype(np.float32)
+        scale_val = s_hat
         texp = 0
     else:
         raise ValueError(f"unknown format {fmt}")
@@ -165,7 +189,8 @@ def quantize(x: np.ndarray, fmt: int, rounding: str = "rne", seed: int = 0,
     q = F.e2m1_decode(codes)
     xhat = np.ldexp(q * np.repeat(scale_val, blk, axis=1), texp)
     bad = np.repeat(~fin.reshape(R, nb, blk).all(axis=2), blk, axis=1)
-    out.update(codes=codes, packed=F.pack_nibbles(codes), scales=s_code.astype(np.uint8),
+    scales = s_code.astype(np.uint16 if kind == "bf16" else np.uint8)
+    out.update(codes=codes, packed=F.pack_nibbles(codes), scales=scales,
                texp=texp, xhat=xhat, bad_blocks=bad)
     out["stats"] = _stats(x, xhat, A)
     return out
