@@ -84,6 +84,14 @@ extern "C" {
 #define SNIP_FP8_E4M3  1
 #define SNIP_NVFP4     2
 #define SNIP_MXFP4     3
+/* FP4 design-space variants [FP4 All the Way, Outline: block size, scaling
+ * format and rounding were explored]: E2M1 codes with another block size or
+ * scale format than NVFP4 / MX-FP4. Quantizer only (snip_quantize); the
+ * GEMM and layer calls reject them with SNIP_E_FORMAT. */
+#define SNIP_FP4_E4M3_B32  4  /* E4M3 scale per 32, power-of-two tensor scale */
+#define SNIP_FP4_E8M0_B16  5  /* E8M0 scale per 16 (MX rule)                  */
+#define SNIP_FP4_BF16_B16  6  /* BF16 scale per 16: bf16_RNE(blockmax / 6)    */
+#define SNIP_FP4_BF16_B32  7  /* BF16 scale per 32                            */
 
 #define SNIP_RNE       0
 #define SNIP_SR        1
@@ -99,11 +107,14 @@ extern "C" {
  *   codes       device. NVFP4/MXFP4: u8[rows][k/2], element k in the low
  *               nibble when k is even, bit 3 of a nibble = sign.
  *               FP8: u8[rows][k]. BF16: bf16[rows][k].
+ *               The FP4 variants (formats 4..7): as NVFP4.
  *   scales      device. NVFP4: E4M3 u8[rows][k/16]; MXFP4: E8M0 u8[rows][k/32];
- *               NULL for FP8 and BF16.
- *   tensor_exp  device int32: exponent e of the tensor scale 2^e for NVFP4
- *               and FP8 (written by snip_quantize); unused (may be NULL)
- *               for MXFP4 and BF16. */
+ *               FP4_E4M3_B32: E4M3 u8[rows][k/32]; FP4_E8M0_B16: E8M0
+ *               u8[rows][k/16]; FP4_BF16_B16 / _B32: bf16 bits
+ *               u16[rows][k/16] / [k/32]; NULL for FP8 and BF16.
+ *   tensor_exp  device int32: exponent e of the tensor scale 2^e for NVFP4,
+ *               FP8 and FP4_E4M3_B32 (written by snip_quantize); unused (may
+ *               be NULL) for the other formats. */
 typedef struct snip_qtensor {
   int32_t  format;
   int32_t  reserved;
@@ -150,7 +161,9 @@ typedef struct snip_tensor_report {
  *              COLWISE: K = rows, rows % 16 == 0 (MXFP4: % 32 == 0).
  *   layout     SNIP_ROWWISE -> out is [rows][cols]; SNIP_COLWISE -> out is
  *              [cols][rows] (the transpose, blocks along the source rows).
- *   format, rounding  as above (BF16 ignores rounding and copies/transposes).
+ *   format, rounding  as above (BF16 ignores rounding and copies/transposes;
+ *              the FP4 variants need cols (ROWWISE) or rows (COLWISE) to be a
+ *              multiple of their block).
  *   seed, tensor_id   random stream for SNIP_SR (ignored for SNIP_RNE).
  *   amax_in    device float or NULL. NULL: the tensor max is computed from x
  *              (an extra read pass). Non-NULL: used as max|x| (delayed

@@ -35,7 +35,14 @@ BF16, FP8_E4M3, NVFP4, MXFP4 = 0, 1, 2, 3
 FP8 = FP8_E4M3
 RNE, SR = 0, 1
 ROWWISE, COLWISE, BOTHWISE = 0, 1, 2
-FORMAT_NAMES = {BF16: "bf16", FP8_E4M3: "fp8_e4m3", NVFP4: "nvfp4", MXFP4: "mxfp4"}
+# FP4 design-space variants (quantizer only): E2M1 with another block or scale
+FP4_E4M3_B32, FP4_E8M0_B16, FP4_BF16_B16, FP4_BF16_B32 = 4, 5, 6, 7
+FORMAT_NAMES = {BF16: "bf16", FP8_E4M3: "fp8_e4m3", NVFP4: "nvfp4", MXFP4: "mxfp4",
+                FP4_E4M3_B32: "fp4_e4m3_b32", FP4_E8M0_B16: "fp4_e8m0_b16",
+                FP4_BF16_B16: "fp4_bf16_b16", FP4_BF16_B32: "fp4_bf16_b32"}
+# (block, scale kind) of every E2M1 format
+FP4_LAYOUT = {NVFP4: (16, "e4m3"), MXFP4: (32, "e8m0"), FP4_E4M3_B32: (32, "e4m3"),
+              FP4_E8M0_B16: (16, "e8m0"), FP4_BF16_B16: (16, "bf16"), FP4_BF16_B32: (32, "bf16")}
 ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "ALIGN", -4: "FORMAT", -5: "WORKSPACE",
           -6: "HIP", -7: "NONFINITE"}
 

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsnip.so")
-SOURCES = ["api.hip", "quantize.hip", "quantize_dual.hip", "gemm.hip", "gemm_staged.hip"]
+SOURCES = ["api.hip", "quantize.hip", "quantize_dual.hip", "quantize_fp4v.hip", "gemm.hip", "gemm_staged.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -77,25 +77,28 @@ int ok() {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-bool valid_format(int f) { return f >= SNIP_BF16 && f <= SNIP_MXFP4; }
-int block_of(int f) { return f == SNIP_MXFP4 ? 32 : 16; }
-bool has_scales(int f) { return f == SNIP_NVFP4 || f == SNIP_MXFP4; }
-bool has_texp(int f) { return f == SNIP_NVFP4 || f == SNIP_FP8_E4M3; }
+// Formats a qtensor may hold (the FP4 design-space variants included) and
+// the formats the GEMM and layer calls take.
+bool valid_format(int f) { return f >= SNIP_BF16 && f <= SNIP_FP4_BF16_B32; }
+bool gemm_format(int f) { return f >= SNIP_BF16 && f <= SNIP_MXFP4; }
+bool fp4_variant(int f) { return f >= SNIP_FP4_E4M3_B32 && f <= SNIP_FP4_BF16_B32; }
+int block_of(int f) {
+  return (f == SNIP_MXFP4 || f == SNIP_FP4_E4M3_B32 || f == SNIP_FP4_BF16_B32) ? 32 : 16;
+}
+bool has_scales(int f) { return f == SNIP_NVFP4 || f == SNIP_MXFP4 || fp4_variant(f); }
+bool has_texp(int f) { return f == SNIP_NVFP4 || f == SNIP_FP8_E4M3 || f == SNIP_FP4_E4M3_B32; }
 bool needs_amax(int f) { return has_texp(f); }
 
 int64_t code_bytes(int f, int64_t rows, int64_t k) {
-  switch (f) {
-    case SNIP_NVFP4:
-    case SNIP_MXFP4: return rows * k / 2;
-    case SNIP_FP8_E4M3: return rows * k;
-    case SNIP_BF16: return rows * k * 2;
-  }
+  if (f == SNIP_NVFP4 || f == SNIP_MXFP4 || fp4_variant(f)) return rows * k / 2;
+  if (f == SNIP_FP8_E4M3) return rows * k;
+  if (f == SNIP_BF16) return rows * k * 2;
   return -1;
 }
 int64_t scale_bytes(int f, int64_t rows, int64_t k) {
-  if (f == SNIP_NVFP4) return rows * k / 16;
-  if (f == SNIP_MXFP4) return rows * k / 32;
-  return 0;
+  if (!has_scales(f)) return 0;
+  const int per = (f == SNIP_FP4_BF16_B16 || f == SNIP_FP4_BF16_B32) ? 2 : 1;
+  return rows * (k / block_of(f)) * per;
 }
 
 constexpr size_t kAlign = 256;
@@ -132,6 +135,8 @@ int quant_wg(int layout, int f, int64_t rows, int64_t cols) {
   int64_t wg;
   if (f == SNIP_BF16) {
     wg = layout == SNIP_ROWWISE ? ceil_div(rows * cols / 8, 256 * 2) : ceil_div(rows, 64) * ceil_div(cols, 64);
+  } else if (fp4_variant(f)) {
+    wg = ceil_div(rows * cols / block_of(f), 256);                  // one thread per block
   } else if (layout == SNIP_ROWWISE) {
     wg = ceil_div(rows * cols / (f == SNIP_MXFP4 ? 32 : 16), 512);     // two items per thread
   } else {
@@ -210,6 +215,8 @@ int run_quant_group(const QPlan* const* ps, int n, hipStream_t s) {
   hipError_t e;
   if (p.format == SNIP_BF16) {
     e = p.layout == SNIP_ROWWISE ? launch_bf16_copy(jobs, wg, s) : launch_bf16_transpose(jobs, wg, s);
+  } else if (fp4_variant(p.format)) {
+    e = launch_quant_fp4v(p.format, p.layout, p.sr, jobs, wg, s);
   } else if (p.layout == SNIP_ROWWISE) {
     e = launch_quant_row(p.format, p.sr, jobs, wg, s);
   } else {
@@ -447,18 +454,18 @@ size_t snip_quantize_workspace(int64_t rows, int64_t cols, int layout, int forma
 }
 
 size_t snip_qgemm_workspace(int64_t M, int64_t N, int64_t K, int format) {
-  if (M <= 0 || N <= 0 || K <= 0 || !valid_format(format)) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || !gemm_format(format)) return 0;
   return gemm_partial_bytes(format, M, N, K);
 }
 
 size_t snip_linear_fwd_workspace(int64_t T, int64_t in, int64_t out, int format) {
-  if (T <= 0 || in <= 0 || out <= 0 || !valid_format(format)) return 0;
+  if (T <= 0 || in <= 0 || out <= 0 || !gemm_format(format)) return 0;
   return 2 * kQuantWS + qtensor_ws_bytes(format, T, in) + qtensor_ws_bytes(format, out, in) +
          align_up(gemm_partial_bytes(format, T, out, in), kAlign);
 }
 
 size_t snip_linear_bwd_workspace(int64_t T, int64_t in, int64_t out, int fmt_dgrad, int fmt_wgrad) {
-  if (T <= 0 || in <= 0 || out <= 0 || !valid_format(fmt_dgrad) || !valid_format(fmt_wgrad)) return 0;
+  if (T <= 0 || in <= 0 || out <= 0 || !gemm_format(fmt_dgrad) || !gemm_format(fmt_wgrad)) return 0;
   const size_t split = std::max(gemm_partial_bytes(fmt_dgrad, T, in, out),
                                 gemm_partial_bytes(fmt_wgrad, out, in, T));
   return 3 * kAmaxBytes + 4 * kPartBytes + qtensor_ws_bytes(fmt_dgrad, T, out) +
@@ -563,6 +570,8 @@ int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t l
   if (!c) return fail(SNIP_E_NULL, "snip_qgemm: c is NULL");
   if (a->format != b->format)
     return fail(SNIP_E_FORMAT, "snip_qgemm: operand formats differ (%d, %d)", a->format, b->format);
+  if (!gemm_format(a->format))
+    return fail(SNIP_E_FORMAT, "snip_qgemm: format %d is a quantizer-only FP4 variant", a->format);
   if (a->k != b->k) return fail(SNIP_E_SHAPE, "snip_qgemm: K differs (%lld, %lld)", (long long)a->k,
                                 (long long)b->k);
   if (a->k % 128) return fail(SNIP_E_SHAPE, "snip_qgemm: K=%lld not a multiple of 128", (long long)a->k);
@@ -642,7 +651,7 @@ int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t
                     uint64_t seed, uint32_t layer_id, float* y, snip_stats* stats2, void* ws,
                     size_t ws_bytes, void* stream) {
   if (!x || !w || !y) return fail(SNIP_E_NULL, "snip_linear_fwd: x, w and y must be non-NULL");
-  if (!valid_format(format)) return fail(SNIP_E_FORMAT, "snip_linear_fwd: unknown format %d", format);
+  if (!gemm_format(format)) return fail(SNIP_E_FORMAT, "snip_linear_fwd: format %d is not a GEMM format", format);
   if (T <= 0 || in <= 0 || out <= 0) return fail(SNIP_E_SHAPE, "snip_linear_fwd: dimensions must be > 0");
   if (in % 128) return fail(SNIP_E_SHAPE, "snip_linear_fwd: in=%lld not a multiple of 128", (long long)in);
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(stats2, 8) || !aligned(ws, 16))
@@ -719,8 +728,8 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int
                     const snip_stats* fwd_stats2, float* dx, float* dw, snip_stats* stats4, void* ws,
                     size_t ws_bytes, void* stream) {
   if (!dy || !x || !w) return fail(SNIP_E_NULL, "snip_linear_bwd: dy, x and w must be non-NULL");
-  if (!valid_format(fmt_dgrad) || !valid_format(fmt_wgrad))
-    return fail(SNIP_E_FORMAT, "snip_linear_bwd: unknown format (%d, %d)", fmt_dgrad, fmt_wgrad);
+  if (!gemm_format(fmt_dgrad) || !gemm_format(fmt_wgrad))
+    return fail(SNIP_E_FORMAT, "snip_linear_bwd: formats (%d, %d) must be GEMM formats", fmt_dgrad, fmt_wgrad);
   if (T <= 0 || in <= 0 || out <= 0) return fail(SNIP_E_SHAPE, "snip_linear_bwd: dimensions must be > 0");
   if (dx) {
     if (out % 128) return fail(SNIP_E_SHAPE, "snip_linear_bwd: out=%lld not a multiple of 128 (dgrad K)", (long long)out);

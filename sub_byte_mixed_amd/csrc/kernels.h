@@ -127,6 +127,7 @@ hipError_t launch_quant_row(int format, bool sr, const QJobs& jobs, int total_wg
 hipError_t launch_quant_col(int format, bool sr, const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_quant_dual(int format, bool sr_row, bool sr_col, const DJobs& jobs, int total_wg,
                              hipStream_t s);
+hipError_t launch_quant_fp4v(int format, int layout, bool sr, const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_bf16_copy(const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_bf16_transpose(const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_finalize(const FJobs& jobs, hipStream_t s);

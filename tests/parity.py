@@ -46,10 +46,11 @@ def gpu_codes(q: S.QuantizedTensor) -> dict:
     R, K = q.rows, q.k
     out = {"texp": int(q.texp.cpu().item())}
     c = q.codes.cpu().numpy()
-    if q.format in (S.NVFP4, S.MXFP4):
+    if q.format in S.FP4_LAYOUT:
         out["packed"] = c.reshape(R, K // 2)
-        blk = 16 if q.format == S.NVFP4 else 32
-        out["scales"] = q.scales.cpu().numpy().reshape(R, K // blk)
+        blk, kind = S.FP4_LAYOUT[q.format]
+        sc = q.scales.cpu().numpy()
+        out["scales"] = (sc.view(np.uint16) if kind == "bf16" else sc).reshape(R, K // blk)
     elif q.format == S.FP8:
         out["codes"] = c.reshape(R, K)
     else:
@@ -62,10 +63,10 @@ def compare_codes(g: dict, o: dict, fmt: int, rows=None, what=""):
     given output rows of the GPU result). Blocks holding non-finite inputs
     are excluded (their codes are unspecified)."""
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
-    if fmt in (S.NVFP4, S.FP8):
+    if fmt in (S.NVFP4, S.FP8, S.FP4_E4M3_B32):
         assert g["texp"] == o["texp"], f"{what}: tensor exponent {g['texp']} != {o['texp']}"
     bad = o.get("bad_blocks")
-    if fmt in (S.NVFP4, S.MXFP4):
+    if fmt in S.FP4_LAYOUT:
         gp = sel(g["packed"])
         op = o["packed"]
         if bad is not None and bad.any():
@@ -73,7 +74,7 @@ def compare_codes(g: dict, o: dict, fmt: int, rows=None, what=""):
             gp, op = gp[keep], op[keep]
         mism = np.argwhere(gp != op)
         assert mism.size == 0, f"{what}: {len(mism)} code bytes differ, first at {mism[:4].tolist()}"
-        blk = 16 if fmt == S.NVFP4 else 32
+        blk = S.FP4_LAYOUT[fmt][0]
         gs, os_ = sel(g["scales"]), o["scales"]
         if bad is not None and bad.any():
             keepb = ~bad[:, ::blk]

@@ -84,7 +84,7 @@ def quant(L, x=P, rows=64, cols=64, ld=64, layout=0, fmt=S.NVFP4, rnd=0, out=Non
 
 def test_quantize_validation(L):
     assert quant(L, x=None) == -1 and "x is NULL" in err(L)
-    assert quant(L, fmt=7) == -4
+    assert quant(L, fmt=9) == -4
     assert quant(L, rnd=3) == -4
     assert quant(L, layout=2) == -4
     assert quant(L, cols=40, ld=40) == -2                       # cols % 16
@@ -197,6 +197,24 @@ def test_saved_linear_validation(L):
     assert bwd(dx=dx + 4) == -3
     assert bwd(ws_bytes=64) == -5
     assert L.snip_linear_bwd_saved_workspace(T, din, dout, S.BF16) == 0
+
+
+def test_fp4_variant_sizes_and_rejections(L):
+    assert L.snip_qtensor_bytes(S.FP4_E4M3_B32, 4, 64, 0) == 128
+    assert L.snip_qtensor_bytes(S.FP4_E4M3_B32, 4, 64, 1) == 8
+    assert L.snip_qtensor_bytes(S.FP4_E8M0_B16, 4, 64, 1) == 16
+    assert L.snip_qtensor_bytes(S.FP4_BF16_B16, 4, 64, 1) == 32     # 2-byte scales
+    assert L.snip_qtensor_bytes(S.FP4_BF16_B32, 4, 64, 1) == 16
+    assert L.snip_qtensor_bytes(S.FP4_BF16_B32, 4, 48, 0) == -1     # k % 32
+    assert L.snip_qtensor_bytes(8, 4, 64, 0) == -1
+    assert quant(L, fmt=S.FP4_E4M3_B32, cols=48, ld=48) == -2        # K % 32
+    assert quant(L, fmt=S.FP4_BF16_B16, layout=1, rows=40) == -2     # K = rows % 16
+    a, b = qdesc(S.FP4_BF16_B16, 64, 256), qdesc(S.FP4_BF16_B16, 32, 256)
+    assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(b), P + 0x800000, 32, None, 0, None) == -4
+    assert "quantizer-only" in err(L)
+    ws, y = P + 0x1000000, P + 0x2000000
+    assert L.snip_linear_fwd(P, P2, 64, 128, 64, S.FP4_E8M0_B16, 0, 0, y, None, ws, 1 << 30, None) == -4
+    assert L.snip_qgemm_workspace(64, 64, 128, S.FP4_E4M3_B32) == 0
 
 
 def test_layer_stats_validation(L):
