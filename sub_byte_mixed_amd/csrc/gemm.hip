@@ -318,8 +318,16 @@ __global__ __launch_bounds__(NT, BM * BN > 256 * 128 ? 1 : 2) void gemm_kernel(G
     Frags f[UK];
 #pragma unroll
     for (int u = 0; u < UK; ++u) load(f[u], it % S, u);
+    // FP8: the wave runs its stage's MFMAs at raised issue priority, so that
+    // with two or three waves per SIMD the one multiplying keeps the matrix
+    // pipe while the others read and decode. Measured on MI355X: 3-15 %
+    // faster for back-to-back GEMMs of 2048-16384 rows (most on the largest),
+    // neutral inside the layer step; neutral to slightly slower for NVFP4,
+    // so not used there.
+    if constexpr (FMT == SNIP_FP8_E4M3) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < UK; ++u) run_stage(f[u]);
+    if constexpr (FMT == SNIP_FP8_E4M3) __builtin_amdgcn_s_setprio(0);
   }
 
   store_tile<TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, r16, grp);
