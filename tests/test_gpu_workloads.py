@@ -1,6 +1,8 @@
-"""GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (snip_linear_fwd, then snip_linear_bwd reusing the forward
-statistics), on sampled outputs the oracle can compute one by one:
+"""GPU parity at the workloads' full sizes, in both launch configurations:
+the saved-operand calls the benchmark times by default (snip_linear_fwd_save,
+snip_linear_bwd_saved) and the separate calls (snip_linear_fwd, then
+snip_linear_bwd reusing the forward statistics), on sampled outputs the
+oracle can compute one by one:
 
   * Y, dX, dW: a seeded sample of output rows x columns against the oracle's
     fp64 product of the oracle-quantized rows / columns involved (quantized
@@ -45,14 +47,22 @@ def oracle_cols(t32, amax, fmt, rnd, seed, tid, cols):
     return OQ.quantize_colwise(t32, fmt, RND[rnd], seed, tid, amax=amax, col_ids=cols)
 
 
-def run_layer(wl, li, fmt, seed=0, full_stats=False, n_rows=8, n_cols=48):
+def run_layer(wl, li, fmt, seed=0, full_stats=False, n_rows=8, n_cols=48, fused=False):
+    """fused: the saved-operand calls the benchmark times by default
+    (snip_linear_fwd_save, snip_linear_bwd_saved: X, W, dY read once)."""
     layer = wl.layers[li]
     T, din, dout = wl.tokens, layer.d_in, layer.d_out
-    say(f"workload {wl.name} layer {layer.name} ({din}->{dout}, T={T}) fmt={fmt} seed={seed}")
+    say(f"workload {wl.name} layer {layer.name} ({din}->{dout}, T={T}) fmt={fmt} seed={seed} fused={fused}")
     x, w, dy = synth.gen_layer(wl, li)
     xd, wd, dyd = x.cuda(), w.cuda(), dy.cuda()
-    y, st_f = S.linear_fwd(xd, wd, fmt, seed, li)
-    dx, dw, st_b = S.linear_bwd(dyd, xd, wd, fmt, fmt, seed, li, fwd_stats=st_f)
+    saved = None
+    if fused:
+        y, saved, st_f4 = S.linear_fwd_save(xd, wd, fmt, seed, li)
+        dx, dw, st_b2 = S.linear_bwd_saved(dyd, saved, seed, li)
+        st_f, st_b = st_f4, st_b2
+    else:
+        y, st_f = S.linear_fwd(xd, wd, fmt, seed, li)
+        dx, dw, st_b = S.linear_bwd(dyd, xd, wd, fmt, fmt, seed, li, fwd_stats=st_f)
     torch.cuda.synchronize()
     x32, w32, dy32 = (synth.bf16_to_f32(t) for t in (x, w, dy))
     ax, aw, ady = (OQ.tensor_amax(t) for t in (x32, w32, dy32))
@@ -78,7 +88,10 @@ def run_layer(wl, li, fmt, seed=0, full_stats=False, n_rows=8, n_cols=48):
                what=f"{wl.name}/{layer.name} dW")
 
     # codes of every operand on the sampled rows (bf16 has none)
-    if fmt != S.BF16:
+    if saved is not None:                   # the saved backward operands themselves
+        compare_codes(gpu_codes(saved.wt), qwt, fmt, rows=rin, what=f"{wl.name}/{layer.name} saved W^T")
+        compare_codes(gpu_codes(saved.xt), qxt, fmt, rows=rin, what=f"{wl.name}/{layer.name} saved X^T")
+    if fmt != S.BF16 and saved is None:
         for src, lay, rnd, role, rows, o in ((xd, S.ROWWISE, S.RNE, 0, rT, qx), (wd, S.ROWWISE, S.RNE, 1, rout, qw),
                                             (dyd, S.ROWWISE, S.SR, 2, rT, qdy), (wd, S.COLWISE, S.SR, 3, rin, qwt),
                                             (dyd, S.COLWISE, S.SR, 4, rout, qdyt), (xd, S.COLWISE, S.SR, 5, rin, qxt)):
@@ -92,13 +105,13 @@ def run_layer(wl, li, fmt, seed=0, full_stats=False, n_rows=8, n_cols=48):
     tensors = {"X": (x32, ax), "W": (w32, aw), "dY": (dy32, ady)}
     sums = {n: float(np.einsum("ij,ij->", t.astype(np.float64), t.astype(np.float64)))
             for n, (t, _) in tensors.items()}
-    names_f, names_b = ["X", "W"], ["dY", "W", "dY", "X"]
+    names_f, names_b = (["X", "W", "W", "X"], ["dY", "dY"]) if fused else (["X", "W"], ["dY", "W", "dY", "X"])
     for g, n in list(zip(gf, names_f)) + list(zip(gb, names_b)):
         assert g["amax"] == float(tensors[n][1]), f"{n} amax"
         sx2 = sums[n]
         assert abs(g["sum_x2"] - sx2) <= TOL * sx2, f"{n} sum_x2 {g['sum_x2']} vs {sx2}"
         assert g["n_nonfinite"] == 0
-    if full_stats:
+    if full_stats and not fused:
         ref = [OQ.quantize(x32, fmt, "rne", seed, tid(0))["stats"],
                OQ.quantize(w32, fmt, "rne", seed, tid(1))["stats"]]
         for g, o, n in zip(gf, ref, names_f):
@@ -109,7 +122,7 @@ def run_layer(wl, li, fmt, seed=0, full_stats=False, n_rows=8, n_cols=48):
                OQ.quantize_colwise(x32, fmt, "sr", seed, tid(5))["stats"]]
         for g, o, n in zip(gb, ref, ["dY", "W^T", "dY^T", "X^T"]):
             compare_stats(g, o, what=f"{wl.name}/{layer.name} bwd {n}")
-    del xd, wd, dyd, y, dx, dw
+    del xd, wd, dyd, y, dx, dw, saved
     torch.cuda.empty_cache()
 
 
@@ -142,3 +155,23 @@ def test_llama70b_block(name):
 def test_down7b_precision_sweep(fmt):
     wl = synth.WORKLOADS["down7b_sweep"]
     run_layer(wl, 0, fmt, seed=fmt)
+
+
+@pytest.mark.parametrize("li", range(7))
+def test_tinyllama1b_block_fused(li):
+    """The benchmark's launch configuration: saved-operand calls."""
+    wl = synth.WORKLOADS["tinyllama1b"]
+    run_layer(wl, li, wl.plan[li], fused=True)
+
+
+@pytest.mark.parametrize("name", ["V", "Down"])
+def test_llama7b_block_fused(name):
+    wl = synth.WORKLOADS["llama7b"]
+    li = [l.name for l in wl.layers].index(name)
+    run_layer(wl, li, wl.plan[li], fused=True)
+
+
+def test_llama70b_block_fused():
+    wl = synth.WORKLOADS["llama70b"]
+    li = [l.name for l in wl.layers].index("K")
+    run_layer(wl, li, wl.plan[li], fused=True)
