@@ -49,8 +49,9 @@
 // longer read.
 //
 // Tiling: a workgroup of 256 threads (2x2 waves) owns a BM x BN output tile:
-// 256x256 (one workgroup per CU), 256x128 (FP8 and NVFP4, two per CU) or
-// 128x128 (two per CU), as plan_gemm decides from the problem's tile rounds. Tile order: the hardware hands workgroups to the 8 XCDs
+// 256x256 (one workgroup per CU), 256x128 (FP8 and NVFP4, two per CU),
+// 128x128 (two per CU) or, for skinny FP8 / NVFP4 problems, 64x64, as
+// plan_gemm decides from the problem's tile rounds. Tile order: the hardware hands workgroups to the 8 XCDs
 // round-robin; tile ids are remapped so each XCD works on a contiguous range,
 // and tiles are ordered in groups of 8 tile-rows so that concurrently running
 // tiles share A and B panels in that XCD's L2. Skinny problems split K across
@@ -400,6 +401,14 @@ GemmPlan plan_gemm(int format, int64_t M, int64_t N, int64_t K) {
   p.tiles = t128;
   p.staged = (format == SNIP_MXFP4 || format == SNIP_BF16) ? 1 : 0;
   int64_t split = p.tiles >= 192 ? 1 : 256 / p.tiles;
+  if (t128 < 192 && (format == SNIP_FP8_E4M3 || format == SNIP_NVFP4)) {
+    // skinny problems: 64x64 tiles, unsplit when they fill the chip, else
+    // split K over about 512 workgroups (measured on the K/V projections:
+    // 4096x256x2048 22 -> 14 us, 256x2048x4096 16 -> 13 us)
+    p.bm = p.bn = 64;
+    p.tiles = ceil_div(M, 64) * ceil_div(N, 64);
+    split = p.tiles >= 192 ? 1 : ceil_div(512, p.tiles);
+  }
   // split in whole stages (the staged MX kernel then runs 128-element
   // stages), at least 4 per split
   const int64_t gran = p.staged ? (format == SNIP_MXFP4 ? 128 : 64) : unit_k(format);
@@ -430,6 +439,12 @@ static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   if constexpr (FMT == SNIP_NVFP4) {
     if (p.bm == 256 && p.bn == 128) {     // 2-stage ring: 54 KiB, two per CU
       hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 2, 1>), grid, dim3(NT), 0, s, g);
+      return;
+    }
+  }
+  if constexpr (FMT == SNIP_FP8_E4M3 || FMT == SNIP_NVFP4) {
+    if (p.bm == 64) {                     // skinny problems: 4-stage ring of 8 KiB stages
+      hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 1>), grid, dim3(NT), 0, s, g);
       return;
     }
   }

@@ -85,6 +85,8 @@ PLAN_CASES = [
     (S.BF16, 2000, 1600, 384),      # staged 128x128
     (S.NVFP4, 2000, 1600, 640),     # LDS-DMA 128x128
     (S.FP8, 2000, 1600, 640),       # LDS-DMA 128x128
+    (S.FP8, 4000, 240, 1024),       # 64x64, unsplit
+    (S.NVFP4, 240, 2000, 2048),     # 64x64, K split 4 ways
 ]
 
 
@@ -98,6 +100,7 @@ def test_gemm_each_plan_ragged(fmt, M, N, K):
     c = S.qgemm(upload_oracle_q(oa, fmt), upload_oracle_q(ob, fmt))
     torch.cuda.synchronize()
     rng = np.random.default_rng(K)
-    rows = np.unique(np.concatenate([rng.choice(M, 96, replace=False), [0, 255, 256, M - 1]]))
+    edge = [r for r in (0, 255, 256, M - 1) if r < M]     # tile edges that exist at this M
+    rows = np.unique(np.concatenate([rng.choice(M, min(M, 96), replace=False), edge]))
     check_gemm(c[rows].cpu().numpy().astype(np.float64), oa["xhat"][rows], ob["xhat"],
                what=f"fmt={fmt} {M}x{N}x{K}")
