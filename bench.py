@@ -174,10 +174,13 @@ def main():
             else:
                 key = f"quantize {fname} {'row' if r['layout'] == 0 else 'col'} {rn[r['rounding']]}"
                 nb = r["work"] * QBYTES[r["format"]]
-            c = by_class.setdefault(key, {"ms": 0.0, "bytes": 0.0, "launches": 0})
+            c = by_class.setdefault(key, {"ms": 0.0, "bytes": 0.0, "launches": 0, "elems": 0.0,
+                                          "dual": (fname, rn[r["rounding"] & 1].upper(), rn[r["rounding"] >> 1].upper())
+                                          if r["kind"] == "quantize" and r["layout"] == S.BOTHWISE else None})
             c["ms"] += r["ms"]
             c["bytes"] += nb
             c["launches"] += 1
+            c["elems"] += r["work"]
         if r["kind"] == "gemm":
             g = gemm_by_fmt.setdefault(r["format"], {"ms": 0.0, "flops": 0.0, "launches": 0})
             g["ms"] += r["ms"]
@@ -222,6 +225,21 @@ def main():
                                        "launches_per_step": g["launches"] // args.steps}
                    for f, g in gemm_by_fmt.items()}
     quant_gbs = quant["bytes"] / (quant["ms"] * 1e-3) / 1e9
+    # The fused quantizers' ALU roofline: VALU lane-operations per element
+    # (rocprofv3 SQ_INSTS_VALU, recorded with a hash of the quantizer
+    # sources) times the elements each launch quantized, over the launches'
+    # measured time, against the chip's full-rate VALU issue rate.
+    valu = profiling.load_valu(wl.name)
+    alu = None
+    duals = [c for c in by_class.values() if c["dual"]]
+    if valu and duals and all(c["dual"] in valu for c in duals):
+        ops = sum(c["elems"] * valu[c["dual"]] for c in duals)
+        ms = sum(c["ms"] for c in duals)
+        achieved_ops = ops / (ms * 1e-3) / 1e12
+        alu = {"bound": "alu", "kernel": "quant_dual_kernel (all formats and roundings of the step)",
+               "achieved": round(achieved_ops, 2), "peak": round(profiling.VALU_LANE_OPS / 1e12, 2),
+               "unit": "T VALU lane-ops/s", "frac": round(achieved_ops * 1e12 / profiling.VALU_LANE_OPS, 4),
+               "ops_per_element": {" ".join(k): v for k, v in valu.items()}}
 
     # ------------------------------------------------------- CPU baseline
     cpu = None
@@ -240,7 +258,7 @@ def main():
         "gemm": gemm_detail,
         "quantize": {"gbs": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / PEAK["hbm_gbs"], 4),
                      "ms_per_step": round(quant["ms"] / args.steps, 4),
-                     "launches_per_step": quant["launches"] // args.steps},
+                     "launches_per_step": quant["launches"] // args.steps, "alu_roofline": alu},
         "other_kernels_ms_per_step": {k: round(v / args.steps, 4) for k, v in other_ms.items()},
         "memory_kernels": {k: {"ms_per_step": round(c["ms"] / args.steps, 4),
                                "launches_per_step": c["launches"] // args.steps,

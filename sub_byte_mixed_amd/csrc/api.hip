@@ -127,7 +127,7 @@ struct Carver {
 // Grid sizes.
 int amax_wg(int64_t rows, int64_t cols) {
   const int64_t chunks = rows * cols / 8;
-  int64_t wg = ceil_div(chunks, 256 * kAmaxUnroll);
+  int64_t wg = ceil_div(chunks, kAmaxThreads * kAmaxUnroll);
   if (wg < 1) wg = 1;
   return (int)(wg > kAmaxWG ? kAmaxWG : wg);
 }

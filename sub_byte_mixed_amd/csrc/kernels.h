@@ -12,6 +12,7 @@ namespace snip {
 constexpr int kMaxJobs = 4;       // tensors per multi-tensor launch
 constexpr int kAmaxWG = 512;      // max workgroups of one amax pass (per tensor)
 constexpr int kAmaxUnroll = 8;    // 16-byte loads in flight per amax thread
+constexpr int kAmaxThreads = 256;  // threads per amax workgroup
 constexpr int kQuantWG = 2048;    // max workgroups of one quantize pass (per tensor)
 
 // One workgroup's partial statistics (already in the unscaled domain).

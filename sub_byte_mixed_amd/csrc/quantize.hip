@@ -32,7 +32,7 @@ __device__ __forceinline__ uint32_t pair_max(uint32_t w, uint32_t m) {
 }
 
 // ------------------------------------------------------------ amax pass
-__global__ __launch_bounds__(256) void amax_kernel(AJobs jobs) {
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(AJobs jobs) {
   int32_t wg0[kMaxJobs];
   for (int i = 0; i < kMaxJobs; ++i) wg0[i] = jobs.j[i].wg0;
   const int jn = find_job(wg0, jobs.n);
@@ -43,12 +43,12 @@ __global__ __launch_bounds__(256) void amax_kernel(AJobs jobs) {
   const bool flat = J.ld == J.cols;
   uint32_t m = 0;
   // kAmaxUnroll independent 16-byte loads per thread in flight
-  for (int64_t c0 = (int64_t)wg * 256 * kAmaxUnroll + threadIdx.x; c0 < nchunk;
-       c0 += (int64_t)J.nwg * 256 * kAmaxUnroll) {
+  for (int64_t c0 = (int64_t)wg * kAmaxThreads * kAmaxUnroll + threadIdx.x; c0 < nchunk;
+       c0 += (int64_t)J.nwg * kAmaxThreads * kAmaxUnroll) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
-      const int64_t c = c0 + u * 256;
+      const int64_t c = c0 + u * kAmaxThreads;
       const int64_t off = flat ? c * 8 : (c / cpr) * J.ld + (c % cpr) * 8;
       v[u] = c < nchunk ? *reinterpret_cast<const uint4*>(J.x + off) : make_uint4(0u, 0u, 0u, 0u);
     }
@@ -61,12 +61,13 @@ __global__ __launch_bounds__(256) void amax_kernel(AJobs jobs) {
     }
   }
   m = wave_max_u(m);
-  __shared__ uint32_t red[4];
+  constexpr int NW = kAmaxThreads / 64;
+  __shared__ uint32_t red[NW];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
-    for (int w = 1; w < 4; ++w) r = red[w] > r ? red[w] : r;
+    for (int w = 1; w < NW; ++w) r = red[w] > r ? red[w] : r;
     J.part[wg] = r;
   }
 }
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(FJobs jobs) { finalize_on
 
 // ------------------------------------------------------------ launchers
 hipError_t launch_amax(const AJobs& jobs, int total_wg, hipStream_t s) {
-  hipLaunchKernelGGL(amax_kernel, dim3(total_wg), dim3(256), 0, s, jobs);
+  hipLaunchKernelGGL(amax_kernel, dim3(total_wg), dim3(kAmaxThreads), 0, s, jobs);
   return hipGetLastError();
 }
 

@@ -195,6 +195,41 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(DJobs jobs) {
   __shared__ uint8_t lsc[TC * NB];
   __shared__ __align__(16) uint32_t lrow[4][BLK * 64];         // wave-private row staging
 
+  const int64_t R = J.rows, C = J.cols;
+  const int64_t rowbytes = R / BLK * CB;                        // column-wise output row (codes)
+  const int64_t tiles_c = ceil_div(C, TC);
+  const int64_t ntiles = ceil_div(R, TR) * tiles_c;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // a tile's block rows of this wave: lane l holds columns 2l, 2l+1 (dword loads)
+  uint32_t w[NBT][BLK];
+  auto load_tile = [&](int64_t tile) {
+    const int64_t r0 = (tile / tiles_c) * TR;
+    const int64_t c0 = (tile % tiles_c) * TC;
+    const int nbt = (int)((R - r0) / BLK < NB ? (R - r0) / BLK : NB);
+    const int64_t col = c0 + 2 * lane;
+    const bool lane_ok = col < C;
+    // Lanes past the last column read column 0 of the same rows (in bounds)
+    // and drop it, so all loads issue without branches. ld is a multiple of
+    // 8, so a row is a whole number of dwords.
+    const int64_t pitch = J.ld >> 1;
+    const uint32_t* base = reinterpret_cast<const uint32_t*>(J.x + r0 * J.ld + (lane_ok ? col : 0));
+#pragma unroll
+    for (int t = 0; t < NBT; ++t) {
+      const int rb = wave + 4 * t;
+      if (rb < nbt) {
+        const uint32_t* src = base + (int64_t)rb * BLK * pitch;
+        uint32_t v[BLK];
+#pragma unroll
+        for (int i = 0; i < BLK; ++i) v[i] = src[i * pitch];
+#pragma unroll
+        for (int i = 0; i < BLK; ++i) w[t][i] = lane_ok ? v[i] : 0u;
+      }
+    }
+  };
+  // The first tile's loads need no tensor scale: issue them before the
+  // tensor max is reduced from the amax partials, so the two reads overlap.
+  if (wg < ntiles) load_tile(wg);
+
   const float A = (FMT == SNIP_MXFP4) ? 0.0f : wg_tensor_amax(J.amax_in, J.amax_part, J.n_amax_part, ured);
   const int eS = tensor_exp(A, FMT);
   if (wg == 0 && threadIdx.x == 0) {
@@ -204,11 +239,6 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(DJobs jobs) {
   __shared__ float inv_lut[FMT == SNIP_NVFP4 ? 128 : 1];
   if constexpr (FMT == SNIP_NVFP4) fill_inv_lut(inv_lut);
 
-  const int64_t R = J.rows, C = J.cols;
-  const int64_t rowbytes = R / BLK * CB;                        // column-wise output row (codes)
-  const int64_t tiles_c = ceil_div(C, TC);
-  const int64_t ntiles = ceil_div(R, TR) * tiles_c;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double e2s = 0.0, x2s = 0.0, e2r = 0.0, x2r = 0.0;           // column-wise statistics
   uint32_t nf = 0u, amax_bits = 0u;
   RowStats rs;
@@ -220,17 +250,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(DJobs jobs) {
     const int nbt = (int)((R - r0) / BLK < NB ? (R - r0) / BLK : NB);
     const int64_t col = c0 + 2 * lane;
     const bool lane_ok = col < C;
-    uint32_t w[NBT][BLK];
-#pragma unroll
-    for (int t = 0; t < NBT; ++t) {
-      const int rb = wave + 4 * t;
-      if (rb < nbt) {
-        const uint16_t* src = J.x + (r0 + (int64_t)rb * BLK) * J.ld + col;
-#pragma unroll
-        for (int i = 0; i < BLK; ++i)
-          w[t][i] = lane_ok ? *reinterpret_cast<const uint32_t*>(src + (int64_t)i * J.ld) : 0u;
-      }
-    }
+    if (tile != wg) load_tile(tile);
     static_for<NBT>([&](auto tc) {
       constexpr int t = decltype(tc)::value;
       const int rb = wave + 4 * t;                              // wave-uniform

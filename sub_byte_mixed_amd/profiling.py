@@ -14,6 +14,25 @@ except for the `copy` calibration run).
       dispatch), each scaled by the factor that makes the calibration copy
       read and write exactly its known size. The summary records a hash of
       the kernel sources, so a later change of the kernel invalidates it.
+  python -m sub_byte_mixed_amd.profiling kernels --fetch F.csv --write W.csv
+         --copy-fetch CF.csv --copy-write CW.csv --stats STATS_CSV
+         --workload NAME --out OUT_MD --cmd "..."
+      the same copy-calibrated HBM bytes for every kernel of the library,
+      divided by the kernel's average duration from a kernel-trace run of
+      the same command: each kernel's achieved HBM GB/s.
+  python -m sub_byte_mixed_amd.profiling mfma --pmc P.csv --stats STATS_CSV
+         --workload NAME --steps N --out OUT_MD --cmd "..."
+      MFMA utilisation of the GEMM kernels from one --pmc run (MfmaUtil =
+      MFMA-busy cycles over active cycles of all SIMDs; MFMA flops from the
+      SQ_INSTS_VALU_MFMA_MOPS_* counters, 512 flops each), and the counted
+      MFMA flops against the workload's 2*M*N*K over the N steps the run made.
+  python -m sub_byte_mixed_amd.profiling valu --pmc P.csv --stats STATS_CSV
+         --workload NAME --steps N --out OUT_MD --cmd "..."
+      VALU work of the fused quantize kernels from one --pmc run: VALU
+      lane-operations per element (SQ_INSTS_VALU x 64 over the elements the
+      kernel quantized in the run's N steps), the element rate the chip's
+      VALU issue rate allows at that count (256 CUs x 4 SIMDs x 16 lanes x
+      2.4 GHz = 39.3e12 lane-operations/s), and the rate reached.
   python -m sub_byte_mixed_amd.profiling vendor --workload NAME --out OUT_MD
       times the vendor library's fp16 and bf16 GEMM (torch.mm, hipBLASLt) on
       the workload's forward, dgrad and wgrad shapes: a reference point for
@@ -32,6 +51,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/gemm_common.h", "csrc/device.h", "csrc/kernels.h")
+QUANT_SOURCES = ("csrc/quantize_dual.hip", "csrc/quant_common.h", "csrc/stats_common.h", "csrc/device.h",
+                 "csrc/kernels.h")
 TRAFFIC_TAG = "traffic-json:"
 
 
@@ -61,6 +82,22 @@ def load_traffic(workload: str, kernel_prefix: str):
     return None
 
 
+def load_valu(workload: str):
+    """{(format name, row rounding, column rounding): VALU lane-ops per
+    element} of the fused quantize kernels recorded for this workload, or
+    None when absent or taken on other quantizer sources."""
+    path = os.path.join(ROOT, "profiles", f"quantize_valu_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("valu-json:"):
+            d = json.loads(line[len("valu-json:"):])
+            if d.get("source_hash") != source_hash(QUANT_SOURCES):
+                return None
+            return {tuple(k["kernel"].split(", ")): k["ops_per_elem"] for k in d["kernels"]}
+    return None
+
+
 def _counter_rows(path):
     with open(path) as fh:
         return list(csv.DictReader(fh))
@@ -80,6 +117,187 @@ def _per_dispatch(path, counter, prefix=None, contains=None):
             continue
         out[r["Dispatch_Id"]] = out.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     return out
+
+
+def _per_kernel(path, counter):
+    """{kernel name: {dispatch id: value}} of one counter."""
+    out = {}
+    for r in _counter_rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        d = out.setdefault(r["Kernel_Name"].strip(), {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _stats_by_name(path):
+    """{kernel name: (calls, average ns)} from a --stats kernel summary."""
+    return {r["Name"].strip(): (int(r["Calls"]), float(r["AverageNs"])) for r in _counter_rows(path)}
+
+
+def _short(name, n=90):
+    return re.sub(r"\s+", " ", name.replace("(anonymous namespace)::", ""))[:n]
+
+
+def _copy_factors(a):
+    cf = _per_dispatch(a.copy_fetch, "FETCH_SIZE", contains=a.copy_kernel)
+    cw = _per_dispatch(a.copy_write, "WRITE_SIZE", contains=a.copy_kernel)
+    if not cf or not cw:
+        sys.exit("missing copy dispatches")
+    known = a.copy_mib * (1 << 20)
+    med = lambda v: sorted(v)[len(v) // 2]
+    return known / (med(list(cf.values())) * 1024.0), known / (med(list(cw.values())) * 1024.0)
+
+
+def cmd_kernels(a):
+    f_r, f_w = _copy_factors(a)
+    fetch = _per_kernel(a.fetch, "FETCH_SIZE")
+    write = _per_kernel(a.write, "WRITE_SIZE")
+    stats = _stats_by_name(a.stats)
+    rows = []
+    for name, fd in fetch.items():
+        if not name.startswith("void snip::") and not name.startswith("snip::"):
+            continue
+        wd = write.get(name)
+        if not wd or name not in stats:
+            continue
+        rd = sum(fd.values()) / len(fd) * 1024 * f_r
+        wr = sum(wd.values()) / len(wd) * 1024 * f_w
+        calls, avg_ns = stats[name]
+        rows.append((name, len(fd), rd, wr, avg_ns, (rd + wr) / avg_ns))
+    rows.sort(key=lambda r: -r[1] * r[4])
+    # bf16 input bytes per dispatch of the fused quantizers (one read of X, W, dY per step)
+    sys.path.insert(0, ROOT)
+    import synth
+    elems = dual_elements_per_step(synth.WORKLOADS[a.workload])
+    launches = {}
+    for l, f in zip(synth.WORKLOADS[a.workload].layers, synth.WORKLOADS[a.workload].plan):
+        for key in ((f, False, True), (f, True, True)):
+            launches[key] = launches.get(key, 0) + 1
+
+    def input_mb(name):
+        m = re.search(r"quant_dual_kernel<(\d+), (true|false), (true|false)>", name)
+        if not m:
+            return "-"
+        key = (int(m.group(1)), m.group(2) == "true", m.group(3) == "true")
+        return f"{2.0 * elems[key] / launches[key] / 1e6:.2f}"
+    lines = [f"# HBM bytes and achieved HBM GB/s of every kernel on the {a.workload} workload", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, two --pmc runs of the benchmark), each scaled",
+             f"by the factor that makes a plain fp32 copy of {a.copy_mib} MiB read and write exactly its size",
+             f"(read {f_r:.4f}, write {f_w:.4f}); GB/s = bytes per dispatch over the kernel's average",
+             "duration in a kernel-trace run of the same benchmark (same launches per step). HBM peak 8000",
+             "GB/s. Commands (from the repository root):", "", "```", a.cmd, "```", "",
+             "The fused quantizers' bf16 input per dispatch (X and W of a layer, or its dY) is listed beside",
+             "the bytes they fetch: each tensor is read once.", "",
+             "| Kernel | Dispatches | Read MB / dispatch | bf16 input MB / dispatch | Written MB / dispatch | "
+             "Average us (trace) | HBM GB/s | of peak |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name, n, rd, wr, ns, gbs in rows:
+        lines.append(f"| `{_short(name)}` | {n} | {rd / 1e6:.2f} | {input_mb(name)} | {wr / 1e6:.2f} | {ns / 1e3:.2f} | "
+                     f"{gbs:.0f} | {gbs / 8000 * 100:.1f} % |")
+    lines.append("")
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def cmd_mfma(a):
+    sys.path.insert(0, ROOT)
+    import synth
+    wl = synth.WORKLOADS[a.workload]
+    flops_step = sum(3 * 2 * wl.tokens * l.d_in * l.d_out for l in wl.layers)
+    util = _per_kernel(a.pmc, "MfmaUtil")
+    mops = {k: _per_kernel(a.pmc, f"SQ_INSTS_VALU_MFMA_MOPS_{k}") for k in ("F16", "BF16", "F6F4", "F8")}
+    grbm = _per_kernel(a.pmc, "GRBM_GUI_ACTIVE")
+    stats = _stats_by_name(a.stats) if a.stats else {}
+    res = {}
+    for r in _counter_rows(a.pmc):
+        res.setdefault(r["Kernel_Name"].strip(), r["LDS_Block_Size"])
+    lines = [f"# MFMA utilisation of the GEMM kernels on the {a.workload} workload", "",
+             "One rocprofv3 --pmc run of the benchmark. MfmaUtil (rocprofv3's derived counter) = MFMA-busy",
+             "cycles summed over the SIMDs / (active GPU cycles x SIMDs), per dispatch, averaged over the",
+             "kernel's dispatches. MFMA TFLOP per dispatch = SQ_INSTS_VALU_MFMA_MOPS_* x 512. Commands (from",
+             "the repository root):", "", "```", a.cmd, "```", "",
+             "| Kernel | Dispatches | MfmaUtil % | MFMA GFLOP / dispatch (counted) | MFMA type | Average us (trace) | "
+             "LDS bytes |", "|---|---|---|---|---|---|---|"]
+    total = 0.0
+    for name in sorted(util, key=lambda n: -sum(util[n].values())):
+        if "gemm_kernel" not in name:
+            continue
+        ud = util[name]
+        fl = {k: sum(m.get(name, {}).values()) * 512 for k, m in mops.items()}
+        kind = max(fl, key=fl.get)
+        n = len(ud)
+        total += sum(fl.values())
+        avg = f"{stats[name][1] / 1e3:.2f}" if name in stats else "-"
+        lines.append(f"| `{_short(name)}` | {n} | {sum(ud.values()) / n:.1f} | {fl[kind] / n / 1e9:.2f} | {kind} | {avg} | "
+                     f"{res.get(name, '-')} |")
+    lines += ["", f"Counted MFMA flops over all GEMM dispatches: {total:.6e}; the workload's 2*M*N*K over the "
+              f"run's {a.steps} steps: {flops_step * a.steps:.6e} (ratio {total / (flops_step * a.steps):.6f}).",
+              ""]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9      # lane-operations per second, full-rate VALU
+
+
+def dual_elements_per_step(wl):
+    """Elements each fused quantize kernel family (format, row SR, column
+    SR) reads per step of the saved-operand layer calls: X and W once in the
+    forward (nearest row-wise, stochastic column-wise), dY once in the
+    backward (stochastic both ways)."""
+    out = {}
+    for l, f in zip(wl.layers, wl.plan):
+        fwd = (f, False, True)
+        bwd = (f, True, True)
+        out[fwd] = out.get(fwd, 0) + wl.tokens * l.d_in + l.d_out * l.d_in
+        out[bwd] = out.get(bwd, 0) + wl.tokens * l.d_out
+    return out
+
+
+def cmd_valu(a):
+    sys.path.insert(0, ROOT)
+    import synth
+    wl = synth.WORKLOADS[a.workload]
+    elems = dual_elements_per_step(wl)
+    insts = _per_kernel(a.pmc, "SQ_INSTS_VALU")
+    busy = _per_kernel(a.pmc, "VALUBusy")
+    stats = _stats_by_name(a.stats)
+    names = {0: "bf16", 1: "fp8_e4m3", 2: "nvfp4", 3: "mxfp4"}
+    lines = [f"# VALU work of the fused quantize kernels on the {a.workload} workload", "",
+             "One rocprofv3 --pmc run of the benchmark. Lane-ops per element = SQ_INSTS_VALU x 64 over the",
+             f"elements the kernel family quantized in the run's {a.steps} steps (X and W in the forward,",
+             "dY in the backward, one read each). VALU-bound rate = 39.3e12 lane-ops/s (256 CUs x 4 SIMDs",
+             "x 16 lanes x 2.4 GHz, full-rate instructions) over the lane-ops per element; reached = elements",
+             "per dispatch over the average duration of a kernel-trace run of the same benchmark. VALUBusy is",
+             "rocprofv3's derived counter. Commands (from the repository root):", "", "```", a.cmd, "```", "",
+             "| Kernel (format, row rounding, column rounding) | Dispatches | VALU lane-ops / element | VALUBusy % | "
+             "VALU-bound Gelem/s | reached Gelem/s | of VALU bound |", "|---|---|---|---|---|---|---|"]
+    out = []
+    for name, d in insts.items():
+        m = re.search(r"quant_dual_kernel<(\d+), (true|false), (true|false)>", name)
+        if not m:
+            continue
+        key = (int(m.group(1)), m.group(2) == "true", m.group(3) == "true")
+        n = len(d)
+        e_total = elems[key] * a.steps
+        ops = sum(d.values()) * 64 / e_total
+        bound = VALU_LANE_OPS / ops / 1e9
+        calls, avg_ns = stats[name]
+        reached = e_total / n / avg_ns
+        vb = sum(busy.get(name, {}).values()) / max(1, len(busy.get(name, {})))
+        label = f"{names[key[0]]}, {'SR' if key[1] else 'RNE'}, {'SR' if key[2] else 'RNE'}"
+        out.append({"kernel": label, "ops_per_elem": round(ops, 2), "valu_busy": round(vb, 1),
+                    "bound_gelem_s": round(bound, 1), "reached_gelem_s": round(reached, 1)})
+        lines.append(f"| `quant_dual_kernel` {label} | {n} | {ops:.1f} | {vb:.1f} | {bound:.0f} | {reached:.0f} | "
+                     f"{reached / bound * 100:.1f} % |")
+    lines += ["", "valu-json:" + json.dumps({"workload": a.workload, "source_hash": source_hash(QUANT_SOURCES),
+                                              "kernels": out}), ""]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def cmd_copy(a):
@@ -210,12 +428,28 @@ def main(argv=None):
         f.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     f.add_argument("--copy-kernel", default="MulFunctor", help="substring of the copy kernel's name")
     f.add_argument("--copy-mib", type=int, default=1024)
+    k = sub.add_parser("kernels")
+    for key in ("fetch", "write", "copy_fetch", "copy_write", "stats", "workload", "out", "cmd"):
+        k.add_argument("--" + key.replace("_", "-"), dest=key, required=True)
+    k.add_argument("--copy-kernel", default="MulFunctor")
+    k.add_argument("--copy-mib", type=int, default=1024)
+    m = sub.add_parser("mfma")
+    for key in ("pmc", "workload", "out", "cmd"):
+        m.add_argument("--" + key, dest=key, required=True)
+    m.add_argument("--stats", default=None)
+    m.add_argument("--steps", type=int, required=True, help="steps the profiled run made (warmup + 2 * steps)")
+    q = sub.add_parser("valu")
+    for key in ("pmc", "stats", "workload", "out", "cmd"):
+        q.add_argument("--" + key, dest=key, required=True)
+    q.add_argument("--steps", type=int, required=True, help="steps the profiled run made (warmup + 2 * steps)")
     v = sub.add_parser("vendor")
     v.add_argument("--workload", default="tinyllama1b")
     v.add_argument("--out", required=True)
     v.add_argument("--reps", type=int, default=20)
     a = ap.parse_args(argv)
-    {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic, "vendor": cmd_vendor}[a.cmd_name](a)
+    {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic, "kernels": cmd_kernels, "mfma": cmd_mfma,
+     "valu": cmd_valu,
+     "vendor": cmd_vendor}[a.cmd_name](a)
 
 
 if __name__ == "__main__":
