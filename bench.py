@@ -16,7 +16,8 @@ its MFMA roofline, the quantizers' credited HBM bandwidth, and the CPU
 oracle timed on a bounded sample on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--path fused|unfused] [--no-cpu-baseline] [--graph]
+                       [--path fused|unfused] [--scaling current|delayed]
+                       [--no-cpu-baseline] [--graph]
 """
 from __future__ import annotations
 
@@ -53,6 +54,9 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--path", choices=("fused", "unfused"), default="fused",
                     help="fused: one read of X, W and dY per step (saved-operand calls)")
+    ap.add_argument("--scaling", choices=("current", "delayed"), default="current",
+                    help="delayed: tensor maxima from the previous step's statistics (fused path only; "
+                         "the first warm-up step uses current scaling)")
     return ap.parse_args()
 
 
@@ -104,12 +108,21 @@ def main():
         layers.append(d)
     torch.cuda.synchronize()
 
+    delayed = {"on": False}
+    if args.scaling == "delayed" and not fused:
+        print(json.dumps({"error": "--scaling delayed needs the fused path and no BF16 layer"}))
+        sys.exit(2)
+
     def step_fused():
         for li, d in enumerate(layers):
+            # delayed scaling: the maxima are read in place from the records the
+            # step overwrites, i.e. the previous step's statistics
+            am = ((S.StatsAmax(d["st_f4"], 0), S.StatsAmax(d["st_f4"], 1), S.StatsAmax(d["st_b2"], 0))
+                  if delayed["on"] else (None, None, None))
             S.linear_fwd_save(d["x"], d["w"], d["fmt"], seed, li, y=d["y"], saved=d["saved"], stats=d["st_f4"],
-                              ws=d["ws_fs"])
+                              ws=d["ws_fs"], amax_x=am[0], amax_w=am[1])
             S.linear_bwd_saved(d["dy"], d["saved"], seed, li, dx=d["dx"], dw=d["dw"], stats=d["st_b2"],
-                               ws=d["ws_bs"])
+                               ws=d["ws_bs"], amax_dy=am[2])
 
     def step_unfused():
         for li, d in enumerate(layers):
@@ -120,6 +133,10 @@ def main():
     step = step_fused if fused else step_unfused
     gemm_flops = sum(3 * 2 * T * d["din"] * d["dout"] for d in layers)
 
+    if args.scaling == "delayed":
+        step()                                   # current scaling: seeds every statistics record
+        torch.cuda.synchronize()
+        delayed["on"] = True
     graph = None
     if args.graph:
         step()
@@ -254,7 +271,9 @@ def main():
         "config": {"workload": wl.name, "tokens": T,
                    "layers": [f"{d['name']} {d['din']}->{d['dout']}" for d in layers],
                    "plan": [S.FORMAT_NAMES[d["fmt"]] for d in layers], "graph": bool(graph),
-                   "quantizers": "fused: one read of X, W, dY per step" if fused else "separate passes"},
+                   "quantizers": "fused: one read of X, W, dY per step" if fused else "separate passes",
+                   "scaling": "delayed: tensor maxima from the previous step's statistics, no max pre-pass"
+                   if args.scaling == "delayed" else "current: tensor max of each tensor (pre-pass)"},
         "gemm": gemm_detail,
         "quantize": {"gbs": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / PEAK["hbm_gbs"], 4),
                      "ms_per_step": round(quant["ms"] / args.steps, 4),

@@ -128,7 +128,10 @@ typedef struct snip_qtensor {
 /* Per-tensor statistics of one quantize pass (device memory, 24 bytes):
  *   sum_err2    sum over finite elements of (Q(x) - x)^2 (fp64 total)
  *   sum_x2      sum over finite elements of x^2
- *   amax        max |x| over the finite elements (the tensor-scale input)
+ *   amax        max |x| over the finite elements of the tensor quantized:
+ *               the tensor-scale input, or, when a max was supplied
+ *               (amax_in), the tensor's own max, so that a delayed-scaling
+ *               caller can pass it to the next step
  *   n_nonfinite number of NaN / Inf inputs (their blocks' codes are
  *               unspecified) */
 typedef struct snip_stats {
@@ -166,8 +169,9 @@ typedef struct snip_tensor_report {
  *              multiple of their block).
  *   seed, tensor_id   random stream for SNIP_SR (ignored for SNIP_RNE).
  *   amax_in    device float or NULL. NULL: the tensor max is computed from x
- *              (an extra read pass). Non-NULL: used as max|x| (delayed
- *              scaling; elements beyond it saturate).
+ *              (an extra read pass). Non-NULL: used as max|x| for the tensor
+ *              scale (delayed scaling; elements beyond it saturate); stats
+ *              still reports x's own max.
  *   out        host descriptor of caller-owned device buffers; out->format,
  *              out->rows and out->k must match the call.
  *   stats      device snip_stats or NULL.
@@ -272,14 +276,23 @@ int snip_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld, in
  *   x          device bf16 [T][in]; w device bf16 [out][in] (contiguous).
  *   format     NVFP4, FP8_E4M3 or MXFP4, for all three GEMMs of the layer.
  *   T, in, out multiples of 128.
+ *   amax_x, amax_w  device float each, or NULL. NULL: that tensor's max is
+ *              computed from it (a read pass before quantizing). Non-NULL:
+ *              used as max|x| for the tensor scale of both layouts (delayed
+ *              scaling; elements beyond it saturate) and the pre-pass is
+ *              skipped. The pointer may be the amax field of an earlier
+ *              call's statistics record, including one that this call
+ *              overwrites: it is read before the statistics are written.
  *   wt, xt     host descriptors of caller-owned device buffers in `format`
  *              (rows in, k = out; rows in, k = T); the caller keeps them
  *              until snip_linear_bwd_saved.
- *   stats4     device snip_stats[4] = {X, W, W^T, X^T} or NULL.
+ *   stats4     device snip_stats[4] = {X, W, W^T, X^T} or NULL. The amax
+ *              field is always max|x| of the tensor quantized now.
  *   ws         device, snip_linear_fwd_save_workspace() bytes.
  * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
 int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, int64_t out,
-                         int format, uint64_t seed, uint32_t layer_id, float* y,
+                         int format, uint64_t seed, uint32_t layer_id,
+                         const float* amax_x, const float* amax_w, float* y,
                          const snip_qtensor* wt, const snip_qtensor* xt, snip_stats* stats4,
                          void* ws, size_t ws_bytes, void* stream);
 
@@ -293,13 +306,15 @@ int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, in
  *   dy         device bf16 [T][out].
  *   wt, xt     as written by snip_linear_fwd_save (same format; wt [in][out],
  *              xt [in][T]); T, in, out multiples of 128.
+ *   amax_dy    device float or NULL: a supplied max for dy, as amax_x of
+ *              snip_linear_fwd_save.
  *   dx, dw     device fp32 or NULL (NULL skips that GEMM).
- *   stats2     device snip_stats[2] = {dY, dY^T} or NULL.
+ *   stats2     device snip_stats[2] = {dY, dY^T} or NULL (amax: max|dy|).
  *   ws         device, snip_linear_bwd_saved_workspace() bytes.
  * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
 int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qtensor* xt,
                           int64_t T, int64_t in, int64_t out, uint64_t seed, uint32_t layer_id,
-                          float* dx, float* dw, snip_stats* stats2,
+                          const float* amax_dy, float* dx, float* dw, snip_stats* stats2,
                           void* ws, size_t ws_bytes, void* stream);
 
 /* Synchronise `stream`, copy n device statistics records to the host and

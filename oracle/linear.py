@@ -31,12 +31,13 @@ def tid(layer_id: int, role: int) -> int:
     return 8 * layer_id + role
 
 
-def linear_fwd(x, w, fmt: int, seed: int = 0, layer_id: int = 0, rows=None):
+def linear_fwd(x, w, fmt: int, seed: int = 0, layer_id: int = 0, rows=None, amax_x=None, amax_w=None):
     """x [T, in], w [out, in] (fp32 arrays of bf16 values). rows: optional
     subset of output rows (tokens) to compute; stats always cover the whole
-    tensors."""
-    qx = quantize(x, fmt, "rne", seed, tid(layer_id, ROLE_X_FWD))
-    qw = quantize(w, fmt, "rne", seed, tid(layer_id, ROLE_W_FWD))
+    tensors. amax_x, amax_w: supplied tensor maxima (delayed scaling) or
+    None for each tensor's own max."""
+    qx = quantize(x, fmt, "rne", seed, tid(layer_id, ROLE_X_FWD), amax=amax_x)
+    qw = quantize(w, fmt, "rne", seed, tid(layer_id, ROLE_W_FWD), amax=amax_w)
     y, bound = gemm_q(qx, qw, rows)
     return {"y": y, "bound": bound, "qx": qx, "qw": qw,
             "stats": [qx["stats"], qw["stats"]]}
@@ -64,21 +65,23 @@ def quantize_dual(x, fmt: int, rounding_row: str, rounding_col: str, seed: int, 
             quantize_colwise(x, fmt, rounding_col, seed, tid_col, amax=amax))
 
 
-def linear_fwd_save(x, w, fmt: int, seed: int = 0, layer_id: int = 0):
+def linear_fwd_save(x, w, fmt: int, seed: int = 0, layer_id: int = 0, amax_x=None, amax_w=None):
     """Forward plus the backward operands built from x and w, in the
     layer's one format: what linear_fwd computes, and the column-wise SR
-    operands W^T (dgrad B) and X^T (wgrad B) that linear_bwd builds."""
-    f = linear_fwd(x, w, fmt, seed, layer_id)
-    qwt = quantize_colwise(w, fmt, "sr", seed, tid(layer_id, ROLE_WT_DGRAD))
-    qxt = quantize_colwise(x, fmt, "sr", seed, tid(layer_id, ROLE_XT_WGRAD))
+    operands W^T (dgrad B) and X^T (wgrad B) that linear_bwd builds. With
+    supplied maxima both layouts of a tensor use the same one."""
+    f = linear_fwd(x, w, fmt, seed, layer_id, amax_x=amax_x, amax_w=amax_w)
+    qwt = quantize_colwise(w, fmt, "sr", seed, tid(layer_id, ROLE_WT_DGRAD), amax=amax_w)
+    qxt = quantize_colwise(x, fmt, "sr", seed, tid(layer_id, ROLE_XT_WGRAD), amax=amax_x)
     f.update(qwt=qwt, qxt=qxt, stats=[f["qx"]["stats"], f["qw"]["stats"], qwt["stats"], qxt["stats"]])
     return f
 
 
-def linear_bwd_saved(dy, qwt: dict, qxt: dict, fmt: int, seed: int = 0, layer_id: int = 0):
-    """Backward from saved W^T and X^T operands: dY quantized both ways."""
-    qdy = quantize(dy, fmt, "sr", seed, tid(layer_id, ROLE_DY_DGRAD))
-    qdyt = quantize_colwise(dy, fmt, "sr", seed, tid(layer_id, ROLE_DYT_WGRAD))
+def linear_bwd_saved(dy, qwt: dict, qxt: dict, fmt: int, seed: int = 0, layer_id: int = 0, amax_dy=None):
+    """Backward from saved W^T and X^T operands: dY quantized both ways
+    (with the supplied max amax_dy, or its own)."""
+    qdy = quantize(dy, fmt, "sr", seed, tid(layer_id, ROLE_DY_DGRAD), amax=amax_dy)
+    qdyt = quantize_colwise(dy, fmt, "sr", seed, tid(layer_id, ROLE_DYT_WGRAD), amax=amax_dy)
     dx, bdx = gemm_q(qdy, qwt)
     dw, bdw = gemm_q(qdyt, qxt)
     return {"dx": dx, "bound_dx": bdx, "dw": dw, "bound_dw": bdw, "q": [qdy, qdyt],

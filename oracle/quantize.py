@@ -35,6 +35,11 @@ Readings (the pages do not fix these):
     s = bf16_RNE(fp32(a_b / 6)) of the raw block max (bf16 has the range, so
     no tensor scale), then r = fp32(x * fp32(1 / s)). NVFP4 is the (16,
     E4M3) variant and MX-FP4 the (32, E8M0) one.
+  * The max|x| statistic is that of the tensor quantized, also when the
+    tensor scale comes from a supplied max (delayed scaling: the supplied
+    max is an earlier step's statistic, so each step must report its own).
+    For a caller quantizing a subset of a larger tensor's rows it is the
+    subset's max, like the sums.
   * Non-finite inputs lie outside the contract: they are counted, the tensor
     max ignores them, the statistics sum only finite elements, and the codes
     of a block holding one are unspecified (reported in `bad_blocks`).
@@ -127,7 +132,7 @@ def quantize(x: np.ndarray, fmt: int, rounding: str = "rne", seed: int = 0,
     if fmt == BF16:
         out.update(codes=None, packed=None, scales=None, texp=0,
                    xhat=x.astype(np.float64))
-        out["stats"] = _stats(x, out["xhat"], A)
+        out["stats"] = _stats(x, out["xhat"], tensor_amax(x))
         out["bad_blocks"] = ~fin
         return out
 
@@ -137,7 +142,7 @@ def quantize(x: np.ndarray, fmt: int, rounding: str = "rne", seed: int = 0,
         codes = F.e4m3_encode(r, rounding, draws)
         xhat = np.ldexp(F.e4m3_decode(codes), eS)
         out.update(codes=codes, packed=codes, scales=None, texp=eS, xhat=xhat)
-        out["stats"] = _stats(x, xhat, A)
+        out["stats"] = _stats(x, xhat, tensor_amax(x))
         out["bad_blocks"] = ~fin
         return out
 
@@ -192,7 +197,7 @@ def quantize(x: np.ndarray, fmt: int, rounding: str = "rne", seed: int = 0,
     scales = s_code.astype(np.uint16 if kind == "bf16" else np.uint8)
     out.update(codes=codes, packed=F.pack_nibbles(codes), scales=scales,
                texp=texp, xhat=xhat, bad_blocks=bad)
-    out["stats"] = _stats(x, xhat, A)
+    out["stats"] = _stats(x, xhat, tensor_amax(x))
     return out
 
 

@@ -99,13 +99,13 @@ _SIGS = {
                                       _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc), _c.c_void_p,
                                       _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "snip_linear_fwd_save": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
-                                        _c.c_int, _c.c_uint64, _c.c_uint32, _c.c_void_p,
-                                        _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc), _c.c_void_p,
-                                        _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+                                        _c.c_int, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
+                                        _c.c_void_p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
+                                        _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "snip_linear_bwd_saved": (_c.c_int, [_c.c_void_p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
                                          _c.c_int64, _c.c_int64, _c.c_int64, _c.c_uint64, _c.c_uint32,
-                                         _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
-                                         _c.c_void_p]),
+                                         _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                         _c.c_size_t, _c.c_void_p]),
     "snip_layer_stats": (_c.c_int, [_c.c_void_p, _c.c_int, _c.POINTER(TensorReport), _c.c_void_p]),
     "snip_quantize_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "snip_qgemm_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
@@ -151,6 +151,32 @@ def _stream(stream) -> int:
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+class StatsAmax:
+    """Device address of the amax field of record i of a statistics tensor
+    (snip_stats: sum_err2, sum_x2 as fp64, then amax as fp32 at byte 16):
+    a supplied tensor max for delayed scaling, read by the kernels without
+    a copy. Keeps the statistics tensor alive."""
+
+    def __init__(self, stats: torch.Tensor, i: int):
+        if not stats.is_cuda or stats.dtype != torch.float64 or stats.shape[-1] != 3 or not 0 <= i < stats.shape[0]:
+            raise ValueError("stats must be a GPU statistics tensor (new_stats) and i one of its records")
+        self.stats, self.i = stats, i
+
+    def data_ptr(self) -> int:
+        return self.stats.data_ptr() + STATS_BYTES * self.i + 16
+
+
+def _amax_ptr(a) -> Optional[int]:
+    """None, a device float32 tensor holding max|x|, or a StatsAmax."""
+    if a is None:
+        return None
+    if isinstance(a, StatsAmax):
+        return a.data_ptr()
+    if not a.is_cuda or a.dtype != torch.float32:
+        raise ValueError("a supplied max must be a device float32 tensor or a StatsAmax")
+    return a.data_ptr()
 
 
 def _require_cuda_bf16(t: torch.Tensor, name: str):
@@ -324,10 +350,12 @@ class SavedOperands:
 def linear_fwd_save(x: torch.Tensor, w: torch.Tensor, fmt: int, seed: int = 0, layer_id: int = 0,
                     y: Optional[torch.Tensor] = None, saved: Optional[SavedOperands] = None,
                     stats: Optional[torch.Tensor] = None, with_stats: bool = True,
-                    ws: Optional[torch.Tensor] = None, stream=None):
+                    ws: Optional[torch.Tensor] = None, stream=None, amax_x=None, amax_w=None):
     """snip_linear_fwd_save: y = Q_rne(x) . Q_rne(w)^T, plus the backward
     operands W^T and X^T from the same reads. Returns (y, saved, stats[4] =
-    {X, W, W^T, X^T})."""
+    {X, W, W^T, X^T}). amax_x, amax_w: supplied tensor maxima (delayed
+    scaling: a device float32 tensor or StatsAmax(stats, i) of an earlier
+    call's statistics) or None."""
     _require_cuda_bf16(x, "x")
     _require_cuda_bf16(w, "w")
     L = lib()
@@ -342,7 +370,8 @@ def linear_fwd_save(x: torch.Tensor, w: torch.Tensor, fmt: int, seed: int = 0, l
     if ws is None:
         ws = _workspace(L.snip_linear_fwd_save_workspace(T, din, dout, fmt), x.device)
     dwt, dxt = saved.wt.desc(), saved.xt.desc()
-    _check(L.snip_linear_fwd_save(_ptr(x), _ptr(w), T, din, dout, fmt, seed, layer_id, _ptr(y),
+    _check(L.snip_linear_fwd_save(_ptr(x), _ptr(w), T, din, dout, fmt, seed, layer_id, _amax_ptr(amax_x),
+                                  _amax_ptr(amax_w), _ptr(y),
                                   ctypes.byref(dwt), ctypes.byref(dxt), _ptr(stats), _ptr(ws), ws.numel(),
                                   _stream(stream)))
     return y, saved, stats
@@ -351,10 +380,12 @@ def linear_fwd_save(x: torch.Tensor, w: torch.Tensor, fmt: int, seed: int = 0, l
 def linear_bwd_saved(dy: torch.Tensor, saved: SavedOperands, seed: int = 0, layer_id: int = 0,
                      need_dx: bool = True, need_dw: bool = True, dx: Optional[torch.Tensor] = None,
                      dw: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
-                     with_stats: bool = True, ws: Optional[torch.Tensor] = None, stream=None):
+                     with_stats: bool = True, ws: Optional[torch.Tensor] = None, stream=None,
+                     amax_dy=None):
     """snip_linear_bwd_saved: dY read once (row-wise and column-wise SR),
     dx = Q(dy) . W^T-operand, dw = Q(dy^T) . X^T-operand. Returns (dx, dw,
-    stats[2] = {dY, dY^T})."""
+    stats[2] = {dY, dY^T}). amax_dy: a supplied max for dy, as in
+    linear_fwd_save."""
     _require_cuda_bf16(dy, "dy")
     L = lib()
     T, dout = dy.shape
@@ -369,7 +400,7 @@ def linear_bwd_saved(dy: torch.Tensor, saved: SavedOperands, seed: int = 0, laye
         ws = _workspace(L.snip_linear_bwd_saved_workspace(T, din, dout, saved.format), dy.device)
     dwt, dxt = saved.wt.desc(), saved.xt.desc()
     _check(L.snip_linear_bwd_saved(_ptr(dy), ctypes.byref(dwt), ctypes.byref(dxt), T, din, dout, seed,
-                                   layer_id, _ptr(dx) if need_dx else None, _ptr(dw) if need_dw else None,
+                                   layer_id, _amax_ptr(amax_dy), _ptr(dx) if need_dx else None, _ptr(dw) if need_dw else None,
                                    _ptr(stats), _ptr(ws), ws.numel(), _stream(stream)))
     return dx, dw, stats
 

@@ -913,9 +913,9 @@ int snip_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld, in
 }
 
 int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, int64_t out, int format,
-                         uint64_t seed, uint32_t layer_id, float* y, const snip_qtensor* wt,
-                         const snip_qtensor* xt, snip_stats* stats4, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         uint64_t seed, uint32_t layer_id, const float* amax_x, const float* amax_w, float* y,
+                         const snip_qtensor* wt, const snip_qtensor* xt, snip_stats* stats4, void* ws,
+                         size_t ws_bytes, void* stream) {
   if (!x || !w || !y) return fail(SNIP_E_NULL, "snip_linear_fwd_save: x, w and y must be non-NULL");
   if (!dual_format(format))
     return fail(SNIP_E_FORMAT, "snip_linear_fwd_save: format %d is not NVFP4, FP8_E4M3 or MXFP4", format);
@@ -932,7 +932,8 @@ int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, in
   if (wt->rows != in || wt->k != out || xt->rows != in || xt->k != T)
     return fail(SNIP_E_SHAPE, "snip_linear_fwd_save: wt must be [%lld][%lld] and xt [%lld][%lld]", (long long)in,
                 (long long)out, (long long)in, (long long)T);
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(stats4, 8) || !aligned(ws, 16))
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(stats4, 8) || !aligned(ws, 16) ||
+      !aligned(amax_x, 4) || !aligned(amax_w, 4))
     return fail(SNIP_E_ALIGN, "snip_linear_fwd_save: misaligned pointer");
   const size_t need = snip_linear_fwd_save_workspace(T, in, out, format);
   if (!ws || ws_bytes < need)
@@ -970,6 +971,8 @@ int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, in
   pw.col = dout_of(*wt, part[2], 8u * layer_id + 3u);
   pw.stats_row = stats4 ? stats4 + 1 : nullptr;
   pw.stats_col = stats4 ? stats4 + 2 : nullptr;
+  px.amax_in = amax_x;
+  pw.amax_in = amax_w;
   for (DPlan* p : {&px, &pw}) {
     p->format = format;
     p->sr_row = false;
@@ -978,13 +981,24 @@ int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, in
     p->nwg = dual_wg(format, p->rows, p->cols);
   }
   if (needs_amax(format)) {
-    APlan a[2] = {{xs, T, in, in, apx, amax_wg(T, in)}, {wsrc, out, in, in, apw, amax_wg(out, in)}};
-    rc = run_amax(a, 2, s);
-    if (rc) return rc;
-    px.amax_part = apx;
-    px.n_amax_part = a[0].nwg;
-    pw.amax_part = apw;
-    pw.n_amax_part = a[1].nwg;
+    // the tensor-max pre-pass of every tensor without a supplied max
+    APlan a[2];
+    DPlan* of[2];
+    uint32_t* dst[2] = {apx, apw};
+    int na = 0;
+    for (DPlan* p : {&px, &pw}) {
+      if (p->amax_in) continue;
+      a[na] = APlan{p->x, p->rows, p->cols, p->ld, dst[na], amax_wg(p->rows, p->cols)};
+      of[na++] = p;
+    }
+    if (na) {
+      rc = run_amax(a, na, s);
+      if (rc) return rc;
+      for (int i = 0; i < na; ++i) {
+        of[i]->amax_part = a[i].part;
+        of[i]->n_amax_part = a[i].nwg;
+      }
+    }
   }
   const DPlan* grp[2] = {&px, &pw};
   rc = run_dual_group(grp, 2, s);
@@ -996,8 +1010,8 @@ int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, in
 }
 
 int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qtensor* xt, int64_t T,
-                          int64_t in, int64_t out, uint64_t seed, uint32_t layer_id, float* dx, float* dw,
-                          snip_stats* stats2, void* ws, size_t ws_bytes, void* stream) {
+                          int64_t in, int64_t out, uint64_t seed, uint32_t layer_id, const float* amax_dy,
+                          float* dx, float* dw, snip_stats* stats2, void* ws, size_t ws_bytes, void* stream) {
   if (!dy) return fail(SNIP_E_NULL, "snip_linear_bwd_saved: dy is NULL");
   int rc = validate_qtensor(wt, "snip_linear_bwd_saved: wt");
   if (rc) return rc;
@@ -1013,7 +1027,8 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
   if (wt->rows != in || wt->k != out || xt->rows != in || xt->k != T)
     return fail(SNIP_E_SHAPE, "snip_linear_bwd_saved: wt must be [%lld][%lld] and xt [%lld][%lld]", (long long)in,
                 (long long)out, (long long)in, (long long)T);
-  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw, 16) || !aligned(stats2, 8) || !aligned(ws, 16))
+  if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw, 16) || !aligned(stats2, 8) || !aligned(ws, 16) ||
+      !aligned(amax_dy, 4))
     return fail(SNIP_E_ALIGN, "snip_linear_bwd_saved: misaligned pointer");
   const size_t need = snip_linear_bwd_saved_workspace(T, in, out, format);
   if (!ws || ws_bytes < need)
@@ -1031,7 +1046,7 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
   float* split = split_bytes ? reinterpret_cast<float*>(cv.take(split_bytes)) : nullptr;
   const uint16_t* dys = static_cast<const uint16_t*>(dy);
   int n_ap = 0;
-  if (needs_amax(format)) {
+  if (needs_amax(format) && !amax_dy) {
     APlan a{dys, T, out, out, ap, amax_wg(T, out)};
     rc = run_amax(&a, 1, s);
     if (rc) return rc;
@@ -1047,6 +1062,7 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
     p.sr_row = true;
     p.sr_col = true;
     p.seed = seed;
+    p.amax_in = amax_dy;
     p.amax_part = n_ap ? ap : nullptr;
     p.n_amax_part = n_ap;
     p.row = dout_of(qr.t, prow, 8u * layer_id + 2u);
@@ -1076,6 +1092,7 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
   p.sr = true;
   p.seed = seed;
   p.tensor_id = 8u * layer_id + (row ? 2u : 4u);
+  p.amax_in = amax_dy;
   p.amax_part = n_ap ? ap : nullptr;
   p.n_amax_part = n_ap;
   const snip_qtensor& q = row ? qr.t : qc.t;

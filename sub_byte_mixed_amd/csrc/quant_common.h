@@ -214,6 +214,18 @@ __device__ __forceinline__ void nonfinite_stats(const float (&x)[N], uint32_t& n
   }
 }
 
+// max |x| of a block whose values are all finite, as fp32 bits: the
+// current tensor's max is reported from these when the tensor scale comes
+// from a supplied max (a block with a non-finite value takes the finite max
+// nonfinite_stats finds instead).
+template <int N>
+__device__ __forceinline__ uint32_t block_absmax_bits(const float (&x)[N]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(x[i]));
+  return __float_as_uint(m);
+}
+
 __device__ __forceinline__ void unpack16(const uint4& v0, const uint4& v1, float (&x)[16]) {
   const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll

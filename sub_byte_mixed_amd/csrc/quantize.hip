@@ -81,6 +81,7 @@ struct RowAcc {
   double e2s = 0.0, x2s = 0.0;      // tensor-scaled domain (NVFP4, FP8)
   double e2r = 0.0, x2r = 0.0;      // raw domain (MX, non-finite blocks)
   uint32_t nf = 0u, amax_bits = 0u;
+  uint32_t tmax = 0u;               // max |x| seen (reported under a supplied max)
 };
 
 template <int FMT, bool SR>
@@ -143,6 +144,7 @@ __device__ __forceinline__ void row_item(const QJob& J, int eS, const float* inv
     uint32_t bnf = 0u, dummy = 0u;
     double rx2 = 0.0;
     if (bad) nonfinite_stats<16>(x, bnf, rx2, dummy);
+    if (J.amax_in) acc.tmax = max(acc.tmax, bad ? dummy : block_absmax_bits<16>(x));
     acc.nf += bnf;
     acc.x2r += rx2;
     acc.e2s += bad ? 0.0 : (double)be2;
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(256) void quant_row_kernel(QJobs jobs) {
     row_item<FMT, SR>(J, eS, inv_lut, it, cur[0], acc);
     if (it + 256 < nitems) row_item<FMT, SR>(J, eS, inv_lut, it + 256, cur[1], acc);
   }
-  if (FMT != SNIP_MXFP4) acc.amax_bits = __float_as_uint(A);
+  if (FMT != SNIP_MXFP4) acc.amax_bits = J.amax_in ? acc.tmax : __float_as_uint(A);
   const double e2 = ldexp(acc.e2s, 2 * eS) + acc.e2r;
   const double x2 = ldexp(acc.x2s, 2 * eS) + acc.x2r;
   wg_store_stats(J.part + wg, e2, x2, acc.nf, acc.amax_bits, dred, ured);
@@ -241,6 +243,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double e2s = 0.0, x2s = 0.0, e2r = 0.0, x2r = 0.0;
   uint32_t nf = 0u, amax_bits = 0u;
+  uint32_t tmax = 0u;                                          // max |x| seen (supplied-max runs)
 
   for (int64_t tile = wg; tile < ntiles; tile += J.nwg) {
     const int64_t r0 = (tile / tiles_c) * TR;
@@ -316,6 +319,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
             uint32_t bnf = 0u, dummy = 0u;
             double rx2 = 0.0;
             if (bad) nonfinite_stats<16>(x, bnf, rx2, dummy);
+            if (J.amax_in) tmax = max(tmax, bad ? dummy : block_absmax_bits<16>(x));
             nf += bnf;
             x2r += rx2;
             e2s += bad ? 0.0 : (double)be2;
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(256) void quant_col_kernel(QJobs jobs) {
     }
     __syncthreads();
   }
-  if (FMT != SNIP_MXFP4) amax_bits = __float_as_uint(A);
+  if (FMT != SNIP_MXFP4) amax_bits = J.amax_in ? tmax : __float_as_uint(A);
   const double e2 = ldexp(e2s, 2 * eS) + e2r;
   const double x2 = ldexp(x2s, 2 * eS) + x2r;
   wg_store_stats(J.part + wg, e2, x2, nf, amax_bits, dred, ured);

@@ -241,6 +241,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(DJobs jobs) {
 
   double e2s = 0.0, x2s = 0.0, e2r = 0.0, x2r = 0.0;           // column-wise statistics
   uint32_t nf = 0u, amax_bits = 0u;
+  uint32_t tmax = 0u;                                          // max |x| seen (supplied-max runs)
   RowStats rs;
   uint32_t* stg = lrow[wave];
 
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(DJobs jobs) {
             uint32_t bnf = 0u, dummy = 0u;
             double rx2 = 0.0;
             if (bad) nonfinite_stats<16>(x, bnf, rx2, dummy);
+            if (J.amax_in) tmax = max(tmax, bad ? dummy : block_absmax_bits<16>(x));
             nf += bnf;
             x2r += rx2;
             e2s += bad ? 0.0 : (double)be2;
@@ -365,8 +367,11 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(DJobs jobs) {
     __syncthreads();
   }
   if (FMT != SNIP_MXFP4) {
-    amax_bits = __float_as_uint(A);
-    rs.amax_bits = __float_as_uint(A);
+    // the tensor max used for scaling, or under a supplied max the current
+    // tensor's own (the column blocks cover every element once)
+    const uint32_t rep = J.amax_in ? tmax : __float_as_uint(A);
+    amax_bits = rep;
+    rs.amax_bits = rep;
   }
   wg_store_stats(J.col.part + wg, ldexp(e2s, 2 * eS) + e2r, ldexp(x2s, 2 * eS) + x2r, nf, amax_bits, dred, ured);
   __syncthreads();

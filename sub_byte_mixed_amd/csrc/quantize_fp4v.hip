@@ -43,6 +43,7 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float t) {
 struct VAcc {
   double e2 = 0.0, x2 = 0.0;
   uint32_t nf = 0u, amax_bits = 0u;
+  uint32_t tmax = 0u;                           // E4M3 scales: max |x| seen
 };
 
 // One block: codes (BLK/8 words), scale code, statistics.
@@ -55,11 +56,13 @@ __device__ __forceinline__ void fp4v_block(const float (&x)[BLK], int eS, uint64
   float shat;                                   // decoded scale (E4M3: scaled domain)
   int X = 0;                                    // E8M0 exponent
   float am = 0.0f;
+  float amr = 0.0f;                             // E4M3: max |x| before scaling
   if constexpr (KIND == kE4M3) {
 #pragma unroll
     for (int i = 0; i < BLK; ++i) {
       ref[i] = ldexpf(x[i], -eS);
       am = fmaxf(am, fabsf(ref[i]));
+      amr = fmaxf(amr, fabsf(x[i]));
     }
     sc = e4m3_rne(am / 6.0f);
     shat = e4m3_val(sc);
@@ -123,10 +126,12 @@ __device__ __forceinline__ void fp4v_block(const float (&x)[BLK], int eS, uint64
     acc.nf += bnf;
     acc.x2 += rx2;
     if (KIND != kE4M3) acc.amax_bits = max(acc.amax_bits, bam);
+    else acc.tmax = max(acc.tmax, bam);
   } else {
     acc.e2 += ldexp((double)be2, sh);
     acc.x2 += ldexp((double)bx2, sh);
     if (KIND != kE4M3) acc.amax_bits = max(acc.amax_bits, __float_as_uint(am));
+    else acc.tmax = max(acc.tmax, __float_as_uint(amr));
   }
 }
 
@@ -187,7 +192,9 @@ __global__ __launch_bounds__(256) void quant_fp4v_kernel(QJobs jobs) {
     store_codes<BLK>(J.codes + first / 2, out);
     store_scale<KIND>(J.scales, first / BLK, sc);
   }
-  if (KIND == kE4M3) acc.amax_bits = __float_as_uint(A);
+  // E4M3 scales: the tensor max used for scaling, or under a supplied max
+  // the current tensor's own
+  if (KIND == kE4M3) acc.amax_bits = J.amax_in ? acc.tmax : __float_as_uint(A);
   wg_store_stats(J.part + wg, acc.e2, acc.x2, acc.nf, acc.amax_bits, dred, ured);
 }
 

@@ -173,9 +173,9 @@ def test_saved_linear_validation(L):
     wt, xt = qdesc(S.NVFP4, din, dout), qdesc(S.NVFP4, din, T, codes=P2 + 0x20000)
     big = 1 << 30
 
-    def fwd(x=P, w=P2, T=T, din=din, dout=dout, fmt=S.NVFP4, wt=wt, xt=xt, ws_bytes=big):
-        return L.snip_linear_fwd_save(x, w, T, din, dout, fmt, 0, 0, y, ctypes.byref(wt), ctypes.byref(xt),
-                                      None, ws, ws_bytes, None)
+    def fwd(x=P, w=P2, T=T, din=din, dout=dout, fmt=S.NVFP4, wt=wt, xt=xt, ws_bytes=big, amax_x=None, amax_w=None):
+        return L.snip_linear_fwd_save(x, w, T, din, dout, fmt, 0, 0, amax_x, amax_w, y, ctypes.byref(wt),
+                                      ctypes.byref(xt), None, ws, ws_bytes, None)
     assert fwd(x=None) == -1
     assert fwd(fmt=S.BF16) == -4
     assert fwd(T=200) == -2                                      # T % 128
@@ -183,18 +183,21 @@ def test_saved_linear_validation(L):
     assert fwd(wt=qdesc(S.NVFP4, din, 256)) == -2                # wt shape
     assert fwd(xt=qdesc(S.FP8, din, T, scales=None)) == -4       # xt format
     assert fwd(x=P + 4) == -3
+    assert fwd(amax_x=P + 2) == -3                               # supplied max: 4-byte aligned
+    assert fwd(amax_w=P + 6) == -3
     assert fwd(ws_bytes=64) == -5
     assert L.snip_linear_fwd_save_workspace(T, din, dout, S.NVFP4) > 0
 
-    def bwd(dy=P, T=T, din=din, dout=dout, wt=wt, xt=xt, dx=dx, dw=dw, ws_bytes=big):
-        return L.snip_linear_bwd_saved(dy, ctypes.byref(wt), ctypes.byref(xt), T, din, dout, 0, 0, dx, dw,
-                                       None, ws, ws_bytes, None)
+    def bwd(dy=P, T=T, din=din, dout=dout, wt=wt, xt=xt, dx=dx, dw=dw, ws_bytes=big, amax_dy=None):
+        return L.snip_linear_bwd_saved(dy, ctypes.byref(wt), ctypes.byref(xt), T, din, dout, 0, 0, amax_dy, dx,
+                                       dw, None, ws, ws_bytes, None)
     assert bwd(dy=None) == -1
     assert bwd(xt=qdesc(S.MXFP4, din, T)) == -4                  # formats differ
     assert bwd(wt=qdesc(S.BF16, din, dout)) == -4
     assert bwd(T=128) == -2                                      # xt is [in][256]
     assert bwd(dout=200) == -2
     assert bwd(dx=dx + 4) == -3
+    assert bwd(amax_dy=P + 1) == -3
     assert bwd(ws_bytes=64) == -5
     assert L.snip_linear_bwd_saved_workspace(T, din, dout, S.BF16) == 0
 

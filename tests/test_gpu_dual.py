@@ -188,3 +188,76 @@ def test_saved_layer_full_size_matches_unfused():
         assert torch.equal(dw, dw0), layer.name
         del x, w, dy, y, saved, dx, dw, y0, dx0, dw0
     torch.cuda.empty_cache()
+
+
+def _layer_step(xd, wd, dyd, fmt, seed, layer_id, saved, st_f, st_b, amax=(None, None, None)):
+    y, _, _ = S.linear_fwd_save(xd, wd, fmt, seed, layer_id, saved=saved, stats=st_f, amax_x=amax[0],
+                                amax_w=amax[1])
+    dx, dw, _ = S.linear_bwd_saved(dyd, saved, seed, layer_id, stats=st_b, amax_dy=amax[2])
+    return y, dx, dw
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_saved_layer_delayed_scaling(fmt):
+    """Delayed scaling through the saved-operand calls: the tensor maxima
+    come from the previous step's statistics records (read in place, no
+    copy), the tensor-max pre-pass is skipped, and the statistics report the
+    current tensors' own maxima for the next step.
+      step 1: current scaling on (x, w, dy);
+      step 2: the same tensors with the maxima of step 1's records -> the
+              same bytes as step 1 (the maxima are equal);
+      step 3: new tensors (x/2 exactly, 2w, a new dy) with step 2's records,
+              which this step overwrites -> the oracle with those stale
+              maxima (codes, scales and exponents bit-exact, Y/dX/dW within
+              the bound), and statistics of the new tensors (amax = their
+              own max)."""
+    T, din, dout = 384, 256, 640
+    seed, layer_id = 5, 2
+    x = synth.gen_matrix((T, din), seed=11)
+    w = synth.gen_matrix((dout, din), seed=12, std=0.02)
+    dy = synth.gen_matrix((T, dout), seed=13, std=1e-3)
+    dev = torch.device("cuda:0")
+    say(f"delayed scaling fmt={fmt} T={T} in={din} out={dout}")
+    xd, wd, dyd = x.to(dev), w.to(dev), dy.to(dev)
+    saved = S.SavedOperands(fmt, T, din, dout, dev)
+    st_f, st_b = S.new_stats(4, dev), S.new_stats(2, dev)
+    y1, dx1, dw1 = (t.clone() for t in _layer_step(xd, wd, dyd, fmt, seed, layer_id, saved, st_f, st_b))
+    torch.cuda.synchronize()
+    wt1, xt1 = gpu_codes(saved.wt), gpu_codes(saved.xt)
+    sf1, sb1 = st_f.clone(), st_b.clone()
+
+    # step 2: maxima of step 1's records, read from a copy of them
+    amax = (S.StatsAmax(sf1, 0), S.StatsAmax(sf1, 1), S.StatsAmax(sb1, 0))
+    y2, dx2, dw2 = _layer_step(xd, wd, dyd, fmt, seed, layer_id, saved, st_f, st_b, amax)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y1) and torch.equal(dx2, dx1) and torch.equal(dw2, dw1)
+    for a, b in ((gpu_codes(saved.wt), wt1), (gpu_codes(saved.xt), xt1)):
+        for k in a:
+            assert np.array_equal(np.asarray(a[k]), np.asarray(b[k])), k
+    assert torch.equal(st_f.view(torch.uint8), sf1.view(torch.uint8))
+    assert torch.equal(st_b.view(torch.uint8), sb1.view(torch.uint8))
+
+    # step 3: new tensors, maxima read in place from the records this step overwrites
+    x3 = (x.float() * 0.5).to(torch.bfloat16)
+    w3 = (w.float() * 2.0).to(torch.bfloat16)
+    dy3 = synth.gen_matrix((T, dout), seed=14, std=3e-3)
+    stale = [S.decode_stats(st_f)[0]["amax"], S.decode_stats(st_f)[1]["amax"], S.decode_stats(st_b)[0]["amax"]]
+    amax = (S.StatsAmax(st_f, 0), S.StatsAmax(st_f, 1), S.StatsAmax(st_b, 0))
+    y3, dx3, dw3 = _layer_step(x3.to(dev), w3.to(dev), dy3.to(dev), fmt, seed, layer_id, saved, st_f, st_b, amax)
+    torch.cuda.synchronize()
+    x32, w32, dy32 = f32(x3), f32(w3), f32(dy3)
+    of = OL.linear_fwd_save(x32, w32, fmt, seed, layer_id, amax_x=stale[0], amax_w=stale[1])
+    ob = OL.linear_bwd_saved(dy32, of["qwt"], of["qxt"], fmt, seed, layer_id, amax_dy=stale[2])
+    compare_codes(gpu_codes(saved.wt), of["qwt"], fmt, what="delayed W^T")
+    compare_codes(gpu_codes(saved.xt), of["qxt"], fmt, what="delayed X^T")
+    check_gemm(y3.cpu().numpy().astype(np.float64), of["qx"]["xhat"], of["qw"]["xhat"], what="delayed Y")
+    check_gemm(dx3.cpu().numpy().astype(np.float64), ob["q"][0]["xhat"], of["qwt"]["xhat"], what="delayed dX")
+    check_gemm(dw3.cpu().numpy().astype(np.float64), ob["q"][1]["xhat"], of["qxt"]["xhat"], what="delayed dW")
+    for g, o, n in zip(S.decode_stats(st_f), of["stats"], ["X", "W", "W^T", "X^T"]):
+        compare_stats(g, o, what=f"delayed fwd_save stats {n}")
+    for g, o, n in zip(S.decode_stats(st_b), ob["stats"], ["dY", "dY^T"]):
+        compare_stats(g, o, what=f"delayed bwd_saved stats {n}")
+    # the reported maxima are the new tensors' own (x/2, 2w: exact halving/doubling)
+    got = S.decode_stats(st_f)
+    assert got[0]["amax"] == stale[0] / 2 and got[1]["amax"] == stale[1] * 2
+    assert S.decode_stats(st_b)[0]["amax"] == float(np.max(np.abs(dy32)))

@@ -196,3 +196,25 @@ def test_row_subset_matches_full(fmt):
     cols = np.array([5, 0, 63])
     colsub = Q.quantize_colwise(x, fmt, "sr", seed=3, tensor_id=11, col_ids=cols)
     assert np.array_equal(colsub["codes"], colw["codes"][cols])
+
+
+def test_supplied_max_sets_scale_stats_report_own_max():
+    """Delayed scaling: a supplied max (8.0 = 1.0 * 2^3) fixes the tensor
+    exponent by the closed forms (NVFP4 3 - 11 = -8, FP8 3 - 8 = -5), while
+    the max|x| statistic stays the tensor's own (0.75); a constant block is
+    still represented exactly (NVFP4: 0.75 * 2^8 = 192, block scale 32, code
+    6; FP8: 0.75 * 2^5 = 24, an E4M3 value)."""
+    x = np.full((4, 32), 0.75, np.float32)
+    for fmt, e in ((NVFP4, -8), (FP8, -5)):
+        q = Q.quantize(x, fmt, "rne", amax=8.0)
+        assert q["texp"] == e
+        assert q["stats"]["amax"] == 0.75
+        assert q["stats"]["sum_err2"] == 0.0
+        assert np.all(q["xhat"] == 0.75)
+    # a smaller supplied max saturates: 0.75 with max 0.25 -> FP8 eS = -9 (0.25 = 2^-2),
+    # 0.75 * 2^9 = 384 is still an E4M3 value; NVFP4 eS = -2 - 11 + 0 = -13 and the block
+    # scale saturates at 448: 0.75 * 2^13 / 6 = 1024 -> 448, r = 6144 / 448 > 6 -> 6
+    q = Q.quantize(x, NVFP4, "rne", amax=0.25)
+    assert q["texp"] == -13
+    assert np.all(q["xhat"] == 6.0 * 448.0 * 2.0 ** -13)
+    assert q["stats"]["amax"] == 0.75
