@@ -155,15 +155,19 @@ def main():
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         run()
-    e1.record()
+        ev[i + 1].record()                       # per-step boundaries (percentiles)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+    ms_step = max(ev[0].elapsed_time(ev[-1]), wall * 1e3) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    pct = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)}
+    from sub_byte_mixed_amd.profiling import copy_bandwidth
+    copy_gbs = copy_bandwidth(torch, dev)
     value = gemm_flops / (ms_step * 1e-3) / 1e12
 
     # ---------------------------------------------------- per-kernel timing
@@ -275,7 +279,10 @@ def main():
                    "scaling": "delayed: tensor maxima from the previous step's statistics, no max pre-pass"
                    if args.scaling == "delayed" else "current: tensor max of each tensor (pre-pass)"},
         "gemm": gemm_detail,
+        "step_ms_percentiles": pct,
+        "hbm_copy_gbs": round(copy_gbs, 1),
         "quantize": {"gbs": round(quant_gbs, 1), "frac_hbm": round(quant_gbs / PEAK["hbm_gbs"], 4),
+                     "frac_copy": round(quant_gbs / copy_gbs, 4),
                      "ms_per_step": round(quant["ms"] / args.steps, 4),
                      "launches_per_step": quant["launches"] // args.steps, "alu_roofline": alu},
         "other_kernels_ms_per_step": {k: round(v / args.steps, 4) for k, v in other_ms.items()},

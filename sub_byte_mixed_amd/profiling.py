@@ -300,6 +300,26 @@ def cmd_valu(a):
     print("\n".join(lines))
 
 
+def copy_bandwidth(torch, dev, mib: int = 1024, reps: int = 10) -> float:
+    """Measured device-to-device copy rate (GB/s, bytes read + written) of a
+    plain torch copy of `mib` MiB, the median of `reps`: the practical HBM
+    ceiling the quantizers are also compared with."""
+    a = torch.empty(mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    return 2.0 * (mib << 20) / (sorted(ts)[reps // 2] * 1e-3) / 1e9
+
+
 def cmd_copy(a):
     import torch
     n = a.mib * (1 << 20) // 4

@@ -73,10 +73,21 @@ def split_call(recs):
     return gemms, q_s, q_bytes, amax_s, fin_s
 
 
-def run_layer(S, torch, dev, wl, li, fmt, x, w, dy, reps, seed=0):
-    """Times one layer's forward and backward calls; returns a dict."""
+def rotation(torch, x, w, dy, min_bytes=512 << 20, most=32):
+    """Copies of a layer's inputs that together exceed the 256 MB Infinity
+    Cache twice over (at most `most`), so that repeated calls read their
+    inputs from HBM as a training step does."""
+    per = sum(t.numel() * t.element_size() for t in (x, w, dy))
+    n = max(1, min(most, -(-min_bytes // per)))
+    return [(x, w, dy)] + [(x.clone(), w.clone(), dy.clone()) for _ in range(n - 1)]
+
+
+def run_layer(S, torch, dev, wl, li, fmt, inputs, reps, seed=0):
+    """Times one layer's forward and backward calls, rotating over the
+    copies of its inputs; returns a dict."""
     L = S.lib()
     T, din, dout = wl.tokens, wl.layers[li].d_in, wl.layers[li].d_out
+    nrot = len(inputs)
     fused = fmt != S.BF16
     y = torch.empty((T, dout), dtype=torch.float32, device=dev)
     dx = torch.empty((T, din), dtype=torch.float32, device=dev)
@@ -87,37 +98,40 @@ def run_layer(S, torch, dev, wl, li, fmt, x, w, dy, reps, seed=0):
         wsf = torch.empty(L.snip_linear_fwd_save_workspace(T, din, dout, fmt), dtype=torch.uint8, device=dev)
         wsb = torch.empty(L.snip_linear_bwd_saved_workspace(T, din, dout, fmt), dtype=torch.uint8, device=dev)
 
-        def fwd():
+        def fwd(r):
+            x, w, _ = inputs[r % nrot]
             S.linear_fwd_save(x, w, fmt, seed, li, y=y, saved=saved, stats=st4, ws=wsf)
 
-        def bwd():
-            S.linear_bwd_saved(dy, saved, seed, li, dx=dx, dw=dw, stats=st2, ws=wsb)
+        def bwd(r):
+            S.linear_bwd_saved(inputs[r % nrot][2], saved, seed, li, dx=dx, dw=dw, stats=st2, ws=wsb)
     else:
         stf, stb = S.new_stats(2, dev), S.new_stats(4, dev)
         wsf = torch.empty(L.snip_linear_fwd_workspace(T, din, dout, fmt), dtype=torch.uint8, device=dev)
         wsb = torch.empty(L.snip_linear_bwd_workspace(T, din, dout, fmt, fmt), dtype=torch.uint8, device=dev)
 
-        def fwd():
+        def fwd(r):
+            x, w, _ = inputs[r % nrot]
             S.linear_fwd(x, w, fmt, seed, li, y=y, stats=stf, ws=wsf)
 
-        def bwd():
+        def bwd(r):
+            x, w, dy = inputs[r % nrot]
             S.linear_bwd(dy, x, w, fmt, fmt, seed, li, dx=dx, dw=dw, stats=stb, ws=wsb, fwd_stats=stf)
 
-    out = {"fused": fused}
+    out = {"fused": fused, "nrot": nrot}
     for name, call in (("fwd", fwd), ("bwd", bwd)):
-        for _ in range(2):
-            call()
+        for r in range(2):
+            call(r)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            call()
+        for r in range(reps):
+            call(r)
         e1.record()
         torch.cuda.synchronize()
         out[name + "_s"] = e0.elapsed_time(e1) * 1e-3 / reps
         S.timing_start(64 * reps)
-        for _ in range(reps):
-            call()
+        for r in range(reps):
+            call(r)
         recs, _ = S.timing_read()
         n = len(recs) // reps
         parts = [split_call(recs[i * n:(i + 1) * n]) for i in range(reps)]
@@ -139,19 +153,21 @@ def run_layer(S, torch, dev, wl, li, fmt, x, w, dy, reps, seed=0):
     return out
 
 
-def fmt_row(S, name, fmt, r):
+def fmt_row(S, name, fmt, r, copy_gbs):
     g = r["gemm_s"]
     cells = []
     for t, fl, rf in zip(g, r["flops"], r["roof_gemm"]):
         cells.append(f"{t * 1e6:.1f} ({fl / t / 1e12:.0f}, {fl / t / exec_peak(fmt) * 100:.0f} %, {rf / t * 100:.0f} %)")
     qgbs = r["q_bytes"] / r["q_s"] / 1e9 if r["q_s"] else 0.0
     return (f"| {name} | {S.FORMAT_NAMES[fmt]} | " + " | ".join(cells) +
-            f" | {r['q_s'] * 1e6:.1f} ({qgbs:.0f} GB/s, {qgbs * 1e9 / HBM * 100:.0f} %) | {r['amax_s'] * 1e6:.1f} | "
+            f" | {r['q_s'] * 1e6:.1f} ({qgbs:.0f} GB/s, {qgbs * 1e9 / HBM * 100:.0f} %, "
+            f"{qgbs / copy_gbs * 100:.0f} %) | {r['amax_s'] * 1e6:.1f} | "
             f"{r['call_s'] * 1e6:.1f} | {r['roof'] / r['call_s'] * 100:.0f} % |")
 
 
 HEADER = ("| layer | format | fwd GEMM us (TFLOP/s, % peak, t_roof/t) | dgrad GEMM | wgrad GEMM | "
-          "quantize us (credited GB/s, % HBM) | tensor max us | layer fwd+bwd us | sum t_roof / t |\n"
+          "quantize us (credited GB/s, % of 8 TB/s, % of copy) | tensor max us | layer fwd+bwd us | "
+          "sum t_roof / t |\n"
           "|---|---|---|---|---|---|---|---|---|")
 
 
@@ -167,6 +183,8 @@ def main(argv=None):
     import sub_byte_mixed_amd as S
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    from sub_byte_mixed_amd.profiling import copy_bandwidth
+    copy_gbs = copy_bandwidth(torch, dev)
     lines = ["# Per-configuration report: quantized linear layers on one MI355X", "",
              "Each layer's forward and backward calls on synthetic bf16 inputs resident in HBM (saved-operand",
              "calls for FP8/NVFP4/MX-FP4, separate calls for BF16), one layer at a time. Layer time = HIP events",
@@ -175,7 +193,10 @@ def main(argv=None):
              "repetitions for the GEMMs). GEMM cells: us (TFLOP/s, % of the peak of the MFMA it runs on: fp16",
              "2516.6 TFLOP/s for NVFP4, FP8 and BF16, FP4 10066.3 for MX-FP4; t_roof / t with t_roof =",
              "max(2MNK / peak, operand codes and scales + fp32 output / 8 TB/s)). Quantize = the quantize",
-             "passes of both calls, credited with the bf16 read and every layout's codes and scales written.",
+             "passes of both calls, credited with the bf16 read and every layout's codes and scales written,",
+             f"against 8 TB/s and against a measured device copy ({copy_gbs:.0f} GB/s read + written, torch copy",
+             "of 1 GiB, median of 10). Repetitions rotate over copies of the layer's inputs totalling over 512 MB",
+             "(at most 32), so inputs come from HBM as in a training step, not from the 256 MB Infinity Cache.",
              "sum t_roof / t = (the three GEMMs' t_roof + credited quantize bytes / 8 TB/s) over the layer's",
              "call time. Command (from the repository root):", "", "```",
              f"python -m sub_byte_mixed_amd.report --workloads {a.workloads} --reps {a.reps}"
@@ -187,28 +208,28 @@ def main(argv=None):
         runs = []
         if sweep:
             li = 0
-            x, w, dy = (t.to(dev) for t in synth.gen_layer(wl, li))
+            inputs = rotation(torch, *(t.to(dev) for t in synth.gen_layer(wl, li)))
             for fmt in (S.BF16, S.FP8, S.NVFP4, S.MXFP4):
                 t0 = time.time()
-                r = run_layer(S, torch, dev, wl, li, fmt, x, w, dy, a.reps)
+                r = run_layer(S, torch, dev, wl, li, fmt, inputs, a.reps)
                 runs.append((wl.layers[li], fmt, r))
                 print(f"[report] {wname} {S.FORMAT_NAMES[fmt]}: {r['call_s'] * 1e3:.3f} ms "
                       f"({time.time() - t0:.1f} s)", flush=True)
-            del x, w, dy
+            del inputs
         else:
             for li, layer in enumerate(wl.layers):
                 t0 = time.time()
-                x, w, dy = (t.to(dev) for t in synth.gen_layer(wl, li))
+                inputs = rotation(torch, *(t.to(dev) for t in synth.gen_layer(wl, li)))
                 fmt = wl.plan[li]
-                r = run_layer(S, torch, dev, wl, li, fmt, x, w, dy, a.reps)
+                r = run_layer(S, torch, dev, wl, li, fmt, inputs, a.reps)
                 runs.append((layer, fmt, r))
                 print(f"[report] {wname} {layer.name} {S.FORMAT_NAMES[fmt]}: {r['call_s'] * 1e3:.3f} ms "
                       f"({time.time() - t0:.1f} s)", flush=True)
-                del x, w, dy
+                del inputs
                 torch.cuda.empty_cache()
         lines += [f"## {wname} (T = {T})", "", HEADER]
         for layer, fmt, r in runs:
-            lines.append(fmt_row(S, f"{layer.name} {layer.d_in}->{layer.d_out}", fmt, r))
+            lines.append(fmt_row(S, f"{layer.name} {layer.d_in}->{layer.d_out}", fmt, r, copy_gbs))
         if not sweep:
             flops = sum(sum(r["flops"]) for _, _, r in runs)
             fp4 = sum(sum(r["flops"]) for _, f, r in runs if f in (S.NVFP4, S.MXFP4))
@@ -218,7 +239,7 @@ def main(argv=None):
             q = sum(r["q_s"] for _, _, r in runs)
             qb = sum(r["q_bytes"] for _, _, r in runs)
             am = sum(r["amax_s"] for _, _, r in runs)
-            lines += ["", f"Block: {call * 1e3:.3f} ms for {flops / 1e12:.3f} TFLOP of GEMMs "
+            lines += ["", f"Block: {call * 1e3:.3f} ms for {flops / 1e9:.1f} GFLOP of GEMMs "
                       f"({flops / call / 1e12:.0f} TFLOP/s over the layer calls; GEMM kernels alone "
                       f"{flops / gemm / 1e12:.0f} TFLOP/s); quantize {q * 1e3:.3f} ms at {qb / q / 1e9:.0f} GB/s "
                       f"credited; tensor max {am * 1e3:.3f} ms; sum t_roof / t = {roof / call * 100:.0f} %; "
