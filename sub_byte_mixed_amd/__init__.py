@@ -160,8 +160,9 @@ class StatsAmax:
     a copy. Keeps the statistics tensor alive."""
 
     def __init__(self, stats: torch.Tensor, i: int):
-        if not stats.is_cuda or stats.dtype != torch.float64 or stats.shape[-1] != 3 or not 0 <= i < stats.shape[0]:
-            raise ValueError("stats must be a GPU statistics tensor (new_stats) and i one of its records")
+        if (not stats.is_cuda or stats.dtype != torch.float64 or stats.dim() != 2 or stats.shape[1] != 3
+                or not stats.is_contiguous() or not 0 <= i < stats.shape[0]):
+            raise ValueError("stats must be a contiguous GPU statistics tensor (new_stats) and i one of its records")
         self.stats, self.i = stats, i
 
     def data_ptr(self) -> int:
@@ -174,7 +175,7 @@ def _amax_ptr(a) -> Optional[int]:
         return None
     if isinstance(a, StatsAmax):
         return a.data_ptr()
-    if not a.is_cuda or a.dtype != torch.float32:
+    if not a.is_cuda or a.dtype != torch.float32 or a.numel() < 1:
         raise ValueError("a supplied max must be a device float32 tensor or a StatsAmax")
     return a.data_ptr()
 
