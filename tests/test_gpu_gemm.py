@@ -83,8 +83,10 @@ PLAN_CASES = [
     (S.MXFP4, 2000, 1600, 768),     # staged 128x128, 256-element stages
     (S.MXFP4, 2000, 1600, 384),     # staged 128x128, 128-element stages
     (S.BF16, 2000, 1600, 384),      # staged 128x128
-    (S.NVFP4, 2000, 1600, 640),     # LDS-DMA 128x128
-    (S.FP8, 2000, 1600, 640),       # LDS-DMA 128x128
+    (S.NVFP4, 2000, 1600, 640),     # LDS-DMA 128x128, single-unit stages (K % 256 != 0)
+    (S.NVFP4, 2000, 1600, 768),     # LDS-DMA 128x128, two-unit stages
+    (S.FP8, 2000, 1600, 640),       # LDS-DMA 128x128, 208 tiles: two-unit stages
+    (S.FP8, 3000, 2000, 512),       # LDS-DMA 128x128, 384 tiles: 3-stage ring of single units
     (S.FP8, 4000, 240, 1024),       # 64x64, unsplit
     (S.NVFP4, 240, 2000, 2048),     # 64x64, K split 4 ways
 ]
