@@ -443,8 +443,15 @@ static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
     }
   }
   if constexpr (FMT == SNIP_FP8_E4M3 || FMT == SNIP_NVFP4) {
-    if (p.bm == 64) {                     // skinny problems: 4-stage ring of 8 KiB stages
-      hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 1>), grid, dim3(NT), 0, s, g);
+    if (p.bm == 64) {
+      // skinny problems: a 4-stage ring of two units per stage where K and
+      // the K split are whole such stages (4096x256x2048 FP8 13.6 -> 11.4 us,
+      // NVFP4 12.7 -> 11.7 us), else of single units
+      constexpr int K2 = 2 * Unit<FMT>::UE;
+      if (g.K % K2 == 0 && g.kchunk % K2 == 0)
+        hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 2>), grid, dim3(NT), 0, s, g);
+      else
+        hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 1>), grid, dim3(NT), 0, s, g);
       return;
     }
   }

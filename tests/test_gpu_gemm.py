@@ -87,8 +87,9 @@ PLAN_CASES = [
     (S.NVFP4, 2000, 1600, 768),     # LDS-DMA 128x128, two-unit stages
     (S.FP8, 2000, 1600, 640),       # LDS-DMA 128x128, 208 tiles: two-unit stages
     (S.FP8, 3000, 2000, 512),       # LDS-DMA 128x128, 384 tiles: 3-stage ring of single units
-    (S.FP8, 4000, 240, 1024),       # 64x64, unsplit
-    (S.NVFP4, 240, 2000, 2048),     # 64x64, K split 4 ways
+    (S.FP8, 4000, 240, 1024),       # 64x64, unsplit, two-unit stages
+    (S.NVFP4, 240, 2000, 2048),     # 64x64, K split 4 ways (512 each), two-unit stages
+    (S.NVFP4, 240, 2000, 1920),     # 64x64, K split 3 ways (640 each): single-unit stages
 ]
 
 
