@@ -234,6 +234,18 @@ def test_binding_requires_gpu_tensors():
         S.quantize(x, S.ROWWISE, S.NVFP4)
 
 
+def test_supplied_max_arguments_are_checked():
+    """Delayed-scaling maxima are checked in the binding before any library
+    call: a StatsAmax needs a contiguous GPU statistics tensor and a record
+    index inside it, a plain supplied max a device float32 tensor."""
+    import torch
+    with pytest.raises(ValueError):
+        S.StatsAmax(torch.zeros((2, 3), dtype=torch.float64), 0)       # not on the GPU
+    with pytest.raises(ValueError):
+        S._amax_ptr(torch.zeros(1, dtype=torch.float32))                # not on the GPU
+    assert S._amax_ptr(None) is None
+
+
 def test_timing_argument_errors(L):
     assert L.snip_timing_start(0) == -2
     assert L.snip_timing_start((1 << 20) + 1) == -2
