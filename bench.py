@@ -219,8 +219,9 @@ def main():
     ebytes = {S.BF16: 2.0, S.FP8: 1.0, S.NVFP4: 0.5 + 1 / 16, S.MXFP4: 0.5 + 1 / 32}[dom_fmt]
     shapes = [(T, d["dout"], d["din"]) for d in layers if d["fmt"] == dom_fmt]
     shapes = [s_ for (t, o, i) in shapes for s_ in ((t, o, i), (t, i, o), (o, i, t))]
-    alg_bytes = sum((m * k + n * k) * ebytes + 4.0 * m * n for m, n, k in shapes) / len(shapes)
     dom = gemm_by_fmt[dom_fmt]
+    # per launch: a layer's dgrad and wgrad GEMMs may share one launch
+    alg_bytes = sum((m * k + n * k) * ebytes + 4.0 * m * n for m, n, k in shapes) / (dom["launches"] / args.steps)
     avg_launch_s = dom["ms"] / dom["launches"] * 1e-3
     flops_per_launch = dom["flops"] / dom["launches"]
     achieved = flops_per_launch / avg_launch_s / 1e12

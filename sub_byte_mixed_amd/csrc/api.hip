@@ -623,8 +623,8 @@ QBuf carve_q(Carver& cv, int f, int64_t rows, int64_t k) {
 
 // One GEMM; `fin` (may be null) lists statistics finalisations that the
 // launch runs as extra workgroups after the quantize launches before it.
-int gemm_q(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, float* partial,
-           hipStream_t s, const FJobs* fin = nullptr) {
+GemmArgs gemm_args(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, float* partial,
+                   const FJobs* fin) {
   GemmArgs g;
   std::memset(&g, 0, sizeof(g));
   if (fin) g.fin = *fin;
@@ -640,7 +640,23 @@ int gemm_q(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, 
   g.K = a.k;
   g.ldc = ldc;
   g.partial = partial;
-  return hip_check(launch_gemm(a.format, g, s), "gemm launch");
+  return g;
+}
+
+int gemm_q(const snip_qtensor& a, const snip_qtensor& b, float* c, int64_t ldc, float* partial,
+           hipStream_t s, const FJobs* fin = nullptr) {
+  return hip_check(launch_gemm(a.format, gemm_args(a, b, c, ldc, partial, fin), s), "gemm launch");
+}
+
+// A layer's dgrad and wgrad GEMMs (same format, independent): one launch
+// where both run unsplit on 128x128 tiles, else two in order. `fin` rides
+// with the second.
+int gemm_q_pair(const snip_qtensor& a1, const snip_qtensor& b1, float* c1, int64_t ldc1,
+                const snip_qtensor& a2, const snip_qtensor& b2, float* c2, int64_t ldc2, float* partial,
+                hipStream_t s, const FJobs* fin) {
+  return hip_check(launch_gemm_pair(a1.format, gemm_args(a1, b1, c1, ldc1, partial, nullptr),
+                                    gemm_args(a2, b2, c2, ldc2, partial, fin), s),
+                   "gemm launch");
 }
 
 }  // namespace
@@ -833,12 +849,18 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int
   for (int i = 0; i < 4 && stats4; ++i)
     if (use[i]) fin_grp[nfin++] = &p[i];
   const FJobs fin = fjobs_of(fin_grp, nfin);
+  // dX = [T][out] . ([in][out])^T, dW = [out][T] . ([in][T])^T
+  if (dx && dw && fmt_dgrad == fmt_wgrad) {
+    r = gemm_q_pair(q[0].t, q[1].t, dx, in, q[2].t, q[3].t, dw, in, split, s, &fin);
+    if (r) return r;
+    return ok();
+  }
   if (dx) {
-    r = gemm_q(q[0].t, q[1].t, dx, in, split, s, dw ? nullptr : &fin);   // [T][out] . ([in][out])^T
+    r = gemm_q(q[0].t, q[1].t, dx, in, split, s, dw ? nullptr : &fin);
     if (r) return r;
   }
   if (dw) {
-    r = gemm_q(q[2].t, q[3].t, dw, in, split, s, &fin);                  // [out][T] . ([in][T])^T
+    r = gemm_q(q[2].t, q[3].t, dw, in, split, s, &fin);
     if (r) return r;
   }
   return ok();
@@ -1074,9 +1096,7 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
     rc = run_dual_group(grp, 1, s);
     if (rc) return rc;
     const FJobs fin = fjobs_of_dual(grp, 1);
-    rc = gemm_q(qr.t, *wt, dx, in, split, s);
-    if (rc) return rc;
-    rc = gemm_q(qc.t, *xt, dw, in, split, s, &fin);
+    rc = gemm_q_pair(qr.t, *wt, dx, in, qc.t, *xt, dw, in, split, s, &fin);
     if (rc) return rc;
     return ok();
   }

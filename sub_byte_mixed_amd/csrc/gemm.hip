@@ -122,7 +122,7 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
 }
 
 template <int FMT, int BM, int BN, int S, int UK>
-__global__ __launch_bounds__(NT, BM * BN > 256 * 128 ? 1 : 2) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NT, BM * BN > 256 * 128 ? 1 : 2) void gemm_kernel(GemmArgs g_in) {
   using U = Unit<FMT>;
   constexpr int UE = U::UE, NQ = U::NQ, SB = U::SB;
   constexpr int RBA = BM / 16, RBB = BN / 16;              // 16-row blocks per tile
@@ -142,14 +142,36 @@ __global__ __launch_bounds__(NT, BM * BN > 256 * 128 ? 1 : 2) void gemm_kernel(G
   constexpr int TM = WM / 16, TN = WN / 16;                // 16x16 MFMA tiles per wave
   constexpr int KS = UE * UK;                              // K elements per stage
   __shared__ __align__(1024) uint8_t smem[S * STAGE];
-  if (finalize_workgroup(g)) return;
+  if (finalize_workgroup(g_in)) return;
+
+  // Grouped launch: workgroups past the first problem's tiles take the
+  // second problem (unsplit), with tile ids counted from its first tile.
+  GemmArgs g = g_in;
+  int tile = blockIdx.x;
+  if (g_in.nsec && tile >= g_in.tiles_m * g_in.tiles_n) {
+    tile -= g_in.tiles_m * g_in.tiles_n;
+    g.a = g_in.sec.a;
+    g.b = g_in.sec.b;
+    g.as = g_in.sec.as;
+    g.bs = g_in.sec.bs;
+    g.ea = g_in.sec.ea;
+    g.eb = g_in.sec.eb;
+    g.c = g_in.sec.c;
+    g.M = g_in.sec.M;
+    g.N = g_in.sec.N;
+    g.K = g_in.sec.K;
+    g.ldc = g_in.sec.ldc;
+    g.kchunk = g_in.sec.K;
+    g.tiles_m = g_in.sec.tiles_m;
+    g.tiles_n = g_in.sec.tiles_n;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int r16 = lane & 15, grp = lane >> 4;
   int tm, tn;
-  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  tile_coords(tile, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t rowbytes = g.K / UE * 64;                  // code bytes per row
   const int64_t srow = SB ? g.K / UE * SB : 0;             // scale bytes per row
@@ -478,6 +500,46 @@ static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 4, 1>), grid, dim3(NT), 0, s, g);
   }
+}
+
+// Whether two GEMMs of one format share a launch: both FP8 or NVFP4 and
+// unsplit on 128x128 tiles in their own plans.
+static bool pair_grouped(int format, const GemmArgs& g1, const GemmArgs& g2) {
+  if (format != SNIP_FP8_E4M3 && format != SNIP_NVFP4) return false;
+  const GemmPlan p1 = plan_gemm(format, g1.M, g1.N, g1.K), p2 = plan_gemm(format, g2.M, g2.N, g2.K);
+  return p1.ksplit == 1 && p2.ksplit == 1 && p1.bm >= 128 && p2.bm >= 128;
+}
+
+hipError_t launch_gemm_pair(int format, const GemmArgs& g1_in, const GemmArgs& g2_in, hipStream_t s) {
+  if (!pair_grouped(format, g1_in, g2_in)) {
+    hipError_t e = launch_gemm(format, g1_in, s);
+    return e != hipSuccess ? e : launch_gemm(format, g2_in, s);
+  }
+  // the problem with the longer K (longer tiles) is dispatched first
+  const bool swap = g2_in.K > g1_in.K;
+  GemmArgs g = swap ? g2_in : g1_in;
+  const GemmArgs& h = swap ? g1_in : g2_in;
+  g.fin = g2_in.fin;
+  g.tiles_m = (int)ceil_div(g.M, 128);
+  g.tiles_n = (int)ceil_div(g.N, 128);
+  g.kchunk = g.K;
+  g.nsec = 1;
+  g.sec = GemmArgs::Second{h.a, h.b, h.as, h.bs, h.ea, h.eb, h.c, h.M, h.N, h.K, h.ldc,
+                           (int32_t)ceil_div(h.M, 128), (int32_t)ceil_div(h.N, 128)};
+  const int64_t tiles = (int64_t)g.tiles_m * g.tiles_n + (int64_t)g.sec.tiles_m * g.sec.tiles_n;
+  const dim3 grid((unsigned)(tiles + g.fin.n), 1);
+  const double flops = 2.0 * g.M * g.N * g.K + 2.0 * h.M * h.N * h.K;
+  const int slot = timing_begin(LaunchTag{SNIP_LAUNCH_GEMM, format, -1, -1, flops}, s);
+  if (format == SNIP_FP8_E4M3) {
+    hipLaunchKernelGGL((gemm_kernel<SNIP_FP8_E4M3, 128, 128, 3, 1>), grid, dim3(NT), 0, s, g);
+  } else if (g.K % 256 == 0 && h.K % 256 == 0) {
+    hipLaunchKernelGGL((gemm_kernel<SNIP_NVFP4, 128, 128, 2, 2>), grid, dim3(NT), 0, s, g);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<SNIP_NVFP4, 128, 128, 4, 1>), grid, dim3(NT), 0, s, g);
+  }
+  const hipError_t e = hipGetLastError();
+  timing_end(slot, s);
+  return e;
 }
 
 hipError_t launch_gemm(int format, const GemmArgs& g_in, hipStream_t s) {

@@ -36,7 +36,7 @@ __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, in
 // them after the quantize launches that wrote the partials. Returns true
 // for such a workgroup, which then does nothing else.
 __device__ __forceinline__ bool finalize_workgroup(const GemmArgs& g) {
-  const int tiles = g.tiles_m * g.tiles_n;
+  const int tiles = g.tiles_m * g.tiles_n + (g.nsec ? g.sec.tiles_m * g.sec.tiles_n : 0);
   if ((int)blockIdx.x < tiles) return false;
   if (blockIdx.y == 0) finalize_one(g.fin.j[blockIdx.x - tiles]);
   return true;

@@ -108,6 +108,16 @@ struct GemmArgs {
   int64_t kchunk;          // K elements per split (set by launch_gemm)
   FJobs fin;               // statistics finalisations run as extra workgroups
                            // of the launch (fin.n == 0: none)
+  // A second, independent problem of the same format run by the same launch
+  // (launch_gemm_pair): its tiles follow the first problem's, unsplit.
+  struct Second {
+    const uint8_t *a, *b, *as, *bs;
+    const int32_t *ea, *eb;
+    float* c;
+    int64_t M, N, K, ldc;
+    int32_t tiles_m, tiles_n;
+  } sec;
+  int32_t nsec;            // 0: one problem; 1: `sec` follows
 };
 
 // Tile shape and K split chosen on the host for one GEMM.
@@ -133,6 +143,12 @@ hipError_t launch_bf16_copy(const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_bf16_transpose(const QJobs& jobs, int total_wg, hipStream_t s);
 hipError_t launch_finalize(const FJobs& jobs, hipStream_t s);
 hipError_t launch_gemm(int format, const GemmArgs& g, hipStream_t s);
+// Two independent GEMMs of one format (a layer's dgrad and wgrad). Where both
+// run unsplit on 128x128 tiles they share one launch (g2's tiles after
+// g1's) so that each fills the other's idle workgroup slots and tail;
+// otherwise two launches. g2 carries the statistics finalisations; g1.fin
+// must be empty. Both need the same split-K scratch rules as launch_gemm.
+hipError_t launch_gemm_pair(int format, const GemmArgs& g1, const GemmArgs& g2, hipStream_t s);
 
 // Launch timing (snip_timing_*): when enabled, each launch is bracketed by
 // a pair of HIP events. timing_begin returns the slot to close with

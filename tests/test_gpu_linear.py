@@ -128,3 +128,40 @@ def test_launch_timing_records():
     # timing is off again: a further read is an error
     with pytest.raises(S.SnipError):
         S.timing_read()
+
+
+@pytest.mark.parametrize("fmt", [S.FP8, S.NVFP4])
+def test_bwd_grouped_gemms_match_single_launches(fmt):
+    """A layer's dgrad and wgrad GEMMs share one launch when both run unsplit
+    on 128x128 tiles (ragged N = in here). Each output must be byte-identical
+    to the same GEMM launched alone (dx only, dw only), and the grouped call
+    must record a single GEMM launch carrying both GEMMs' flops."""
+    T, din, dout = 2176, 1552, 1920
+    say(f"grouped bwd case T={T} in={din} out={dout} fmt={fmt}")
+    x = synth.gen_matrix((T, din), seed=11).cuda()
+    w = synth.gen_matrix((dout, din), seed=12, std=0.02).cuda()
+    dy = synth.gen_matrix((T, dout), seed=13, std=1e-3).cuda()
+    S.timing_start(64)
+    dx, dw, _ = S.linear_bwd(dy, x, w, fmt, fmt, 3, 2)
+    recs, _ = S.timing_read()
+    gemms = [r for r in recs if r["kind"] == "gemm"]
+    assert len(gemms) == 1
+    assert gemms[0]["work"] == 2.0 * T * din * dout * 2
+    dx1, _, _ = S.linear_bwd(dy, x, w, fmt, fmt, 3, 2, need_dw=False)
+    _, dw1, _ = S.linear_bwd(dy, x, w, fmt, fmt, 3, 2, need_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx1)
+    assert torch.equal(dw, dw1)
+    # the saved-operand calls (d_in a multiple of 128) take the same grouped
+    # launch and give the bytes of the separate calls
+    din = 1664
+    x = synth.gen_matrix((T, din), seed=14).cuda()
+    w = synth.gen_matrix((dout, din), seed=15, std=0.02).cuda()
+    dx, dw, _ = S.linear_bwd(dy, x, w, fmt, fmt, 3, 2)
+    y, saved, _ = S.linear_fwd_save(x, w, fmt, 3, 2)
+    S.timing_start(64)
+    dx2, dw2, _ = S.linear_bwd_saved(dy, saved, 3, 2)
+    recs, _ = S.timing_read()
+    assert len([r for r in recs if r["kind"] == "gemm"]) == 1
+    torch.cuda.synchronize()
+    assert torch.equal(dx2, dx) and torch.equal(dw2, dw)
