@@ -155,9 +155,15 @@ def run_layer(S, torch, dev, wl, li, fmt, inputs, reps, seed=0):
 
 def fmt_row(S, name, fmt, r, copy_gbs):
     g = r["gemm_s"]
-    cells = []
-    for t, fl, rf in zip(g, r["flops"], r["roof_gemm"]):
-        cells.append(f"{t * 1e6:.1f} ({fl / t / 1e12:.0f}, {fl / t / exec_peak(fmt) * 100:.0f} %, {rf / t * 100:.0f} %)")
+    def cell(t, fl, rf):
+        return f"{t * 1e6:.1f} ({fl / t / 1e12:.0f}, {fl / t / exec_peak(fmt) * 100:.0f} %, {rf / t * 100:.0f} %)"
+    fl, rf = r["flops"], r["roof_gemm"]
+    if len(g) == 2:
+        # dgrad and wgrad ran as one grouped launch: one cell for both
+        cells = [cell(g[0], fl[0], rf[0]), "dgrad+wgrad in one launch: " + cell(g[1], fl[1] + fl[2], rf[1] + rf[2]),
+                 "(in the dgrad launch)"]
+    else:
+        cells = [cell(t, f, x) for t, f, x in zip(g, fl, rf)]
     qgbs = r["q_bytes"] / r["q_s"] / 1e9 if r["q_s"] else 0.0
     return (f"| {name} | {S.FORMAT_NAMES[fmt]} | " + " | ".join(cells) +
             f" | {r['q_s'] * 1e6:.1f} ({qgbs:.0f} GB/s, {qgbs * 1e9 / HBM * 100:.0f} %, "
@@ -192,7 +198,8 @@ def main(argv=None):
              "timing (each launch between two HIP events, which adds about 2 us per launch; median over the",
              "repetitions for the GEMMs). GEMM cells: us (TFLOP/s, % of the peak of the MFMA it runs on: fp16",
              "2516.6 TFLOP/s for NVFP4, FP8 and BF16, FP4 10066.3 for MX-FP4; t_roof / t with t_roof =",
-             "max(2MNK / peak, operand codes and scales + fp32 output / 8 TB/s)). Quantize = the quantize",
+             "max(2MNK / peak, operand codes and scales + fp32 output / 8 TB/s)); where a layer's dgrad and",
+             "wgrad share one launch, one cell covers both. Quantize = the quantize",
              "passes of both calls, credited with the bf16 read and every layout's codes and scales written,",
              f"against 8 TB/s and against a measured device copy ({copy_gbs:.0f} GB/s read + written, torch copy",
              "of 1 GiB, median of 10). Repetitions rotate over copies of the layer's inputs totalling over 512 MB",
