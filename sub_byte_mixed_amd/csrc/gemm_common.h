@@ -48,7 +48,41 @@ __device__ __forceinline__ bool finalize_workgroup(const GemmArgs& g) {
 template <int TM, int TN>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, const floatx4_t (&acc)[TM][TN], int64_t r0,
                                            int64_t c0, int r16, int grp) {
-  if (g.kchunk >= g.K) {
+  const bool whole = g.kchunk >= g.K;
+  float* const base = whole ? g.c : g.partial + (int64_t)blockIdx.y * g.M * g.N;
+  const int64_t ld = whole ? g.ldc : g.N;
+  // A wave's sub-tile lying wholly inside C (every tile but the ragged last
+  // row and column of tiles) is stored without per-element checks: r0 and c0
+  // are wave-uniform, so each of the TM*16 rows starts at a scalar address
+  // and a lane adds one 32-bit byte offset (its row within the 4-row group
+  // and its column), with the 16-column blocks j as immediate offsets. The
+  // 128x128 wave tiles keep the checked form: with their 256 accumulators
+  // the extra code path adds register spills.
+  if (TM * TN <= 32 && r0 + 16 * TM <= g.M && c0 + 16 * TN <= g.N && ld <= (int64_t(1) << 26)) {
+    const uint32_t loff = (uint32_t)((4 * grp * ld + r16) * 4);
+    if (whole) {
+      const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          char* const rowp = reinterpret_cast<char*>(base + (r0 + i * 16 + v) * ld + c0) + loff;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) *reinterpret_cast<float*>(rowp + j * 64) = ldexpf(acc[i][j][v], e);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          char* const rowp = reinterpret_cast<char*>(base + (r0 + i * 16 + v) * ld + c0) + loff;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) *reinterpret_cast<float*>(rowp + j * 64) = acc[i][j][v];
+        }
+    }
+    return;
+  }
+  if (whole) {
     const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -58,11 +92,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const floatx4_t (&
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int64_t row = r0 + i * 16 + 4 * grp + v;
-          if (row < g.M && col < g.N) g.c[row * g.ldc + col] = ldexpf(acc[i][j][v], e);
+          if (row < g.M && col < g.N) base[row * ld + col] = ldexpf(acc[i][j][v], e);
         }
       }
   } else {
-    float* part = g.partial + (int64_t)blockIdx.y * g.M * g.N;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -71,7 +104,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const floatx4_t (&
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int64_t row = r0 + i * 16 + 4 * grp + v;
-          if (row < g.M && col < g.N) part[row * g.N + col] = acc[i][j][v];
+          if (row < g.M && col < g.N) base[row * ld + col] = acc[i][j][v];
         }
       }
   }
