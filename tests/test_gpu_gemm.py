@@ -69,6 +69,26 @@ def test_gemm_ldc_and_overwrite():
     check_gemm(h[:, :40].astype(np.float64), oa["xhat"], ob["xhat"], what="ldc")
 
 
+# Outputs written with ldc > N: the wave sub-tiles inside C take the
+# unchecked store (row addresses from ldc), ragged ones the checked store,
+# and the columns past N stay untouched. 384 x 320 runs on 64x64 tiles (all
+# inside C), 1536 x 2000 on 128x128 tiles (the last tile column is ragged).
+@pytest.mark.parametrize("fmt", [S.NVFP4, S.FP8])
+@pytest.mark.parametrize("M,N,ldc", [(384, 320, 400), (1536, 2000, 2048)])
+def test_gemm_ldc_interior_tiles(fmt, M, N, ldc):
+    K = 256
+    say(f"gemm ldc interior case fmt={fmt} M={M} N={N} K={K} ldc={ldc}")
+    a = synth.gen_matrix((M, K), seed=5)
+    b = synth.gen_matrix((N, K), seed=6, std=0.02)
+    oa, ob = oracle_quant(a, S.ROWWISE, fmt, S.RNE), oracle_quant(b, S.ROWWISE, fmt, S.SR, 1, 1)
+    big = torch.full((M, ldc), 7.0, dtype=torch.float32, device="cuda")
+    S.qgemm(upload_oracle_q(oa, fmt), upload_oracle_q(ob, fmt), out=big[:, :N])
+    torch.cuda.synchronize()
+    h = big.cpu().numpy()
+    assert np.all(h[:, N:] == 7.0)
+    check_gemm(h[:, :N].astype(np.float64), oa["xhat"], ob["xhat"], what=f"ldc interior fmt={fmt} {M}x{N}")
+
+
 # Shapes that make the planner pick each kernel and tile: FP8 256x128,
 # 256x256 for NVFP4, MX-FP4 and BF16, the register-staged 128x128 kernel for
 # MX-FP4 and BF16, and the LDS-DMA 128x128 kernel for NVFP4 / FP8 -- all
@@ -83,8 +103,8 @@ PLAN_CASES = [
     (S.MXFP4, 2000, 1600, 768),     # staged 128x128, 256-element stages
     (S.MXFP4, 2000, 1600, 384),     # staged 128x128, 128-element stages
     (S.BF16, 2000, 1600, 384),      # staged 128x128
-    (S.NVFP4, 2000, 1600, 640),     # LDS-DMA 128x128, single-unit stages (K % 256 != 0)
-    (S.NVFP4, 2000, 1600, 768),     # LDS-DMA 128x128, two-unit stages
+    (S.NVFP4, 2000, 1600, 640),     # LDS-DMA 128x128, 2-stage ring (K % 256 != 0)
+    (S.NVFP4, 2000, 1600, 768),     # LDS-DMA 128x128, 2-stage ring (K % 256 == 0)
     (S.FP8, 2000, 1600, 640),       # LDS-DMA 128x128, 208 tiles: two-unit stages
     (S.FP8, 3000, 2000, 512),       # LDS-DMA 128x128, 384 tiles: 3-stage ring of single units
     (S.FP8, 4000, 240, 1024),       # 64x64, unsplit, two-unit stages
