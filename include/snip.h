@@ -188,7 +188,10 @@ int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
 /* c[M][N] (fp32, leading dimension ldc, overwritten) = A . B^T, with
  * A = dequant(a) [M][K] and B = dequant(b) [N][K]; M = a->rows, N = b->rows,
  * K = a->k = b->k. [SNIP, Fig. 5]: the GEMMs of a linear layer.
- *   a, b       host descriptors; same format; K % 128 == 0; M, N > 0.
+ *   a, b       host descriptors; same format; K % 128 == 0; M, N > 0;
+ *              each operand's codes below 4 GiB (rows x K x bytes per
+ *              element), else SHAPE -- the same limit holds for every GEMM
+ *              operand of the layer calls below.
  *              NVFP4 (code x block scale) and FP8 codes are decoded exactly
  *              to fp16 and run on the fp16 MFMA; MXFP4 runs on the gfx950
  *              scaled 4-bit MFMA with its E8M0 block scales in the

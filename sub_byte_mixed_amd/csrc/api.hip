@@ -101,6 +101,21 @@ int64_t scale_bytes(int f, int64_t rows, int64_t k) {
   return rows * (k / block_of(f)) * per;
 }
 
+// The LDS-DMA GEMM kernels address an operand's rows with 32-bit byte
+// offsets, so the codes of every GEMM operand (A[M][K] and B[N][K]; their
+// block scales are smaller) must stay below 4 GiB. Checked before any HIP
+// call; a larger problem is split by the caller.
+constexpr double kMaxOperandBytes = 4294967296.0 - 1024.0;
+int gemm_operands_fit(int f, int64_t M, int64_t N, int64_t K, const char* who) {
+  const double per = f == SNIP_FP8_E4M3 ? 1.0 : f == SNIP_BF16 ? 2.0 : 0.5;
+  const int64_t rows[2] = {M, N};
+  for (int64_t r : rows)
+    if ((double)r * (double)K * per > kMaxOperandBytes)
+      return fail(SNIP_E_SHAPE, "%s: a %lld x %lld GEMM operand exceeds 4 GiB of codes", who, (long long)r,
+                  (long long)K);
+  return 0;
+}
+
 constexpr size_t kAlign = 256;
 constexpr size_t kAmaxBytes = align_up(kAmaxWG * sizeof(uint32_t), kAlign);
 constexpr size_t kPartBytes = align_up(kQuantWG * sizeof(StatPart), kAlign);
@@ -578,6 +593,8 @@ int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t l
   if (ldc < b->rows) return fail(SNIP_E_SHAPE, "snip_qgemm: ldc=%lld < N=%lld", (long long)ldc,
                                  (long long)b->rows);
   if (!aligned(c, 16)) return fail(SNIP_E_ALIGN, "snip_qgemm: c must be 16-byte aligned");
+  rc = gemm_operands_fit(a->format, a->rows, b->rows, a->k, "snip_qgemm");
+  if (rc) return rc;
   GemmArgs g;
   std::memset(&g, 0, sizeof(g));
   g.a = static_cast<const uint8_t*>(a->codes);
@@ -670,6 +687,7 @@ int snip_linear_fwd(const void* x, const void* w, int64_t T, int64_t in, int64_t
   if (!gemm_format(format)) return fail(SNIP_E_FORMAT, "snip_linear_fwd: format %d is not a GEMM format", format);
   if (T <= 0 || in <= 0 || out <= 0) return fail(SNIP_E_SHAPE, "snip_linear_fwd: dimensions must be > 0");
   if (in % 128) return fail(SNIP_E_SHAPE, "snip_linear_fwd: in=%lld not a multiple of 128", (long long)in);
+  if (int rc = gemm_operands_fit(format, T, out, in, "snip_linear_fwd")) return rc;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(stats2, 8) || !aligned(ws, 16))
     return fail(SNIP_E_ALIGN, "snip_linear_fwd: misaligned pointer");
   const size_t need = snip_linear_fwd_workspace(T, in, out, format);
@@ -754,6 +772,12 @@ int snip_linear_bwd(const void* dy, const void* x, const void* w, int64_t T, int
   if (dw) {
     if (T % 128) return fail(SNIP_E_SHAPE, "snip_linear_bwd: T=%lld not a multiple of 128 (wgrad K)", (long long)T);
     if (in % 16 || out % 16) return fail(SNIP_E_SHAPE, "snip_linear_bwd: in and out must be multiples of 16");
+  }
+  if (dx) {
+    if (int rc = gemm_operands_fit(fmt_dgrad, T, in, out, "snip_linear_bwd (dgrad)")) return rc;
+  }
+  if (dw) {
+    if (int rc = gemm_operands_fit(fmt_wgrad, out, in, T, "snip_linear_bwd (wgrad)")) return rc;
   }
   if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(w, 16) || !aligned(dx, 16) || !aligned(dw, 16) ||
       !aligned(stats4, 8) || !aligned(fwd_stats2, 8) || !aligned(ws, 16))
@@ -944,7 +968,11 @@ int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, in
   if (T <= 0 || in <= 0 || out <= 0 || T % 128 || in % 128 || out % 128)
     return fail(SNIP_E_SHAPE, "snip_linear_fwd_save: T=%lld in=%lld out=%lld must be positive multiples of 128",
                 (long long)T, (long long)in, (long long)out);
-  int rc = validate_qtensor(wt, "snip_linear_fwd_save: wt");
+  int rc = gemm_operands_fit(format, T, out, in, "snip_linear_fwd_save");
+  if (!rc) rc = gemm_operands_fit(format, T, in, out, "snip_linear_fwd_save (saved for dgrad)");
+  if (!rc) rc = gemm_operands_fit(format, out, in, T, "snip_linear_fwd_save (saved for wgrad)");
+  if (rc) return rc;
+  rc = validate_qtensor(wt, "snip_linear_fwd_save: wt");
   if (rc) return rc;
   rc = validate_qtensor(xt, "snip_linear_fwd_save: xt");
   if (rc) return rc;
@@ -1049,6 +1077,9 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
   if (wt->rows != in || wt->k != out || xt->rows != in || xt->k != T)
     return fail(SNIP_E_SHAPE, "snip_linear_bwd_saved: wt must be [%lld][%lld] and xt [%lld][%lld]", (long long)in,
                 (long long)out, (long long)in, (long long)T);
+  rc = gemm_operands_fit(format, T, in, out, "snip_linear_bwd_saved (dgrad)");
+  if (!rc) rc = gemm_operands_fit(format, out, in, T, "snip_linear_bwd_saved (wgrad)");
+  if (rc) return rc;
   if (!aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw, 16) || !aligned(stats2, 8) || !aligned(ws, 16) ||
       !aligned(amax_dy, 4))
     return fail(SNIP_E_ALIGN, "snip_linear_bwd_saved: misaligned pointer");

@@ -118,6 +118,13 @@ def test_qgemm_validation(L):
     assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(b), c + 4, 32, None, 0, None) == -3
     bad = qdesc(5, 32, 256)
     assert L.snip_qgemm(ctypes.byref(a), ctypes.byref(bad), c, 32, None, 0, None) == -4
+    # operands of 4 GiB of codes or more are refused before any HIP call
+    # (the GEMM kernels address rows with 32-bit byte offsets)
+    a8, big8 = qdesc(S.FP8, 64, 4096, scales=None), qdesc(S.FP8, 1 << 20, 4096, scales=None)
+    assert L.snip_qgemm(ctypes.byref(a8), ctypes.byref(big8), c, 1 << 20, None, 0, None) == -2
+    assert "4 GiB" in err(L)
+    a4, bigf4 = qdesc(S.NVFP4, 64, 4096), qdesc(S.NVFP4, 1 << 21, 4096)   # 4 GiB of nibbles
+    assert L.snip_qgemm(ctypes.byref(a4), ctypes.byref(bigf4), c, 1 << 21, None, 0, None) == -2
 
 
 def test_linear_validation(L):
@@ -139,6 +146,13 @@ def test_linear_validation(L):
                              1 << 30, None) == -4
     assert L.snip_linear_bwd(P, P2, P3, 128, 64, 128, S.NVFP4, S.FP8, 0, 0, None, dx, dw, None, ws,
                              64, None) == -5
+    # a GEMM operand of 4 GiB of codes: X [2^20][4096] in FP8 (forward A),
+    # X^T [4096][2^20] (wgrad B)
+    big = 1 << 20
+    assert L.snip_linear_fwd(P, P2, big, 4096, 128, S.FP8, 0, 0, y, None, ws, 1 << 30, None) == -2
+    assert "4 GiB" in err(L)
+    assert L.snip_linear_bwd(P, P2, P3, big, 4096, 128, S.FP8, S.FP8, 0, 0, None, None, dw, None, ws,
+                             1 << 30, None) == -2
 
 
 def dual(L, x=P, rows=64, cols=64, ld=64, fmt=S.NVFP4, rr=0, rc=1, out_row=None, out_col=None,
@@ -185,6 +199,7 @@ def test_saved_linear_validation(L):
     assert fwd(x=P + 4) == -3
     assert fwd(amax_x=P + 2) == -3                               # supplied max: 4-byte aligned
     assert fwd(amax_w=P + 6) == -3
+    assert fwd(T=1 << 20, din=4096, dout=128, fmt=S.FP8) == -2 and "4 GiB" in err(L)   # X^T: 4 GiB of codes
     assert fwd(ws_bytes=64) == -5
     assert L.snip_linear_fwd_save_workspace(T, din, dout, S.NVFP4) > 0
 
