@@ -240,6 +240,36 @@ def cmd_mfma(a):
     print("\n".join(lines))
 
 
+def cmd_stalls(a):
+    """Where the GEMM kernels' wave time goes: SQ wave-cycle counters of
+    several --pmc runs, each as a share of SQ_WAVE_CYCLES taken in the same
+    run (all in quad-cycles, summed over the kernel's dispatches)."""
+    rows = []                   # (counter, {kernel: share})
+    for path in a.pmc:
+        names = sorted({r["Counter_Name"] for r in _counter_rows(path)})
+        wave = _per_kernel(path, "SQ_WAVE_CYCLES")
+        for c in names:
+            if c == "SQ_WAVE_CYCLES":
+                continue
+            vals = _per_kernel(path, c)
+            rows.append((c, {k: sum(v.values()) / max(sum(wave.get(k, {}).values()), 1.0) for k, v in vals.items()}))
+    kernels = sorted({k for _, d in rows for k in d if "gemm_kernel" in k})
+    head = "| Counter / SQ_WAVE_CYCLES | " + " | ".join(f"`{_short(k, 48)}`" for k in kernels) + " |"
+    lines = [f"# Wave-cycle breakdown of the GEMM kernels on the {a.workload} workload", "",
+             "SQ counters in quad-cycles, summed over each kernel's dispatches in a --pmc run of the benchmark,",
+             "divided by SQ_WAVE_CYCLES of the same run: WAIT_ANY = waves waiting on a dependency (s_waitcnt,",
+             "barrier), WAIT_INST_ANY = waves with an instruction ready but not issued, ACTIVE_INST_* = waves",
+             "issuing that instruction type. Shares of a wave's time; with several waves per SIMD they overlap.",
+             "Commands (from the repository root):", "", "```", a.cmd, "```", "", head,
+             "|---|" + "---|" * len(kernels)]
+    for c, d in rows:
+        lines.append(f"| {c} | " + " | ".join(f"{100 * d.get(k, 0.0):.1f} %" for k in kernels) + " |")
+    lines.append("")
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9      # lane-operations per second, full-rate VALU
 
 
@@ -462,13 +492,17 @@ def main(argv=None):
     for key in ("pmc", "stats", "workload", "out", "cmd"):
         q.add_argument("--" + key, dest=key, required=True)
     q.add_argument("--steps", type=int, required=True, help="steps the profiled run made (warmup + 2 * steps)")
+    w = sub.add_parser("stalls")
+    w.add_argument("--pmc", nargs="+", required=True)
+    for key in ("workload", "out", "cmd"):
+        w.add_argument("--" + key, dest=key, required=True)
     v = sub.add_parser("vendor")
     v.add_argument("--workload", default="tinyllama1b")
     v.add_argument("--out", required=True)
     v.add_argument("--reps", type=int, default=20)
     a = ap.parse_args(argv)
     {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic, "kernels": cmd_kernels, "mfma": cmd_mfma,
-     "valu": cmd_valu,
+     "valu": cmd_valu, "stalls": cmd_stalls,
      "vendor": cmd_vendor}[a.cmd_name](a)
 
 
