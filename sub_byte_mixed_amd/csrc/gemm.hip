@@ -342,21 +342,42 @@ __global__ __launch_bounds__(NT, (gemm_min_wgs<FMT, BM, BN, S, UK>())) void gemm
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue(kt0 + s, s);
+  // NVFP4 keeps the slots of stages it and it+S-1 in counters advanced each
+  // iteration, and picks its wait by iteration count; FP8 derives both from
+  // `it`. The two forms compute the same slots and waits; their code
+  // schedules differ, and each format keeps the one that measured faster
+  // on MI355X (NVFP4 with counters: the tinyllama1b step's NVFP4 GEMMs -1 %,
+  // llama7b -1.4 %; FP8 with counters +2 %).
+  constexpr bool kSlotCounters = FMT == SNIP_NVFP4;
+  int srd = 0, swr = S - 1;
   for (int it = 0; it < nk; ++it) {
-    const int ahead = min(S - 2, nk - 1 - it);         // stages issued after it
-    if (S > 2 && ahead >= S - 2) wait_vm_barrier<NIW * (S > 2 ? S - 2 : 0)>();
-    else if (S > 3 && ahead == 1) wait_vm_barrier<NIW>();
-    else wait_vm_barrier<0>();
+    if constexpr (kSlotCounters) {
+      // S-2 stages are in flight behind stage it for it < nk-(S-2)
+      if (S > 2 && it < nk - (S - 2)) wait_vm_barrier<NIW * (S > 2 ? S - 2 : 0)>();
+      else if (S > 3 && it == nk - 2) wait_vm_barrier<NIW>();
+      else wait_vm_barrier<0>();
+    } else {
+      const int ahead = min(S - 2, nk - 1 - it);       // stages issued after it
+      if (S > 2 && ahead >= S - 2) wait_vm_barrier<NIW * (S > 2 ? S - 2 : 0)>();
+      else if (S > 3 && ahead == 1) wait_vm_barrier<NIW>();
+      else wait_vm_barrier<0>();
+    }
+    const int rd = kSlotCounters ? srd : it % S;        // slot of stage it
+    const int wr = kSlotCounters ? swr : (it + S - 1) % S;  // slot of stage it+S-1
     // FP8 issues the refill after its fragment reads, so the DMA address
     // and issue instructions run in the shadow of the LDS read latency:
     // measured on MI355X, the tinyllama1b step's FP8 GEMMs 0.593 -> 0.576
     // ms; NVFP4 measured 1-2 % slower that way and keeps the refill first.
     constexpr bool kRefillLate = FMT == SNIP_FP8_E4M3;
-    if (!kRefillLate && it + S - 1 < nk) issue(kt0 + it + S - 1, (it + S - 1) % S);
+    if (!kRefillLate && it + S - 1 < nk) issue(kt0 + it + S - 1, wr);
     Frags f[UK];
 #pragma unroll
-    for (int u = 0; u < UK; ++u) load(f[u], it % S, u);
-    if (kRefillLate && it + S - 1 < nk) issue(kt0 + it + S - 1, (it + S - 1) % S);
+    for (int u = 0; u < UK; ++u) load(f[u], rd, u);
+    if (kRefillLate && it + S - 1 < nk) issue(kt0 + it + S - 1, wr);
+    if constexpr (kSlotCounters) {
+      srd = srd == S - 1 ? 0 : srd + 1;
+      swr = swr == S - 1 ? 0 : swr + 1;
+    }
     // FP8: the wave runs its stage's MFMAs at raised issue priority, so that
     // with two or three waves per SIMD the one multiplying keeps the matrix
     // pipe while the others read and decode. Measured on MI355X: 3-15 %
