@@ -141,3 +141,30 @@ def test_checker_catches_an_early_refill():
             check(3, 6, 1, True)
     finally:
         schedule = good
+
+
+def wait_count_by_iteration(S, nk, niw, it):
+    # the NVFP4 form: S-2 stages are in flight behind stage it while
+    # it < nk - (S - 2); one behind it at it == nk - 2 (S > 3); none after
+    if S > 2 and it < nk - (S - 2):
+        return niw * (S - 2)
+    if S > 3 and it == nk - 2:
+        return niw
+    return 0
+
+
+def slots_by_counters(S, nk):
+    rd, wr, out = 0, S - 1, []
+    for _ in range(nk):
+        out.append((rd, wr))
+        rd = 0 if rd == S - 1 else rd + 1
+        wr = 0 if wr == S - 1 else wr + 1
+    return out
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 5])
+def test_counter_form_matches_derived_form(S):
+    for nk, niw in itertools.product(range(1, 40), (1, 2, 3)):
+        for it in range(nk):
+            assert wait_count_by_iteration(S, nk, niw, it) == wait_count(S, nk, niw, it), (S, nk, niw, it)
+        assert slots_by_counters(S, nk) == [(it % S, (it + S - 1) % S) for it in range(nk)]
