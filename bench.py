@@ -48,9 +48,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="tinyllama1b")
+    ap.add_argument("--workload", default="llama70b",
+                    help="llama70b (the largest single-GPU block, default), llama7b, tinyllama1b, ...")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=None, help="tokens of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=None, help="output rows per quantize pass of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
     ap.add_argument("--path", choices=("fused", "unfused"), default="fused",
                     help="fused: one read of X, W and dY per step (saved-operand calls)")
@@ -266,7 +267,7 @@ def main():
     # ------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_tokens)
+        cpu = cpu_baseline(wl, args.cpu_rows)
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -297,39 +298,120 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, tokens=None):
-    """The oracle as it stands on a bounded sample of the workload: forward +
-    backward of the Gate and Up layers (the first layer if there are none),
-    all six quantize passes and the three GEMMs of each in the layer's
-    format, on the first `tokens` tokens (default: the whole layer when it
-    holds at most 4096 tokens)."""
-    import synth
-    import sub_byte_mixed_amd as S
-    from oracle import linear as OL
+def host_info():
+    """The host the oracle runs on: CPU model, cores, affinity, numpy's BLAS."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            b = libs[0]
+            blas = {"library": b.get("internal_api"), "version": b.get("version"),
+                    "threads": b.get("num_threads"), "architecture": b.get("architecture")}
     except Exception:
-        threads = os.cpu_count() or 1
-    names = [l.name for l in wl.layers]
-    picks = [names.index(n) for n in ("Gate", "Up") if n in names] or [0]
-    Ts = min(tokens or 4096, wl.tokens)
-    flops, sec = 0, 0.0
-    for li in picks:
-        layer = wl.layers[li]
-        x, w, dy = synth.gen_x(wl, li, rows=Ts), synth.gen_w(wl, li), synth.gen_dy(wl, li, rows=Ts)
-        x32, w32, dy32 = (synth.bf16_to_f32(t) for t in (x, w, dy))
-        fmt = wl.plan[li]
-        t0 = time.perf_counter()
-        OL.linear_fwd(x32, w32, fmt, 0, li)
-        OL.linear_bwd(dy32, x32, w32, fmt, fmt, 0, li)
-        sec += time.perf_counter() - t0
-        flops += 3 * 2 * Ts * layer.d_in * layer.d_out
-    desc = ", ".join(f"{wl.layers[li].name} {wl.layers[li].d_in}->{wl.layers[li].d_out} "
-                     f"({S.FORMAT_NAMES[wl.plan[li]]})" for li in picks)
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"layers {desc}, T={Ts} of {wl.tokens} tokens, fwd+bwd incl. all six quantize passes"}
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "affinity_cores": len(os.sched_getaffinity(0)), "numpy": np.__version__, "blas": blas}
+
+
+def cpu_baseline(wl, rows=None, gemm_rows=None):
+    """The oracle as it stands, timed on a bounded sample of the workload and
+    extrapolated to one whole step.
+
+    Quantize passes: the oracle's numpy codec (one thread). Each of the six
+    passes of a layer (X, W row-wise RNE; dY row-wise SR; W, dY, X
+    column-wise SR) is timed on `rows` output rows of the largest layer
+    (tensor max of the whole tensor), in every format of the plan, giving
+    elements/s per (format, pass kind).
+    GEMMs: the oracle's fp64 reference (dequantized product and the
+    elementwise bound sum|a||b|, two BLAS matmuls on all of numpy's
+    threads), timed on a `gemm_rows` x `gemm_rows` block of the largest
+    layer's forward GEMM at its full K, giving fp64 flop/s.
+    The step estimate is every pass's elements over its measured rate plus
+    every GEMM's 2*M*N*K over the measured GEMM rate."""
+    import synth
+    import sub_byte_mixed_amd as S
+    from oracle import gemm as OG
+    from oracle import quantize as OQ
+    rows = rows or 2048
+    gemm_rows = gemm_rows or 4096
+    T = wl.tokens
+    big = max(range(len(wl.layers)), key=lambda i: wl.layers[i].d_in * wl.layers[i].d_out)
+    layer = wl.layers[big]
+    x = synth.bf16_to_f32(synth.gen_x(wl, big))
+    w = synth.bf16_to_f32(synth.gen_w(wl, big))
+    dy = synth.bf16_to_f32(synth.gen_dy(wl, big))
+    amax = {n: OQ.tensor_amax(t) for n, t in (("x", x), ("w", w), ("dy", dy))}
+    # pass kind -> (source, layout, rounding)
+    kinds = {"X row rne": ("x", 0, "rne"), "W row rne": ("w", 0, "rne"), "dY row sr": ("dy", 0, "sr"),
+             "W col sr": ("w", 1, "sr"), "dY col sr": ("dy", 1, "sr"), "X col sr": ("x", 1, "sr")}
+    src = {"x": x, "w": w, "dy": dy}
+    rate = {}
+    qsec = 0.0
+    fmts = sorted(set(f for f in wl.plan if f != S.BF16))
+    for fmt in fmts:
+        for kind, (name, lay, rnd) in kinds.items():
+            t = src[name]
+            n = min(rows, t.shape[0] if lay == 0 else t.shape[1])
+            ids = np.arange(n)
+            t0 = time.perf_counter()
+            if lay == 0:
+                OQ.quantize(t[:n], fmt, rnd, 0, 8 * big, amax=amax[name], row_ids=ids)
+                elems = n * t.shape[1]
+            else:
+                OQ.quantize_colwise(t, fmt, rnd, 0, 8 * big, amax=amax[name], col_ids=ids)
+                elems = n * t.shape[0]
+            dt = time.perf_counter() - t0
+            qsec += dt
+            rate[(fmt, kind)] = elems / dt
+    # fp64 GEMM: a gemm_rows x gemm_rows block of the forward GEMM at full K
+    gm = min(gemm_rows, T)
+    gn = min(gemm_rows, layer.d_out)
+    qa = OQ.quantize(x[:gm], wl.plan[big] if wl.plan[big] != S.BF16 else S.NVFP4, "rne", 0, 0, amax=amax["x"])
+    qb = OQ.quantize(w[:gn], wl.plan[big] if wl.plan[big] != S.BF16 else S.NVFP4, "rne", 0, 1, amax=amax["w"])
+    t0 = time.perf_counter()
+    OG.gemm_ref(qa["xhat"], qb["xhat"])
+    gsec = time.perf_counter() - t0
+    gemm_rate = 2.0 * gm * gn * layer.d_in / gsec          # oracle GEMM: product + bound
+    # one step of the workload at the measured rates
+    t_q = 0.0
+    step_flops = 0.0
+    for li, l in enumerate(wl.layers):
+        f = wl.plan[li]
+        step_flops += 3 * 2.0 * T * l.d_in * l.d_out
+        if f == S.BF16:
+            continue
+        n_elem = {"X": T * l.d_in, "W": l.d_out * l.d_in, "dY": T * l.d_out}
+        for kind in kinds:
+            t_q += n_elem[kind.split()[0]] / rate[(f, kind)]
+    t_g = step_flops / gemm_rate
+    info = host_info()
+    return {
+        "value": round(step_flops / (t_q + t_g) / 1e12, 8), "unit": "TFLOP/s",
+        "cores": int((info["blas"] or {}).get("threads") or info["affinity_cores"]), "kind": "oracle",
+        "sample": (f"{wl.name} {layer.name} {layer.d_in}->{layer.d_out}: each of the 6 quantize passes on "
+                   f"{rows} output rows per format ({', '.join(S.FORMAT_NAMES[f] for f in fmts)}), one thread; "
+                   f"the fp64 GEMM reference on a {gm}x{gn} block of its forward GEMM (K={layer.d_in}) on all "
+                   f"BLAS threads; extrapolated to the whole {T}-token step "
+                   f"({len(wl.layers)} layers, 6 passes and 3 GEMMs each)"),
+        "seconds": round(qsec + gsec, 2),
+        "step_seconds_estimate": round(t_q + t_g, 2),
+        "quantize_elems_per_s_1core": {f"{S.FORMAT_NAMES[f]} {k}": round(v) for (f, k), v in rate.items()},
+        "quantize_step_seconds": round(t_q, 2),
+        "gemm_fp64_flops_per_s": round(gemm_rate), "gemm_note": "per 2*M*N*K of the product; the oracle "
+        "also forms the bound sum|a||b|, a second fp64 matmul of the same size",
+        "gemm_step_seconds": round(t_g, 2),
+        "host": info,
+    }
 
 
 if __name__ == "__main__":

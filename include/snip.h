@@ -341,6 +341,21 @@ size_t snip_quantize_dual_workspace(int64_t rows, int64_t cols, int format);
 size_t snip_linear_fwd_save_workspace(int64_t T, int64_t in, int64_t out, int format);
 size_t snip_linear_bwd_saved_workspace(int64_t T, int64_t in, int64_t out, int format);
 
+/* Workspace bytes of any of the calls above, by operation code: the one
+ * sizing entry of the boundary, equal to the per-call helper of that call.
+ *   op       SNIP_OP_* below; M, N, K as listed there (K is ignored by the
+ *            quantizers); format: the call's format (for SNIP_OP_LINEAR_BWD
+ *            both fmt_dgrad and fmt_wgrad).
+ * Returns 0 on an unknown op or invalid arguments. */
+#define SNIP_OP_QUANTIZE          0  /* M = rows, N = cols                       */
+#define SNIP_OP_QGEMM             1  /* M, N, K of C[M][N] = A[M][K] . B[N][K]^T */
+#define SNIP_OP_LINEAR_FWD        2  /* M = T, N = out, K = in                    */
+#define SNIP_OP_LINEAR_BWD        3  /* M = T, N = out, K = in                    */
+#define SNIP_OP_QUANTIZE_DUAL     4  /* M = rows, N = cols                       */
+#define SNIP_OP_LINEAR_FWD_SAVE   5  /* M = T, N = out, K = in                    */
+#define SNIP_OP_LINEAR_BWD_SAVED  6  /* M = T, N = out, K = in                    */
+size_t snip_workspace_size(int op, int64_t M, int64_t N, int64_t K, int format);
+
 /* Bytes of one part of a quantized operand: part 0 = codes, 1 = scales.
  * Returns -1 on invalid arguments. */
 int64_t snip_qtensor_bytes(int format, int64_t rows, int64_t k, int part);

@@ -35,6 +35,9 @@ BF16, FP8_E4M3, NVFP4, MXFP4 = 0, 1, 2, 3
 FP8 = FP8_E4M3
 RNE, SR = 0, 1
 ROWWISE, COLWISE, BOTHWISE = 0, 1, 2
+# operation codes of snip_workspace_size
+(OP_QUANTIZE, OP_QGEMM, OP_LINEAR_FWD, OP_LINEAR_BWD, OP_QUANTIZE_DUAL, OP_LINEAR_FWD_SAVE,
+ OP_LINEAR_BWD_SAVED) = range(7)
 # FP4 design-space variants (quantizer only): E2M1 with another block or scale
 FP4_E4M3_B32, FP4_E8M0_B16, FP4_BF16_B16, FP4_BF16_B32 = 4, 5, 6, 7
 FORMAT_NAMES = {BF16: "bf16", FP8_E4M3: "fp8_e4m3", NVFP4: "nvfp4", MXFP4: "mxfp4",
@@ -115,6 +118,7 @@ _SIGS = {
     "snip_quantize_dual_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int]),
     "snip_linear_fwd_save_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "snip_linear_bwd_saved_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
+    "snip_workspace_size": (_c.c_size_t, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "snip_qtensor_bytes": (_c.c_int64, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int]),
     "snip_timing_start": (_c.c_int, [_c.c_int]),
     "snip_timing_read": (_c.c_int, [_c.POINTER(LaunchRecord), _c.c_int, _c.POINTER(_c.c_int64)]),

@@ -15,6 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsnip.so")
+BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 SOURCES = ["api.hip", "quantize.hip", "quantize_dual.hip", "quantize_fp4v.hip", "gemm.hip", "gemm_staged.hip"]
 
 HIPCC_FLAGS = [
@@ -51,15 +52,31 @@ def build_checker(verbose: bool = False) -> str:
     return CHECKER_BIN
 
 
-def build(verbose: bool = False) -> str:
-    out_tmp = LIB + ".tmp"
-    cmd = [hipcc_path(), *HIPCC_FLAGS, "-o", out_tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc_path(), *[f for f in HIPCC_FLAGS if f != "-shared"], "-c", "-o", obj, os.path.join(CSRC, src)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
-    errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed:\n{errs}")
+        errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    out_tmp = LIB + ".tmp"
+    cmd = [hipcc_path(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(out_tmp, LIB)
     return LIB
 

@@ -506,6 +506,19 @@ size_t snip_linear_bwd_saved_workspace(int64_t T, int64_t in, int64_t out, int f
          align_up(split, kAlign);
 }
 
+size_t snip_workspace_size(int op, int64_t M, int64_t N, int64_t K, int format) {
+  switch (op) {
+    case SNIP_OP_QUANTIZE: return snip_quantize_workspace(M, N, SNIP_ROWWISE, format);
+    case SNIP_OP_QGEMM: return snip_qgemm_workspace(M, N, K, format);
+    case SNIP_OP_LINEAR_FWD: return snip_linear_fwd_workspace(M, K, N, format);
+    case SNIP_OP_LINEAR_BWD: return snip_linear_bwd_workspace(M, K, N, format, format);
+    case SNIP_OP_QUANTIZE_DUAL: return snip_quantize_dual_workspace(M, N, format);
+    case SNIP_OP_LINEAR_FWD_SAVE: return snip_linear_fwd_save_workspace(M, K, N, format);
+    case SNIP_OP_LINEAR_BWD_SAVED: return snip_linear_bwd_saved_workspace(M, K, N, format);
+    default: return 0;
+  }
+}
+
 int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int layout, int format,
                   int rounding, uint64_t seed, uint32_t tensor_id, const float* amax_in,
                   const snip_qtensor* out, snip_stats* stats, void* ws, size_t ws_bytes,

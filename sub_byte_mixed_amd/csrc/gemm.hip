@@ -53,7 +53,7 @@
 // 128x128 (two per CU) or, for skinny FP8 / NVFP4 problems, 64x64, as
 // plan_gemm decides from the problem's tile rounds. Tile order: the hardware hands workgroups to the 8 XCDs
 // round-robin; tile ids are remapped so each XCD works on a contiguous range,
-// and tiles are ordered in groups of 8 tile-rows so that concurrently running
+// and tiles are ordered in groups of 4 tile-rows so that concurrently running
 // tiles share A and B panels in that XCD's L2. Skinny problems split K across
 // workgroups into fp32 partials that a second kernel sums in a fixed order.
 #include "gemm_common.h"
@@ -123,7 +123,7 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
 
 // Workgroups per CU that the register budget is sized for. NVFP4 128x128
 // tiles on a 2-stage ring of single units (36 KiB of LDS) fit three per CU
-// in 168 registers without spills; measured on MI355X against the former
+// in 144 registers without spills; measured on MI355X against the former
 // two per CU (a 72 KiB ring of two units, or four single-unit stages):
 // the tinyllama1b step's NVFP4 GEMMs 0.457 -> 0.441 ms.
 template <int FMT, int BM, int BN, int S, int UK>
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(NT, (gemm_min_wgs<FMT, BM, BN, S, UK>())) void gemm
   // iteration, and picks its wait by iteration count; FP8 derives both from
   // `it`. The two forms compute the same slots and waits; their code
   // schedules differ, and each format keeps the one that measured faster
-  // on MI355X (NVFP4 with counters: the tinyllama1b step's NVFP4 GEMMs -1 %,
-  // llama7b -1.4 %; FP8 with counters +2 %).
+  // on MI355X (NVFP4 with counters 1-1.5 % faster on the tinyllama1b and
+  // llama7b steps; FP8 with counters 2 % slower).
   constexpr bool kSlotCounters = FMT == SNIP_NVFP4;
   int srd = 0, swr = S - 1;
   for (int it = 0; it < nk; ++it) {
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NT, (gemm_min_wgs<FMT, BM, BN, S, UK>())) void gemm
     const int wr = kSlotCounters ? swr : (it + S - 1) % S;  // slot of stage it+S-1
     // FP8 issues the refill after its fragment reads, so the DMA address
     // and issue instructions run in the shadow of the LDS read latency:
-    // measured on MI355X, the tinyllama1b step's FP8 GEMMs 0.593 -> 0.576
+    // measured on MI355X, the tinyllama1b step's FP8 GEMMs 0.609 -> 0.594
     // ms; NVFP4 measured 1-2 % slower that way and keeps the refill first.
     constexpr bool kRefillLate = FMT == SNIP_FP8_E4M3;
     if (!kRefillLate && it + S - 1 < nk) issue(kt0 + it + S - 1, wr);
@@ -420,7 +420,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nspl
 // K so that about 256 workgroups run.
 static double big_tile_gain(int format) {
   switch (format) {
-    case SNIP_NVFP4: return 1.06;
     case SNIP_FP8_E4M3: return 1.15;
     case SNIP_MXFP4: return 1.03;
     default: return 1.02;
@@ -450,7 +449,7 @@ static TileTimes tile_times(int format, int64_t M, int64_t N) {
   t.t128 = ceil_div(M, 128) * ceil_div(N, 128);
   t.trect = ceil_div(M, 256) * ceil_div(N, 128);
   t.time128 = rounds2(t.t128);
-  t.time256 = (double)ceil_div(t.t256, 256) * 2.0 / big_tile_gain(format);
+  t.time256 = format == SNIP_NVFP4 ? 1e30 : (double)ceil_div(t.t256, 256) * 2.0 / big_tile_gain(format);
   t.timerect = rect_gain(format) > 0.0 ? rounds2(t.trect) * 2.0 / rect_gain(format) : 1e30;
   // FP8 256x128 tiles whose last round is less than half full leave CUs idle
   // that the 128x128 tiles, three per CU, fill. Measured on MI355X for
@@ -506,19 +505,20 @@ size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K) {
   return p.ksplit > 1 ? (size_t)p.ksplit * (size_t)(M * N) * sizeof(float) : 0;
 }
 
+// Returns false when the plan names a kernel this format has no instance of.
 template <int FMT>
-static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
+static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)(p.tiles + g.fin.n), (unsigned)p.ksplit);
   if constexpr (FMT == SNIP_FP8_E4M3) {
     if (p.bm == 256 && p.bn == 128) {     // 3-stage ring: 72 KiB, two per CU
       hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 3, 1>), grid, dim3(NT), 0, s, g);
-      return;
+      return true;
     }
   }
   if constexpr (FMT == SNIP_NVFP4) {
     if (p.bm == 256 && p.bn == 128) {     // 2-stage ring: 54 KiB, two per CU
       hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 2, 1>), grid, dim3(NT), 0, s, g);
-      return;
+      return true;
     }
   }
   if constexpr (FMT == SNIP_FP8_E4M3 || FMT == SNIP_NVFP4) {
@@ -531,17 +531,21 @@ static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
         hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 2>), grid, dim3(NT), 0, s, g);
       else
         hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 1>), grid, dim3(NT), 0, s, g);
-      return;
+      return true;
     }
   }
-  if (p.bm == 256) hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1>), grid, dim3(NT), 0, s, g);
-  else if (p.staged) launch_staged(FMT, p.bk, g, grid, s);
+  if (p.bm == 256) {
+    // NVFP4 has no 256x256 instance: plan_gemm never picks it (its 256x128
+    // tiles are estimated faster at every size)
+    if constexpr (FMT == SNIP_NVFP4) return false;
+    else hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1>), grid, dim3(NT), 0, s, g);
+  } else if (p.staged) launch_staged(FMT, p.bk, g, grid, s);
   else if constexpr (FMT == SNIP_FP8_E4M3) {
     // FP8 128x128: a 3-stage ring (48 KiB) lets a third workgroup share the
     // CU where registers allow (measured up to 7 % faster). With at most one
     // tile per CU (no third workgroup to gain) two 64-element units per
     // stage halve the barriers per K: 2048x2048x4096 45.0 -> 41.6 us.
-    if (p.ksplit == 1 && p.tiles <= 256)
+    if (p.ksplit == 1 && p.tiles <= 256 && g.K % (2 * Unit<FMT>::UE) == 0)
       hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2>), grid, dim3(NT), 0, s, g);
     else
       hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 3, 1>), grid, dim3(NT), 0, s, g);
@@ -552,6 +556,7 @@ static void launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 4, 1>), grid, dim3(NT), 0, s, g);
   }
+  return true;
 }
 
 // Whether two GEMMs of one format share a launch: both FP8 or NVFP4, both
@@ -573,6 +578,8 @@ static bool pair_grouped(int format, const GemmArgs& g1, const GemmArgs& g2) {
 }
 
 hipError_t launch_gemm_pair(int format, const GemmArgs& g1_in, const GemmArgs& g2_in, hipStream_t s) {
+  // every kernel runs whole K units (the ABI requires K % 128 == 0)
+  if (g1_in.K % unit_k(format) || g2_in.K % unit_k(format)) return hipErrorInvalidValue;
   if (!pair_grouped(format, g1_in, g2_in)) {
     hipError_t e = launch_gemm(format, g1_in, s);
     return e != hipSuccess ? e : launch_gemm(format, g2_in, s);
@@ -603,6 +610,8 @@ hipError_t launch_gemm_pair(int format, const GemmArgs& g1_in, const GemmArgs& g
 }
 
 hipError_t launch_gemm(int format, const GemmArgs& g_in, hipStream_t s) {
+  if (format < SNIP_BF16 || format > SNIP_MXFP4) return hipErrorInvalidValue;
+  if (g_in.K % unit_k(format)) return hipErrorInvalidValue;   // whole K units only
   GemmPlan p = plan_gemm(format, g_in.M, g_in.N, g_in.K);
   GemmArgs g = g_in;
   if (p.ksplit > 1 && g.partial == nullptr) {      // no scratch: run unsplit
@@ -613,15 +622,15 @@ hipError_t launch_gemm(int format, const GemmArgs& g_in, hipStream_t s) {
   g.tiles_m = (int)ceil_div(g.M, p.bm);
   g.tiles_n = (int)ceil_div(g.N, p.bn);
   g.kchunk = p.kchunk;
-  if (format < SNIP_BF16 || format > SNIP_MXFP4) return hipErrorInvalidValue;
   int slot = timing_begin(LaunchTag{SNIP_LAUNCH_GEMM, format, -1, -1, 2.0 * g.M * g.N * g.K}, s);
+  bool launched;
   switch (format) {
-    case SNIP_NVFP4: launch_fmt<SNIP_NVFP4>(p, g, s); break;
-    case SNIP_FP8_E4M3: launch_fmt<SNIP_FP8_E4M3>(p, g, s); break;
-    case SNIP_MXFP4: launch_fmt<SNIP_MXFP4>(p, g, s); break;
-    default: launch_fmt<SNIP_BF16>(p, g, s); break;
+    case SNIP_NVFP4: launched = launch_fmt<SNIP_NVFP4>(p, g, s); break;
+    case SNIP_FP8_E4M3: launched = launch_fmt<SNIP_FP8_E4M3>(p, g, s); break;
+    case SNIP_MXFP4: launched = launch_fmt<SNIP_MXFP4>(p, g, s); break;
+    default: launched = launch_fmt<SNIP_BF16>(p, g, s); break;
   }
-  hipError_t e = hipGetLastError();
+  hipError_t e = launched ? hipGetLastError() : hipErrorInvalidValue;
   timing_end(slot, s);
   if (e != hipSuccess || p.ksplit == 1) return e;
   int64_t wg = ceil_div(g.M * g.N, 256);

@@ -8,6 +8,7 @@ sum err^2), max|x| and the non-finite count exactly.
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -124,3 +125,56 @@ def check_gemm(c_gpu: np.ndarray, a_hat: np.ndarray, b_hat: np.ndarray, what="")
         raise AssertionError(f"{what}: GEMM outside 1e-5*sum|a||b| (worst ratio {worst:.3e}) at {i}: "
                              f"gpu {c_gpu[i]} ref {c_ref[i]} bound {bound[i]}")
     return worst
+
+
+# ---------------------------------------------------------------- full-tensor oracle, in chunks
+# The oracle's quantizers are numpy element-wise code: a large tensor is
+# quantized in chunks of output rows (each with the whole tensor's max and
+# its global row indices, so every code, scale and random draw is the one
+# the whole-tensor call gives), on a pool of threads (numpy releases the
+# interpreter lock inside its array loops). The chunks' statistics are summed
+# in fp64; their codes and dequantized values are concatenated when asked for.
+_POOL = None
+
+
+def oracle_threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=oracle_threads())
+    return _POOL
+
+
+def oracle_chunked(t32: np.ndarray, fmt: int, layout: int, rounding: int, seed: int, tid: int,
+                   amax=None, keep: bool = False, chunk_elems: int = 1 << 21) -> dict:
+    """Oracle quantization of the whole tensor t32 [R, C] (row-wise: output
+    [R][C]; column-wise: output [C][R]) computed chunk by chunk. Returns the
+    statistics (and with keep=True the full codes, scales, tensor exponent
+    and dequantized values, as oracle.quantize does)."""
+    A = OQ.tensor_amax(t32) if amax is None else np.float32(amax)
+    R, C = t32.shape
+    n_out, k = (R, C) if layout == S.ROWWISE else (C, R)
+    step = max(16, (chunk_elems // k) // 16 * 16)
+    spans = [(r0, min(n_out, r0 + step)) for r0 in range(0, n_out, step)]
+
+    def one(span):
+        ids = np.arange(span[0], span[1])
+        if layout == S.ROWWISE:
+            return OQ.quantize(t32[span[0]:span[1]], fmt, RND[rounding], seed, tid, amax=A, row_ids=ids)
+        return OQ.quantize_colwise(t32, fmt, RND[rounding], seed, tid, amax=A, col_ids=ids)
+
+    parts = list(_pool().map(one, spans))
+    st = {"sum_err2": float(sum(p["stats"]["sum_err2"] for p in parts)),
+          "sum_x2": float(sum(p["stats"]["sum_x2"] for p in parts)),
+          "amax": float(max(p["stats"]["amax"] for p in parts)),
+          "n_nonfinite": int(sum(p["stats"]["n_nonfinite"] for p in parts))}
+    out = {"stats": st, "texp": parts[0]["texp"], "rows": n_out, "k": k}
+    if keep:
+        for key in ("packed", "scales", "codes", "xhat", "bad_blocks"):
+            if parts[0].get(key) is not None:
+                out[key] = np.concatenate([p[key] for p in parts], axis=0)
+    return out

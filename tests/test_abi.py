@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
     # and nothing else is exported under the snip_ prefix
@@ -267,3 +267,28 @@ def test_timing_argument_errors(L):
     n = ctypes.c_int64(-1)
     assert L.snip_timing_read(None, 0, ctypes.byref(n)) == -4     # not started
     assert "not started" in err(L)
+
+
+def test_workspace_size_matches_per_call_sizers(L):
+    """snip_workspace_size(op, M, N, K, format) is each call's own sizer."""
+    for fmt in (S.BF16, S.FP8, S.NVFP4, S.MXFP4):
+        for (T, din, dout) in ((256, 512, 512), (4096, 2048, 256), (4096, 8192, 28672), (240, 2048, 2000)):
+            assert L.snip_workspace_size(S.OP_QUANTIZE, T, din, 0, fmt) == \
+                L.snip_quantize_workspace(T, din, S.ROWWISE, fmt)
+            assert L.snip_workspace_size(S.OP_QGEMM, T, dout, din, fmt) == L.snip_qgemm_workspace(T, dout, din, fmt)
+            assert L.snip_workspace_size(S.OP_LINEAR_FWD, T, dout, din, fmt) == \
+                L.snip_linear_fwd_workspace(T, din, dout, fmt)
+            assert L.snip_workspace_size(S.OP_LINEAR_BWD, T, dout, din, fmt) == \
+                L.snip_linear_bwd_workspace(T, din, dout, fmt, fmt)
+            assert L.snip_workspace_size(S.OP_QUANTIZE_DUAL, T, din, 0, fmt) == \
+                L.snip_quantize_dual_workspace(T, din, fmt)
+            assert L.snip_workspace_size(S.OP_LINEAR_FWD_SAVE, T, dout, din, fmt) == \
+                L.snip_linear_fwd_save_workspace(T, din, dout, fmt)
+            assert L.snip_workspace_size(S.OP_LINEAR_BWD_SAVED, T, dout, din, fmt) == \
+                L.snip_linear_bwd_saved_workspace(T, din, dout, fmt)
+    # a split-K plan needs scratch: the skinny K projection's wgrad
+    assert L.snip_workspace_size(S.OP_QGEMM, 256, 2048, 4096, S.FP8) > 0
+    assert L.snip_workspace_size(S.OP_LINEAR_FWD, 256, 512, 512, S.NVFP4) > 0
+    assert L.snip_workspace_size(7, 256, 512, 512, S.NVFP4) == 0
+    assert L.snip_workspace_size(-1, 256, 512, 512, S.NVFP4) == 0
+    assert L.snip_workspace_size(S.OP_QGEMM, 0, 512, 512, S.NVFP4) == 0

@@ -89,15 +89,17 @@ def test_gemm_ldc_interior_tiles(fmt, M, N, ldc):
     check_gemm(h[:, :N].astype(np.float64), oa["xhat"], ob["xhat"], what=f"ldc interior fmt={fmt} {M}x{N}")
 
 
-# Shapes that make the planner pick each kernel and tile: FP8 256x128,
-# 256x256 for NVFP4, MX-FP4 and BF16, the register-staged 128x128 kernel for
-# MX-FP4 and BF16, and the LDS-DMA 128x128 kernel for NVFP4 / FP8 -- all
+# Shapes that make the planner pick each kernel and tile: 256x128 for FP8
+# and NVFP4, 256x256 for FP8, MX-FP4 and BF16 (the planner never gives NVFP4
+# 256x256 tiles), the register-staged 128x128 kernel for MX-FP4 and BF16, the
+# LDS-DMA 128x128 kernel for NVFP4 / FP8 and the 64x64 skinny tiles -- all
 # with ragged M and N. Sampled output rows (all columns) against the oracle.
 PLAN_CASES = [
     (S.FP8, 4000, 5600, 1024),      # 128x128 (256x128 would leave a last round of 192 tiles)
     (S.NVFP4, 8000, 4000, 512),     # 256x128, 2-stage ring
     (S.NVFP4, 4000, 5600, 1024),    # 256x128, 2-stage ring
     (S.FP8, 8000, 4000, 512),       # 256x128
+    (S.FP8, 1500, 35500, 512),      # 256x256 (834 tiles: 256x128 would leave a last round of 132)
     (S.MXFP4, 8000, 4000, 512),     # 256x256
     (S.BF16, 8000, 4000, 256),      # 256x256
     (S.MXFP4, 2000, 1600, 768),     # staged 128x128, 256-element stages

@@ -9,7 +9,8 @@ import torch
 import synth
 import sub_byte_mixed_amd as S
 from oracle import linear as OL
-from parity import TOL, check_gemm, compare_stats, f32, say
+from oracle import quantize as OQ
+from parity import RND, TOL, check_gemm, compare_stats, f32, say
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +97,58 @@ def test_layer_stats_report():
     _, _, st = S.linear_bwd(bad.cuda(), x.cuda(), w.cuda(), S.NVFP4, S.NVFP4, 0, 0)
     reps, nonfinite = S.layer_stats(st)
     assert nonfinite and reps[0]["n_nonfinite"] == 1
+
+
+REPORT_FIELDS = ("rel_mse", "norm_ratio", "below_sqrt3", "amax", "n_nonfinite")
+
+
+def compare_report(g: dict, o: dict, what: str):
+    """One snip_layer_stats record against oracle.linear.report of the
+    oracle's statistics of the same tensor: the ratios within the
+    statistics' 1e-5 bound (two sums -> 2e-5 on rel-MSE, 1e-5 on the norm
+    ratio), the flag, the max and the non-finite count exactly."""
+    assert g["below_sqrt3"] == int(o["below_sqrt3"]), f"{what}: sqrt(3) flag {g['below_sqrt3']} vs {o}"
+    assert g["rel_mse"] == pytest.approx(o["rel_mse"], rel=2e-5, abs=0), f"{what}: rel_mse"
+    if np.isinf(o["norm_ratio"]):
+        assert np.isinf(g["norm_ratio"]), f"{what}: norm ratio"
+    else:
+        assert g["norm_ratio"] == pytest.approx(o["norm_ratio"], rel=1e-5, abs=0), f"{what}: norm ratio"
+    assert g["amax"] == np.float32(o["amax"]), f"{what}: amax"
+    assert g["n_nonfinite"] == o["n_nonfinite"], f"{what}: non-finite"
+
+
+def test_layer_stats_matches_oracle_report():
+    """snip_layer_stats field by field against oracle.linear.report ["FP4 All
+    the Way" summary, Outline: sqrt(3) threshold of gradient norm over
+    quantization noise], on a layer's four backward operands and on a
+    gradient quantized with stale (delayed-scaling) maxima 2^k above its own:
+    the coarser tensor scale pushes the block scales (NVFP4) or the codes
+    (FP8) into the subnormal range until the noise exceeds the signal and
+    the flag turns on."""
+    wl = synth.WORKLOADS["linear512"]
+    x, w, dy = synth.gen_layer(wl, 0)
+    say("layer_stats vs oracle.report: linear512 backward, NVFP4")
+    _, _, st = S.linear_bwd(dy.cuda(), x.cuda(), w.cuda(), S.NVFP4, S.NVFP4, 0, 0)
+    reps, nonfinite = S.layer_stats(st)
+    assert not nonfinite
+    ob = OL.linear_bwd(f32(dy), f32(x), f32(w), S.NVFP4, S.NVFP4, 0, 0)
+    for g, o, n in zip(reps, ob["stats"], ("dY", "W^T", "dY^T", "X^T")):
+        compare_report(g, OL.report(o), f"linear512 {n}")
+    g32 = f32(synth.gen_matrix((256, 512), seed=7, std=1e-3))
+    gd = synth.gen_matrix((256, 512), seed=7, std=1e-3).cuda()
+    A = float(OQ.tensor_amax(g32))
+    flags = set()
+    for fmt in (S.NVFP4, S.FP8):
+        for rnd in (S.RNE, S.SR):
+            for k in (0, 16, 18, 20):
+                say(f"layer_stats stale max case fmt={fmt} rounding={rnd} k={k}")
+                amax = torch.tensor([np.float32(A * 2.0 ** k)], dtype=torch.float32, device="cuda")
+                _, st = S.quantize(gd, S.ROWWISE, fmt, rnd, 5, 11, amax=amax)
+                rep, nf = S.layer_stats(st)
+                o = OQ.quantize(g32, fmt, RND[rnd], 5, 11, amax=np.float32(A * 2.0 ** k))
+                compare_report(rep[0], OL.report(o["stats"]), f"fmt={fmt} rnd={rnd} k={k}")
+                flags.add(rep[0]["below_sqrt3"])
+    assert flags == {0, 1}, "the cases must cover both sides of the sqrt(3) threshold"
 
 
 def test_launch_timing_records():

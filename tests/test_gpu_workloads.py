@@ -1,18 +1,23 @@
 """GPU parity at the workloads' full sizes, in both launch configurations:
-the saved-operand calls the benchmark times by default (snip_linear_fwd_save,
-snip_linear_bwd_saved) and the separate calls (snip_linear_fwd, then
-snip_linear_bwd reusing the forward statistics), on sampled outputs the
-oracle can compute one by one:
+the separate calls (snip_linear_fwd, then snip_linear_bwd reusing the
+forward statistics) and the saved-operand calls the benchmark times
+(snip_linear_fwd_save, snip_linear_bwd_saved), on every distinct
+(layer shape, format) of every workload.
 
-  * Y, dX, dW: a seeded sample of output rows x columns against the oracle's
-    fp64 product of the oracle-quantized rows / columns involved (quantized
-    with the full-tensor max and their global element indices), within
-    1e-5 * sum|a||b|;
-  * codes, scales and tensor exponents of every operand (snip_quantize, same
-    tensor ids) bit-exact on the sampled rows;
-  * statistics: max|x| exactly and sum x^2 within 1e-5 on every tensor;
-    sum (Q(x)-x)^2 against the full-tensor oracle where the tensors are small
-    enough for it (TinyLlama-1B block, 512x512 layer).
+For each layer:
+  * the two launch configurations give the same bytes: Y, dX, dW, and the
+    saved W^T / X^T operands equal the separate column-wise passes;
+  * Y, dX, dW against the oracle's fp64 product of the oracle-quantized
+    operands, within 1e-5 * sum|a||b|: every element for the TinyLlama-1B
+    block and the 512x512 layer, a seeded sample of rows x columns (tile
+    edges included) elsewhere;
+  * codes, scales and tensor exponents of all six operands (snip_quantize,
+    same tensor ids) bit-exact: whole tensors for the TinyLlama-1B block and
+    the 512x512 layer, the sampled rows elsewhere;
+  * statistics of all six operands, in both configurations, against the
+    whole-tensor oracle (computed in row chunks with the whole tensor's max):
+    max|x| and the non-finite count exactly, sum x^2 and sum (Q(x)-x)^2
+    within 1e-5.
 """
 import numpy as np
 import pytest
@@ -21,157 +26,153 @@ import torch
 import synth
 import sub_byte_mixed_amd as S
 from oracle import quantize as OQ
-from parity import TOL, check_gemm, compare_codes, compare_stats, gpu_codes, say
+from parity import RND, TOL, check_gemm, compare_codes, compare_stats, gpu_codes, oracle_chunked, say
 
 pytestmark = pytest.mark.gpu
-
-RND = {S.RNE: "rne", S.SR: "sr"}
 
 
 def sample(n, k, seed):
     rng = np.random.default_rng(seed)
     idx = set(rng.choice(n, size=min(k, n), replace=False).tolist())
     idx.update({0, n - 1})
+    for edge in (63, 64, 127, 128, 255, 256):          # tile edges of the 64/128/256 tiles
+        if edge < n:
+            idx.add(edge)
     return np.array(sorted(idx))
 
 
-def oracle_rows(t32, amax, fmt, rnd, seed, tid, rows):
-    """Oracle quantization of the given rows of a row-wise operand (amax: the
-    whole tensor's max, as the device computes it)."""
-    return OQ.quantize(t32[rows], fmt, RND[rnd], seed, tid, amax=amax, row_ids=rows)
+# The six quantized operands of a layer: (name, source, layout, rounding, role).
+OPERANDS = (("X", "x", S.ROWWISE, S.RNE, 0), ("W", "w", S.ROWWISE, S.RNE, 1),
+            ("dY", "dy", S.ROWWISE, S.SR, 2), ("W^T", "w", S.COLWISE, S.SR, 3),
+            ("dY^T", "dy", S.COLWISE, S.SR, 4), ("X^T", "x", S.COLWISE, S.SR, 5))
 
 
-def oracle_cols(t32, amax, fmt, rnd, seed, tid, cols):
-    """Oracle quantization of the given columns of a column-wise operand
-    (rows of the transposed output)."""
-    return OQ.quantize_colwise(t32, fmt, RND[rnd], seed, tid, amax=amax, col_ids=cols)
-
-
-def run_layer(wl, li, fmt, seed=0, full_stats=False, n_rows=8, n_cols=48, fused=False):
-    """fused: the saved-operand calls the benchmark times by default
-    (snip_linear_fwd_save, snip_linear_bwd_saved: X, W, dY read once)."""
+def run_layer(wl, li, fmt, seed=0, full=False, n_rows=8, n_cols=48, stats=True):
+    """full: every output element and every code against the oracle (small
+    workloads); otherwise sampled rows x columns. stats: every operand's
+    statistics against the whole-tensor oracle."""
     layer = wl.layers[li]
     T, din, dout = wl.tokens, layer.d_in, layer.d_out
-    say(f"workload {wl.name} layer {layer.name} ({din}->{dout}, T={T}) fmt={fmt} seed={seed} fused={fused}")
+    say(f"workload {wl.name} layer {layer.name} ({din}->{dout}, T={T}) fmt={fmt} seed={seed} full={full}")
     x, w, dy = synth.gen_layer(wl, li)
     xd, wd, dyd = x.cuda(), w.cuda(), dy.cuda()
-    saved = None
-    if fused:
-        y, saved, st_f4 = S.linear_fwd_save(xd, wd, fmt, seed, li)
-        dx, dw, st_b2 = S.linear_bwd_saved(dyd, saved, seed, li)
-        st_f, st_b = st_f4, st_b2
-    else:
-        y, st_f = S.linear_fwd(xd, wd, fmt, seed, li)
-        dx, dw, st_b = S.linear_bwd(dyd, xd, wd, fmt, fmt, seed, li, fwd_stats=st_f)
-    torch.cuda.synchronize()
-    x32, w32, dy32 = (synth.bf16_to_f32(t) for t in (x, w, dy))
-    ax, aw, ady = (OQ.tensor_amax(t) for t in (x32, w32, dy32))
-
-    rT = sample(T, n_rows, 1000 + li)
-    rin = sample(din, n_cols, 2000 + li)
-    rout = sample(dout, n_cols, 3000 + li)
     tid = lambda role: 8 * li + role
-    # forward: Y[rT, rout]
-    qx = oracle_rows(x32, ax, fmt, S.RNE, seed, tid(0), rT)
-    qw = oracle_rows(w32, aw, fmt, S.RNE, seed, tid(1), rout)
-    check_gemm(y[rT][:, rout].cpu().numpy().astype(np.float64), qx["xhat"], qw["xhat"],
-               what=f"{wl.name}/{layer.name} Y")
-    # dgrad: dX[rT, rin] = Q(dY)[rT] . Q(W^T)[rin]^T
-    qdy = oracle_rows(dy32, ady, fmt, S.SR, seed, tid(2), rT)
-    qwt = oracle_cols(w32, aw, fmt, S.SR, seed, tid(3), rin)
-    check_gemm(dx[rT][:, rin].cpu().numpy().astype(np.float64), qdy["xhat"], qwt["xhat"],
-               what=f"{wl.name}/{layer.name} dX")
-    # wgrad: dW[rout, rin] = Q(dY^T)[rout] . Q(X^T)[rin]^T
-    qdyt = oracle_cols(dy32, ady, fmt, S.SR, seed, tid(4), rout)
-    qxt = oracle_cols(x32, ax, fmt, S.SR, seed, tid(5), rin)
-    check_gemm(dw[rout][:, rin].cpu().numpy().astype(np.float64), qdyt["xhat"], qxt["xhat"],
-               what=f"{wl.name}/{layer.name} dW")
 
-    # codes of every operand on the sampled rows (bf16 has none)
-    if saved is not None:                   # the saved backward operands themselves
-        compare_codes(gpu_codes(saved.wt), qwt, fmt, rows=rin, what=f"{wl.name}/{layer.name} saved W^T")
-        compare_codes(gpu_codes(saved.xt), qxt, fmt, rows=rin, what=f"{wl.name}/{layer.name} saved X^T")
-    if fmt != S.BF16 and saved is None:
-        for src, lay, rnd, role, rows, o in ((xd, S.ROWWISE, S.RNE, 0, rT, qx), (wd, S.ROWWISE, S.RNE, 1, rout, qw),
-                                            (dyd, S.ROWWISE, S.SR, 2, rT, qdy), (wd, S.COLWISE, S.SR, 3, rin, qwt),
-                                            (dyd, S.COLWISE, S.SR, 4, rout, qdyt), (xd, S.COLWISE, S.SR, 5, rin, qxt)):
-            q, _ = S.quantize(src, lay, fmt, rnd, seed, tid(role), with_stats=False)
-            torch.cuda.synchronize()
-            compare_codes(gpu_codes(q), o, fmt, rows=rows, what=f"{wl.name}/{layer.name} role {role}")
-            del q
+    # ---- the separate calls, then the saved-operand calls
+    y, st_f = S.linear_fwd(xd, wd, fmt, seed, li)
+    dx, dw, st_b = S.linear_bwd(dyd, xd, wd, fmt, fmt, seed, li, fwd_stats=st_f)
+    fused = fmt != S.BF16
+    if fused:
+        y2, saved, st_f4 = S.linear_fwd_save(xd, wd, fmt, seed, li)
+        dx2, dw2, st_b2 = S.linear_bwd_saved(dyd, saved, seed, li)
+    torch.cuda.synchronize()
+    if fused:
+        for a, b, n in ((y, y2, "Y"), (dx, dx2, "dX"), (dw, dw2, "dW")):
+            assert torch.equal(a, b), f"{wl.name}/{layer.name}: {n} differs between the launch configurations"
+        del y2, dx2, dw2
 
-    # statistics
-    gf, gb = S.decode_stats(st_f), S.decode_stats(st_b)
-    tensors = {"X": (x32, ax), "W": (w32, aw), "dY": (dy32, ady)}
-    sums = {n: float(np.einsum("ij,ij->", t.astype(np.float64), t.astype(np.float64)))
-            for n, (t, _) in tensors.items()}
-    names_f, names_b = (["X", "W", "W", "X"], ["dY", "dY"]) if fused else (["X", "W"], ["dY", "W", "dY", "X"])
-    for g, n in list(zip(gf, names_f)) + list(zip(gb, names_b)):
-        assert g["amax"] == float(tensors[n][1]), f"{n} amax"
-        sx2 = sums[n]
-        assert abs(g["sum_x2"] - sx2) <= TOL * sx2, f"{n} sum_x2 {g['sum_x2']} vs {sx2}"
-        assert g["n_nonfinite"] == 0
-    if full_stats and not fused:
-        ref = [OQ.quantize(x32, fmt, "rne", seed, tid(0))["stats"],
-               OQ.quantize(w32, fmt, "rne", seed, tid(1))["stats"]]
-        for g, o, n in zip(gf, ref, names_f):
-            compare_stats(g, o, what=f"{wl.name}/{layer.name} fwd {n}")
-        ref = [OQ.quantize(dy32, fmt, "sr", seed, tid(2))["stats"],
-               OQ.quantize_colwise(w32, fmt, "sr", seed, tid(3))["stats"],
-               OQ.quantize_colwise(dy32, fmt, "sr", seed, tid(4))["stats"],
-               OQ.quantize_colwise(x32, fmt, "sr", seed, tid(5))["stats"]]
-        for g, o, n in zip(gb, ref, ["dY", "W^T", "dY^T", "X^T"]):
-            compare_stats(g, o, what=f"{wl.name}/{layer.name} bwd {n}")
-    del xd, wd, dyd, y, dx, dw, saved
+    # ---- quantized operands through snip_quantize (same tensor ids)
+    src = {"x": xd, "w": wd, "dy": dyd}
+    gq = {}
+    if fmt != S.BF16:
+        for name, s_, lay, rnd, role in OPERANDS:
+            q, _ = S.quantize(src[s_], lay, fmt, rnd, seed, tid(role), with_stats=False)
+            gq[name] = q
+        torch.cuda.synchronize()
+        for name, q in (("W^T", saved.wt), ("X^T", saved.xt)):
+            assert torch.equal(q.codes, gq[name].codes), f"{wl.name}/{layer.name}: saved {name} codes"
+            if q.scales is not None:
+                assert torch.equal(q.scales, gq[name].scales), f"{wl.name}/{layer.name}: saved {name} scales"
+            assert torch.equal(q.texp, gq[name].texp), f"{wl.name}/{layer.name}: saved {name} exponent"
+
+    # ---- oracle operands: whole tensors (full) or the sampled rows
+    x32, w32, dy32 = (synth.bf16_to_f32(t) for t in (x, w, dy))
+    t32 = {"x": x32, "w": w32, "dy": dy32}
+    amax = {k: OQ.tensor_amax(v) for k, v in t32.items()}
+    rT, rin, rout = (np.arange(T), np.arange(din), np.arange(dout)) if full else (
+        sample(T, n_rows, 1000 + li), sample(din, n_cols, 2000 + li), sample(dout, n_cols, 3000 + li))
+    sel = {"X": rT, "W": rout, "dY": rT, "W^T": rin, "dY^T": rout, "X^T": rin}
+    oq, ostats = {}, {}
+    for name, s_, lay, rnd, role in OPERANDS:
+        if full or stats:
+            o = oracle_chunked(t32[s_], fmt, lay, rnd, seed, tid(role), amax=amax[s_], keep=full)
+            ostats[name] = o["stats"]
+            if full:
+                oq[name] = o
+        if not full:
+            rows = sel[name]
+            if lay == S.ROWWISE:
+                oq[name] = OQ.quantize(t32[s_][rows], fmt, RND[rnd], seed, tid(role), amax=amax[s_], row_ids=rows)
+            else:
+                oq[name] = OQ.quantize_colwise(t32[s_], fmt, RND[rnd], seed, tid(role), amax=amax[s_], col_ids=rows)
+
+    # ---- codes
+    for name, q in gq.items():
+        compare_codes(gpu_codes(q), oq[name], fmt, rows=None if full else sel[name],
+                      what=f"{wl.name}/{layer.name} {name}")
+    del gq
+
+    # ---- GEMMs
+    def pick(t, r, c):
+        return (t if full else t[r][:, c]).cpu().numpy().astype(np.float64)
+    check_gemm(pick(y, rT, rout), oq["X"]["xhat"], oq["W"]["xhat"], what=f"{wl.name}/{layer.name} Y")
+    check_gemm(pick(dx, rT, rin), oq["dY"]["xhat"], oq["W^T"]["xhat"], what=f"{wl.name}/{layer.name} dX")
+    check_gemm(pick(dw, rout, rin), oq["dY^T"]["xhat"], oq["X^T"]["xhat"], what=f"{wl.name}/{layer.name} dW")
+
+    # ---- statistics of both launch configurations
+    gsep = dict(zip(["X", "W", "dY", "W^T", "dY^T", "X^T"], S.decode_stats(st_f) + S.decode_stats(st_b)))
+    gfus = dict(zip(["X", "W", "W^T", "X^T", "dY", "dY^T"],
+                    S.decode_stats(st_f4) + S.decode_stats(st_b2))) if fused else {}
+    for name, s_, *_ in OPERANDS:
+        for cfg, g in (("separate", gsep), ("saved-operand", gfus)):
+            if name not in g:
+                continue
+            if ostats:
+                compare_stats(g[name], ostats[name], what=f"{wl.name}/{layer.name} {cfg} {name}")
+            else:
+                assert g[name]["amax"] == float(amax[s_]) and g[name]["n_nonfinite"] == 0
+    del xd, wd, dyd, y, dx, dw
     torch.cuda.empty_cache()
+
+
+def layer_index(wl, name):
+    return [l.name for l in wl.layers].index(name)
 
 
 def test_linear512_full():
     wl = synth.WORKLOADS["linear512"]
-    run_layer(wl, 0, wl.plan[0], full_stats=True, n_rows=64, n_cols=128)
+    run_layer(wl, 0, wl.plan[0], full=True)
 
 
 @pytest.mark.parametrize("li", range(7))
-def test_tinyllama1b_block(li):
+def test_tinyllama1b_block_full(li):
+    """Every layer of the TinyLlama-1B block, in its plan format: every
+    output element and every code, in both launch configurations."""
     wl = synth.WORKLOADS["tinyllama1b"]
-    run_layer(wl, li, wl.plan[li], full_stats=True)
+    run_layer(wl, li, wl.plan[li], full=True)
 
 
-@pytest.mark.parametrize("name", ["Q", "V", "Down"])
+# Llama-7B: one layer per distinct (shape, format): Q/K 4096->4096 NVFP4,
+# V/O 4096->4096 FP8, Gate/Up 4096->11008 NVFP4, Down 11008->4096 NVFP4.
+@pytest.mark.parametrize("name", ["Q", "V", "Gate", "Down"])
 def test_llama7b_block(name):
     wl = synth.WORKLOADS["llama7b"]
-    li = [l.name for l in wl.layers].index(name)
+    li = layer_index(wl, name)
     run_layer(wl, li, wl.plan[li])
 
 
-@pytest.mark.parametrize("name", ["K", "Gate"])
+# Llama-70B (all NVFP4): Q/O 8192->8192, K/V 8192->1024, Gate/Up
+# 8192->28672, Down 28672->8192 (K = 28672 in the forward GEMM).
+@pytest.mark.parametrize("name", ["Q", "K", "Gate", "Down"])
 def test_llama70b_block(name):
     wl = synth.WORKLOADS["llama70b"]
-    li = [l.name for l in wl.layers].index(name)
+    li = layer_index(wl, name)
     run_layer(wl, li, wl.plan[li])
 
 
 @pytest.mark.parametrize("fmt", [S.BF16, S.FP8, S.NVFP4, S.MXFP4])
 def test_down7b_precision_sweep(fmt):
+    """The 7B Down projection at T = 16384 in each format of the sweep (seed
+    = format id: the sweep's seeds differ per run)."""
     wl = synth.WORKLOADS["down7b_sweep"]
     run_layer(wl, 0, fmt, seed=fmt)
-
-
-@pytest.mark.parametrize("li", range(7))
-def test_tinyllama1b_block_fused(li):
-    """The benchmark's launch configuration: saved-operand calls."""
-    wl = synth.WORKLOADS["tinyllama1b"]
-    run_layer(wl, li, wl.plan[li], fused=True)
-
-
-@pytest.mark.parametrize("name", ["V", "Down"])
-def test_llama7b_block_fused(name):
-    wl = synth.WORKLOADS["llama7b"]
-    li = [l.name for l in wl.layers].index(name)
-    run_layer(wl, li, wl.plan[li], fused=True)
-
-
-def test_llama70b_block_fused():
-    wl = synth.WORKLOADS["llama70b"]
-    li = [l.name for l in wl.layers].index("K")
-    run_layer(wl, li, wl.plan[li], fused=True)
