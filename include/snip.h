@@ -320,6 +320,41 @@ int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qte
                           const float* amax_dy, float* dx, float* dw, snip_stats* stats2,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* ---- allocation-free forward ------------------------------------------- */
+
+/* Bytes of the static device scratch array behind
+ * snip_linear_fwd_save_noalloc (held on every GPU the library runs on until
+ * the process ends). */
+#define SNIP_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* snip_linear_fwd_save without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving or training loops, harnesses that forbid hipMalloc): the
+ * quantized row-wise X and W, the tensor-max and statistics partials and
+ * any split-K partials live in the library's static scratch array instead
+ * of a caller workspace. Same arguments (minus ws, ws_bytes), same results
+ * byte for byte as snip_linear_fwd_save. Allocates nothing: no hipMalloc,
+ * no allocating library call.
+ *   Limit      the layer's workspace (snip_linear_fwd_save_workspace) must
+ *              fit in SNIP_NOALLOC_SCRATCH_BYTES, else SNIP_E_WORKSPACE
+ *              (checked before any HIP call). Layers up to the
+ *              TinyLlama-1B shapes (T = 4096, 2048 -> 5632) fit.
+ *   Sharing    every call on one GPU uses that GPU's one array, whose
+ *              contents the last call leaves behind (nothing in it needs
+ *              initialising: each call writes before it reads). Calls that
+ *              overlap in time on one GPU (other streams, other threads)
+ *              race on it and must be serialised by the caller.
+ *   Set-up     the first call on a device looks up the array's device
+ *              address there (hipGetSymbolAddress, with that device
+ *              current); make it outside graph capture.
+ *   stream     its device is the one whose array is used.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE (layer too large), HIP. */
+int snip_linear_fwd_save_noalloc(const void* x, const void* w, int64_t T, int64_t in, int64_t out,
+                                 int format, uint64_t seed, uint32_t layer_id,
+                                 const float* amax_x, const float* amax_w, float* y,
+                                 const snip_qtensor* wt, const snip_qtensor* xt, snip_stats* stats4,
+                                 void* stream);
+
 /* Synchronise `stream`, copy n device statistics records to the host and
  * derive the report of each. [SNIP, Abstract] (statistics for the precision
  * decision); [FP4 All the Way, Outline] (sqrt(3) threshold).

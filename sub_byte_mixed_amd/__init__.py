@@ -105,6 +105,10 @@ _SIGS = {
                                         _c.c_int, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
                                         _c.c_void_p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
                                         _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "snip_linear_fwd_save_noalloc": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64,
+                                                _c.c_int, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
+                                                _c.c_void_p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
+                                                _c.c_void_p, _c.c_void_p]),
     "snip_linear_bwd_saved": (_c.c_int, [_c.c_void_p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
                                          _c.c_int64, _c.c_int64, _c.c_int64, _c.c_uint64, _c.c_uint32,
                                          _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
@@ -379,6 +383,34 @@ def linear_fwd_save(x: torch.Tensor, w: torch.Tensor, fmt: int, seed: int = 0, l
                                   _amax_ptr(amax_w), _ptr(y),
                                   ctypes.byref(dwt), ctypes.byref(dxt), _ptr(stats), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+    return y, saved, stats
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # SNIP_NOALLOC_SCRATCH_BYTES
+
+
+def linear_fwd_save_noalloc(x: torch.Tensor, w: torch.Tensor, fmt: int, seed: int = 0, layer_id: int = 0,
+                            y: Optional[torch.Tensor] = None, saved: Optional[SavedOperands] = None,
+                            stats: Optional[torch.Tensor] = None, with_stats: bool = True, stream=None,
+                            amax_x=None, amax_w=None):
+    """snip_linear_fwd_save_noalloc: linear_fwd_save with the library's
+    static scratch array as its workspace (the call allocates nothing; the
+    outputs y, saved and stats are the caller's). Returns (y, saved, stats)."""
+    _require_cuda_bf16(x, "x")
+    _require_cuda_bf16(w, "w")
+    L = lib()
+    T, din = x.shape
+    dout = w.shape[0]
+    if y is None:
+        y = torch.empty((T, dout), dtype=torch.float32, device=x.device)
+    if saved is None:
+        saved = SavedOperands(fmt, T, din, dout, x.device)
+    if stats is None and with_stats:
+        stats = new_stats(4, x.device)
+    dwt, dxt = saved.wt.desc(), saved.xt.desc()
+    _check(L.snip_linear_fwd_save_noalloc(_ptr(x), _ptr(w), T, din, dout, fmt, seed, layer_id, _amax_ptr(amax_x),
+                                          _amax_ptr(amax_w), _ptr(y), ctypes.byref(dwt), ctypes.byref(dxt),
+                                          _ptr(stats), _stream(stream)))
     return y, saved, stats
 
 

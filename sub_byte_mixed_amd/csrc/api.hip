@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -971,36 +972,50 @@ int snip_quantize_dual(const void* x, int64_t rows, int64_t cols, int64_t ld, in
   return ok();
 }
 
-int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, int64_t out, int format,
-                         uint64_t seed, uint32_t layer_id, const float* amax_x, const float* amax_w, float* y,
-                         const snip_qtensor* wt, const snip_qtensor* xt, snip_stats* stats4, void* ws,
-                         size_t ws_bytes, void* stream) {
-  if (!x || !w || !y) return fail(SNIP_E_NULL, "snip_linear_fwd_save: x, w and y must be non-NULL");
+}  // extern "C"
+
+namespace {
+
+// snip_linear_fwd_save and its allocation-free variant. `who` names the entry
+// point in error messages; check_only: validate every argument (all on the
+// host: no HIP call) and return; noalloc: the workspace is the library's
+// static scratch array (its size is the one that must fit).
+int linear_fwd_save_impl(const char* who, const void* x, const void* w, int64_t T, int64_t in, int64_t out,
+                         int format, uint64_t seed, uint32_t layer_id, const float* amax_x, const float* amax_w,
+                         float* y, const snip_qtensor* wt, const snip_qtensor* xt, snip_stats* stats4, void* ws,
+                         size_t ws_bytes, void* stream, bool check_only, bool noalloc) {
+  if (!x || !w || !y) return fail(SNIP_E_NULL, "%s: x, w and y must be non-NULL", who);
   if (!dual_format(format))
-    return fail(SNIP_E_FORMAT, "snip_linear_fwd_save: format %d is not NVFP4, FP8_E4M3 or MXFP4", format);
+    return fail(SNIP_E_FORMAT, "%s: format %d is not NVFP4, FP8_E4M3 or MXFP4", who, format);
   if (T <= 0 || in <= 0 || out <= 0 || T % 128 || in % 128 || out % 128)
-    return fail(SNIP_E_SHAPE, "snip_linear_fwd_save: T=%lld in=%lld out=%lld must be positive multiples of 128",
+    return fail(SNIP_E_SHAPE, "%s: T=%lld in=%lld out=%lld must be positive multiples of 128", who,
                 (long long)T, (long long)in, (long long)out);
-  int rc = gemm_operands_fit(format, T, out, in, "snip_linear_fwd_save");
-  if (!rc) rc = gemm_operands_fit(format, T, in, out, "snip_linear_fwd_save (saved for dgrad)");
-  if (!rc) rc = gemm_operands_fit(format, out, in, T, "snip_linear_fwd_save (saved for wgrad)");
+  int rc = gemm_operands_fit(format, T, out, in, who);
+  if (!rc) rc = gemm_operands_fit(format, T, in, out, who);
+  if (!rc) rc = gemm_operands_fit(format, out, in, T, who);
   if (rc) return rc;
-  rc = validate_qtensor(wt, "snip_linear_fwd_save: wt");
+  char what[160];
+  std::snprintf(what, sizeof(what), "%s: wt", who);
+  rc = validate_qtensor(wt, what);
   if (rc) return rc;
-  rc = validate_qtensor(xt, "snip_linear_fwd_save: xt");
+  std::snprintf(what, sizeof(what), "%s: xt", who);
+  rc = validate_qtensor(xt, what);
   if (rc) return rc;
   if (wt->format != format || xt->format != format)
-    return fail(SNIP_E_FORMAT, "snip_linear_fwd_save: wt/xt formats (%d, %d) != format %d", wt->format,
-                xt->format, format);
+    return fail(SNIP_E_FORMAT, "%s: wt/xt formats (%d, %d) != format %d", who, wt->format, xt->format, format);
   if (wt->rows != in || wt->k != out || xt->rows != in || xt->k != T)
-    return fail(SNIP_E_SHAPE, "snip_linear_fwd_save: wt must be [%lld][%lld] and xt [%lld][%lld]", (long long)in,
+    return fail(SNIP_E_SHAPE, "%s: wt must be [%lld][%lld] and xt [%lld][%lld]", who, (long long)in,
                 (long long)out, (long long)in, (long long)T);
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || !aligned(stats4, 8) || !aligned(ws, 16) ||
       !aligned(amax_x, 4) || !aligned(amax_w, 4))
-    return fail(SNIP_E_ALIGN, "snip_linear_fwd_save: misaligned pointer");
+    return fail(SNIP_E_ALIGN, "%s: misaligned pointer", who);
   const size_t need = snip_linear_fwd_save_workspace(T, in, out, format);
-  if (!ws || ws_bytes < need)
-    return fail(SNIP_E_WORKSPACE, "snip_linear_fwd_save: workspace of %zu bytes needed", need);
+  if (noalloc && need > ws_bytes)
+    return fail(SNIP_E_WORKSPACE, "%s: this layer needs %zu bytes of scratch, more than the %zu bytes of the "
+                "library's static scratch array; use snip_linear_fwd_save with a caller workspace", who, need,
+                ws_bytes);
+  if (!ws || ws_bytes < need) return fail(SNIP_E_WORKSPACE, "%s: workspace of %zu bytes needed", who, need);
+  if (check_only) return SNIP_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carver cv(ws);
@@ -1070,6 +1085,77 @@ int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, in
   rc = gemm_q(qx.t, qw.t, y, out, split, s, &fin);
   if (rc) return rc;
   return ok();
+}
+
+// ---------------------------------------------------------------- static scratch
+// Scratch of the allocation-free entry point: device memory the library
+// holds on every GPU it runs on until the process ends. In host code
+// `scratch` names a host-side stand-in, not a device address: its device
+// address on each GPU comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = SNIP_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch granularity");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream` (the
+// current device for the null stream).
+int scratch_for(hipStream_t stream, void** out) {
+  int dev = 0;
+  int rc = stream ? hip_check(hipStreamGetDevice(stream, &dev), "hipStreamGetDevice")
+                  : hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(SNIP_E_HIP, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = 0;
+    if ((rc = hip_check(hipGetDevice(&cur), "hipGetDevice"))) return rc;
+    if (cur != dev && (rc = hip_check(hipSetDevice(dev), "hipSetDevice"))) return rc;
+    void* p = nullptr;
+    rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (cur != dev) {
+      const int rc2 = hip_check(hipSetDevice(cur), "hipSetDevice");
+      if (!rc) rc = rc2;
+    }
+    if (rc) return rc;
+    if (!p || !aligned(p, 256)) return fail(SNIP_E_HIP, "scratch array at a bad device address %p", p);
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return SNIP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int snip_linear_fwd_save(const void* x, const void* w, int64_t T, int64_t in, int64_t out, int format,
+                         uint64_t seed, uint32_t layer_id, const float* amax_x, const float* amax_w, float* y,
+                         const snip_qtensor* wt, const snip_qtensor* xt, snip_stats* stats4, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return linear_fwd_save_impl("snip_linear_fwd_save", x, w, T, in, out, format, seed, layer_id, amax_x, amax_w,
+                              y, wt, xt, stats4, ws, ws_bytes, stream, false, false);
+}
+
+int snip_linear_fwd_save_noalloc(const void* x, const void* w, int64_t T, int64_t in, int64_t out, int format,
+                                 uint64_t seed, uint32_t layer_id, const float* amax_x, const float* amax_w,
+                                 float* y, const snip_qtensor* wt, const snip_qtensor* xt, snip_stats* stats4,
+                                 void* stream) {
+  const char* who = "snip_linear_fwd_save_noalloc";
+  // every argument, the scratch size included, is checked before any HIP
+  // call (a 256-aligned stand-in marks the workspace as present)
+  void* const present = reinterpret_cast<void*>(uintptr_t(256));
+  int rc = linear_fwd_save_impl(who, x, w, T, in, out, format, seed, layer_id, amax_x, amax_w, y, wt, xt, stats4,
+                                present, kScratchBytes, stream, true, true);
+  if (rc) return rc;
+  void* p = nullptr;
+  rc = scratch_for(static_cast<hipStream_t>(stream), &p);
+  if (rc) return rc;
+  return linear_fwd_save_impl(who, x, w, T, in, out, format, seed, layer_id, amax_x, amax_w, y, wt, xt, stats4, p,
+                              kScratchBytes, stream, false, true);
 }
 
 int snip_linear_bwd_saved(const void* dy, const snip_qtensor* wt, const snip_qtensor* xt, int64_t T,

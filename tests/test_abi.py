@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     # and nothing else is exported under the snip_ prefix
@@ -292,3 +292,25 @@ def test_workspace_size_matches_per_call_sizers(L):
     assert L.snip_workspace_size(7, 256, 512, 512, S.NVFP4) == 0
     assert L.snip_workspace_size(-1, 256, 512, 512, S.NVFP4) == 0
     assert L.snip_workspace_size(S.OP_QGEMM, 0, 512, 512, S.NVFP4) == 0
+
+
+def test_noalloc_validates_before_any_hip_call(L):
+    """The allocation-free forward checks every argument, the size of the
+    static scratch included, before its first HIP call (fake device
+    addresses below are never touched)."""
+    d_wt = S.QTensorDesc(S.NVFP4, 0, 4096, 11008, P2, P3, P3 + 4096)
+    d_xt = S.QTensorDesc(S.NVFP4, 0, 4096, 8192, P2, P3, P3 + 4096)
+    rc = L.snip_linear_fwd_save_noalloc(P, P, 8192, 4096, 11008, S.NVFP4, 0, 0, None, None, P,
+                                        ctypes.byref(d_wt), ctypes.byref(d_xt), None, None)
+    assert rc == -5
+    assert b"static scratch" in L.snip_last_error()
+    assert L.snip_linear_fwd_save_workspace(8192, 4096, 11008, S.NVFP4) > S.NOALLOC_SCRATCH_BYTES
+    rc = L.snip_linear_fwd_save_noalloc(P, None, 256, 512, 512, S.NVFP4, 0, 0, None, None, P,
+                                        ctypes.byref(d_wt), ctypes.byref(d_xt), None, None)
+    assert rc == -1
+    rc = L.snip_linear_fwd_save_noalloc(P, P, 256, 500, 512, S.NVFP4, 0, 0, None, None, P,
+                                        ctypes.byref(d_wt), ctypes.byref(d_xt), None, None)
+    assert rc == -2
+    rc = L.snip_linear_fwd_save_noalloc(P, P, 256, 512, 512, S.BF16, 0, 0, None, None, P,
+                                        ctypes.byref(d_wt), ctypes.byref(d_xt), None, None)
+    assert rc == -4
