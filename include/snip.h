@@ -203,6 +203,32 @@ int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld,
 int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t ldc,
                void* ws, size_t ws_bytes, void* stream);
 
+/* GEMM whose output is also quantized in the same launch: c = A . B^T as
+ * snip_qgemm, and the row-wise quantization of c (blocks along N) in
+ * out->format, as snip_quantize(..., SNIP_ROWWISE, out->format, rounding,
+ * seed, tensor_id, amax_in, ...) would quantize a tensor holding c's fp32
+ * values: the layer output becomes the next GEMM's quantized operand
+ * without another read of it. [SNIP, Fig. 5]: a linear layer's output is
+ * the input of the next layer; [FP4 All the Way, Outline]: forward
+ * operands with nearest rounding, gradients with stochastic rounding.
+ *   a, b, c, ldc  as snip_qgemm; a and b are FP8_E4M3 or NVFP4; ldc % 4 == 0.
+ *   rounding      SNIP_RNE or SNIP_SR (Philox stream seed / tensor_id,
+ *                 element index row * N + col).
+ *   amax_in       device float, required: the tensor max that sets the
+ *                 tensor scale (delayed scaling: c's own max is known only
+ *                 after the launch; stats->amax reports it for the next call).
+ *                 Values beyond it saturate.
+ *   out           host descriptor, format NVFP4 or FP8_E4M3, rows = M,
+ *                 k = N; N % 16 == 0.
+ *   stats         device snip_stats or NULL: Sum (Q(c) - c)^2, Sum c^2,
+ *                 max|c| and the non-finite count of c.
+ *   ws            device, snip_qgemm_qout_workspace() bytes.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, WORKSPACE, HIP. */
+int snip_qgemm_qout(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t ldc,
+                    int rounding, uint64_t seed, uint32_t tensor_id, const float* amax_in,
+                    const snip_qtensor* out, snip_stats* stats, void* ws, size_t ws_bytes,
+                    void* stream);
+
 /* ---- quantized linear layer --------------------------------------------- */
 
 /* Forward: y[T][out] (fp32) = Q_rne(x) . Q_rne(w)^T. [SNIP, Fig. 5];
@@ -375,6 +401,8 @@ size_t snip_linear_bwd_workspace(int64_t T, int64_t in, int64_t out,
 size_t snip_quantize_dual_workspace(int64_t rows, int64_t cols, int format);
 size_t snip_linear_fwd_save_workspace(int64_t T, int64_t in, int64_t out, int format);
 size_t snip_linear_bwd_saved_workspace(int64_t T, int64_t in, int64_t out, int format);
+/* format: the operands' format (the output format does not change it). */
+size_t snip_qgemm_qout_workspace(int64_t M, int64_t N, int64_t K, int format);
 
 /* Workspace bytes of any of the calls above, by operation code: the one
  * sizing entry of the boundary, equal to the per-call helper of that call.
@@ -389,6 +417,7 @@ size_t snip_linear_bwd_saved_workspace(int64_t T, int64_t in, int64_t out, int f
 #define SNIP_OP_QUANTIZE_DUAL     4  /* M = rows, N = cols                       */
 #define SNIP_OP_LINEAR_FWD_SAVE   5  /* M = T, N = out, K = in                    */
 #define SNIP_OP_LINEAR_BWD_SAVED  6  /* M = T, N = out, K = in                    */
+#define SNIP_OP_QGEMM_QOUT        7  /* M, N, K as SNIP_OP_QGEMM                 */
 size_t snip_workspace_size(int op, int64_t M, int64_t N, int64_t K, int format);
 
 /* Bytes of one part of a quantized operand: part 0 = codes, 1 = scales.

@@ -8,6 +8,7 @@ the C entry points (include/snip.h):
 
   quantize(x, layout, fmt, rounding, ...)  -> QuantizedTensor, stats
   qgemm(a, b)                              -> fp32 [M, N]
+  qgemm_qout(a, b, out_fmt, amax, ...)     -> fp32 [M, N], its row-wise quantization, stats
   linear_fwd(x, w, fmt, ...)               -> y, stats[2]
   linear_bwd(dy, x, w, fmt_d, fmt_w, ...)  -> dx, dw, stats[4]
   quantize_dual(x, fmt, rnd_row, rnd_col, ...)  -> row-wise, column-wise, stats[2]
@@ -37,7 +38,7 @@ RNE, SR = 0, 1
 ROWWISE, COLWISE, BOTHWISE = 0, 1, 2
 # operation codes of snip_workspace_size
 (OP_QUANTIZE, OP_QGEMM, OP_LINEAR_FWD, OP_LINEAR_BWD, OP_QUANTIZE_DUAL, OP_LINEAR_FWD_SAVE,
- OP_LINEAR_BWD_SAVED) = range(7)
+ OP_LINEAR_BWD_SAVED, OP_QGEMM_QOUT) = range(8)
 # FP4 design-space variants (quantizer only): E2M1 with another block or scale
 FP4_E4M3_B32, FP4_E8M0_B16, FP4_BF16_B16, FP4_BF16_B32 = 4, 5, 6, 7
 FORMAT_NAMES = {BF16: "bf16", FP8_E4M3: "fp8_e4m3", NVFP4: "nvfp4", MXFP4: "mxfp4",
@@ -113,6 +114,10 @@ _SIGS = {
                                          _c.c_int64, _c.c_int64, _c.c_int64, _c.c_uint64, _c.c_uint32,
                                          _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                          _c.c_size_t, _c.c_void_p]),
+    "snip_qgemm_qout": (_c.c_int, [_c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc), _c.c_void_p, _c.c_int64,
+                                   _c.c_int, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.POINTER(QTensorDesc),
+                                   _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "snip_qgemm_qout_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
     "snip_layer_stats": (_c.c_int, [_c.c_void_p, _c.c_int, _c.POINTER(TensorReport), _c.c_void_p]),
     "snip_quantize_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int, _c.c_int]),
     "snip_qgemm_workspace": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int64, _c.c_int]),
@@ -271,6 +276,31 @@ def qgemm(a: QuantizedTensor, b: QuantizedTensor, out: Optional[torch.Tensor] = 
     _check(L.snip_qgemm(ctypes.byref(da), ctypes.byref(db), _ptr(out), out.stride(0), None, 0,
                         _stream(stream)))
     return out
+
+
+def qgemm_qout(a: QuantizedTensor, b: QuantizedTensor, out_fmt: int, amax, rounding: int = RNE,
+               seed: int = 0, tensor_id: int = 0, c: Optional[torch.Tensor] = None,
+               q: Optional[QuantizedTensor] = None, stats: Optional[torch.Tensor] = None,
+               with_stats: bool = True, stream=None):
+    """snip_qgemm_qout: c fp32 [M, N] = dequant(a) . dequant(b)^T and, from
+    the same launch, q = c quantized row-wise in out_fmt with the tensor
+    scale of the supplied max `amax` (device float32 tensor or StatsAmax).
+    Returns (c, q, stats)."""
+    L = lib()
+    M, N = a.rows, b.rows
+    dev = a.codes.device
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if q is None:
+        q = QuantizedTensor(out_fmt, M, N, dev)
+    if stats is None and with_stats:
+        stats = new_stats(1, dev)
+    ws = _workspace(L.snip_qgemm_qout_workspace(M, N, a.k, a.format), dev)
+    da, db, dq = a.desc(), b.desc(), q.desc()
+    _check(L.snip_qgemm_qout(ctypes.byref(da), ctypes.byref(db), _ptr(c), c.stride(0), rounding, seed, tensor_id,
+                             _amax_ptr(amax), ctypes.byref(dq), _ptr(stats), _ptr(ws), ws.numel(),
+                             _stream(stream)))
+    return c, q, stats
 
 
 def linear_fwd(x: torch.Tensor, w: torch.Tensor, fmt: int, seed: int = 0, layer_id: int = 0,
@@ -462,7 +492,8 @@ def workspace_bytes(op: str, *args) -> int:
             "linear_bwd": L.snip_linear_bwd_workspace,
             "quantize_dual": L.snip_quantize_dual_workspace,
             "linear_fwd_save": L.snip_linear_fwd_save_workspace,
-            "linear_bwd_saved": L.snip_linear_bwd_saved_workspace}[op](*args)
+            "linear_bwd_saved": L.snip_linear_bwd_saved_workspace,
+            "qgemm_qout": L.snip_qgemm_qout_workspace}[op](*args)
 
 
 def version() -> int:

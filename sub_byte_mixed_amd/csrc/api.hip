@@ -516,8 +516,15 @@ size_t snip_workspace_size(int op, int64_t M, int64_t N, int64_t K, int format) 
     case SNIP_OP_QUANTIZE_DUAL: return snip_quantize_dual_workspace(M, N, format);
     case SNIP_OP_LINEAR_FWD_SAVE: return snip_linear_fwd_save_workspace(M, K, N, format);
     case SNIP_OP_LINEAR_BWD_SAVED: return snip_linear_bwd_saved_workspace(M, K, N, format);
+    case SNIP_OP_QGEMM_QOUT: return snip_qgemm_qout_workspace(M, N, K, format);
     default: return 0;
   }
+}
+
+size_t snip_qgemm_qout_workspace(int64_t M, int64_t N, int64_t K, int format) {
+  if (M <= 0 || N <= 0 || K <= 0 || (format != SNIP_FP8_E4M3 && format != SNIP_NVFP4)) return 0;
+  return align_up((size_t)gemm_qout_parts(format, M, N, K) * sizeof(StatPart), kAlign) +
+         align_up(gemm_partial_bytes(format, M, N, K), kAlign);
 }
 
 int snip_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld, int layout, int format,
@@ -628,6 +635,78 @@ int snip_qgemm(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t l
   g.partial = (need > 0 && ws && ws_bytes >= need) ? static_cast<float*>(ws) : nullptr;
   rc = hip_check(launch_gemm(a->format, g, static_cast<hipStream_t>(stream)), "gemm launch");
   if (rc) return rc;
+  return ok();
+}
+
+int snip_qgemm_qout(const snip_qtensor* a, const snip_qtensor* b, float* c, int64_t ldc, int rounding,
+                    uint64_t seed, uint32_t tensor_id, const float* amax_in, const snip_qtensor* out,
+                    snip_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "snip_qgemm_qout";
+  int rc = validate_qtensor(a, "snip_qgemm_qout: a");
+  if (rc) return rc;
+  rc = validate_qtensor(b, "snip_qgemm_qout: b");
+  if (rc) return rc;
+  rc = validate_qtensor(out, "snip_qgemm_qout: out");
+  if (rc) return rc;
+  if (!c || !amax_in) return fail(SNIP_E_NULL, "%s: c and amax_in must be non-NULL", who);
+  if (a->format != b->format || (a->format != SNIP_FP8_E4M3 && a->format != SNIP_NVFP4))
+    return fail(SNIP_E_FORMAT, "%s: operands must both be FP8_E4M3 or NVFP4 (got %d, %d)", who, a->format,
+                b->format);
+  if (out->format != SNIP_FP8_E4M3 && out->format != SNIP_NVFP4)
+    return fail(SNIP_E_FORMAT, "%s: output format %d is not FP8_E4M3 or NVFP4", who, out->format);
+  if (rounding != SNIP_RNE && rounding != SNIP_SR) return fail(SNIP_E_FORMAT, "%s: unknown rounding %d", who, rounding);
+  if (a->k != b->k) return fail(SNIP_E_SHAPE, "%s: K differs (%lld, %lld)", who, (long long)a->k, (long long)b->k);
+  if (a->k % 128) return fail(SNIP_E_SHAPE, "%s: K=%lld not a multiple of 128", who, (long long)a->k);
+  if (b->rows % 16) return fail(SNIP_E_SHAPE, "%s: N=%lld not a multiple of 16", who, (long long)b->rows);
+  if (out->rows != a->rows || out->k != b->rows)
+    return fail(SNIP_E_SHAPE, "%s: out is [%lld][%lld], expected [%lld][%lld]", who, (long long)out->rows,
+                (long long)out->k, (long long)a->rows, (long long)b->rows);
+  if (ldc < b->rows || ldc % 4)
+    return fail(SNIP_E_SHAPE, "%s: ldc=%lld must be >= N=%lld and a multiple of 4", who, (long long)ldc,
+                (long long)b->rows);
+  if (!aligned(c, 16) || !aligned(amax_in, 4) || !aligned(stats, 8) || !aligned(ws, 16))
+    return fail(SNIP_E_ALIGN, "%s: misaligned pointer", who);
+  rc = gemm_operands_fit(a->format, a->rows, b->rows, a->k, who);
+  if (rc) return rc;
+  const int64_t M = a->rows, N = b->rows, K = a->k;
+  const size_t need = snip_qgemm_qout_workspace(M, N, K, a->format);
+  if (!ws || ws_bytes < need) return fail(SNIP_E_WORKSPACE, "%s: workspace of %zu bytes needed", who, need);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  const int64_t nparts = gemm_qout_parts(a->format, M, N, K);
+  StatPart* part = reinterpret_cast<StatPart*>(cv.take((size_t)nparts * sizeof(StatPart)));
+  const size_t split_bytes = gemm_partial_bytes(a->format, M, N, K);
+  float* split = split_bytes ? reinterpret_cast<float*>(cv.take(split_bytes)) : nullptr;
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.a = static_cast<const uint8_t*>(a->codes);
+  g.b = static_cast<const uint8_t*>(b->codes);
+  g.as = static_cast<const uint8_t*>(a->scales);
+  g.bs = static_cast<const uint8_t*>(b->scales);
+  g.ea = a->tensor_exp;
+  g.eb = b->tensor_exp;
+  g.c = c;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ldc = ldc;
+  g.partial = split;
+  g.q = QOut{static_cast<uint8_t*>(out->codes), static_cast<uint8_t*>(out->scales), out->tensor_exp, amax_in,
+             part, seed, tensor_id, out->format, rounding == SNIP_SR ? 1 : 0};
+  rc = hip_check(launch_gemm(a->format, g, s), "gemm launch");
+  if (rc) return rc;
+  if (stats) {
+    FJobs f;
+    std::memset(&f, 0, sizeof(f));
+    f.j[0] = FJob{part, (int32_t)nparts, stats};
+    f.n = 1;
+    const int slot = timing_begin(LaunchTag{SNIP_LAUNCH_FINALIZE, -1, -1, -1, 1.0}, s);
+    const hipError_t e = launch_finalize(f, s);
+    timing_end(slot, s);
+    rc = hip_check(e, "finalize launch");
+    if (rc) return rc;
+  }
   return ok();
 }
 

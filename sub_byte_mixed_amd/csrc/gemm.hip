@@ -131,7 +131,8 @@ constexpr int gemm_min_wgs() {
   return BM * BN > 256 * 128 ? 1 : (FMT == SNIP_NVFP4 && BM == 128 && BN == 128 && S == 2 && UK == 1) ? 3 : 2;
 }
 
-template <int FMT, int BM, int BN, int S, int UK>
+// QO: the epilogue also quantizes C row-wise (store_tile_q; unsplit only).
+template <int FMT, int BM, int BN, int S, int UK, bool QO = false>
 __global__ __launch_bounds__(NT, (gemm_min_wgs<FMT, BM, BN, S, UK>())) void gemm_kernel(GemmArgs g_in) {
   using U = Unit<FMT>;
   constexpr int UE = U::UE, NQ = U::NQ, SB = U::SB;
@@ -390,7 +391,11 @@ __global__ __launch_bounds__(NT, (gemm_min_wgs<FMT, BM, BN, S, UK>())) void gemm
     if constexpr (FMT == SNIP_FP8_E4M3) __builtin_amdgcn_s_setprio(0);
   }
 
-  store_tile<TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, r16, grp);
+  if constexpr (QO) {
+    static_assert(4 * 16 * (TN * 16 + 4) * 4 <= S * STAGE, "output staging fits in the operand ring");
+    store_tile_q<TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, r16, grp, smem);
+  }
+  else store_tile<TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, r16, grp);
 }
 
 // Split-K reduction: C = 2^(ea+eb) * sum over splits, in split order.
@@ -403,6 +408,64 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nspl
     const int64_t row = i / g.N, col = i - row * g.N;
     g.c[row * g.ldc + col] = ldexpf(s, e);
   }
+}
+
+// Split-K reduction that also quantizes C row-wise (QOut): a thread sums
+// and quantizes one 16-element row block at a time (N % 16 == 0), with the
+// row-wise quantizer's block codecs; one statistics partial per workgroup.
+template <int OF, bool SR>
+__global__ __launch_bounds__(256) void splitk_reduce_q_kernel(GemmArgs g, int nsplit) {
+  __shared__ double dred[8];
+  __shared__ uint32_t ured[8];
+  __shared__ float inv_lut[OF == SNIP_NVFP4 ? 128 : 1];
+  if constexpr (OF == SNIP_NVFP4) fill_inv_lut(inv_lut);
+  const QOut& q = g.q;
+  const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
+  const int eS = tensor_exp(*q.amax_in, OF);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *q.texp = eS;
+  const int64_t total = g.M * g.N;
+  const int64_t nblk = total / 16;
+  double e2s = 0.0, x2s = 0.0, x2r = 0.0;
+  uint32_t nf = 0u, amax_bits = 0u;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * 256) {
+    const int64_t i0 = b * 16;
+    const int64_t row = i0 / g.N, col = i0 - row * g.N;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float s = 0.0f;
+      for (int k = 0; k < nsplit; ++k) s += g.partial[k * total + i0 + t];
+      x[t] = ldexpf(s, e);
+      g.c[row * g.ldc + col + t] = x[t];
+    }
+    Words4 d0, d1;
+    if (SR) {
+      d0 = draws8(q.seed, q.tensor_id, (uint64_t)i0 >> 3);
+      d1 = draws8(q.seed, q.tensor_id, ((uint64_t)i0 >> 3) + 1);
+    }
+    float be2, bx2;
+    if constexpr (OF == SNIP_NVFP4) {
+      uint32_t lo, hi, sc;
+      nvfp4_block<SR>(x, eS, d0, d1, inv_lut, lo, hi, sc, be2, bx2);
+      *reinterpret_cast<uint2*>(q.codes + i0 / 2) = make_uint2(lo, hi);
+      q.scales[i0 / 16] = (uint8_t)sc;
+    } else {
+      uint32_t out[4];
+      fp8_chunk<SR>(x, eS, d0, d1, out, be2, bx2);
+      *reinterpret_cast<uint4*>(q.codes + i0) = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+    const bool bad = !(bx2 <= 3.0e38f);
+    uint32_t bnf = 0u, bam = 0u;
+    double rx2 = 0.0;
+    if (bad) nonfinite_stats<16>(x, bnf, rx2, bam);
+    else bam = block_absmax_bits<16>(x);
+    amax_bits = max(amax_bits, bam);
+    nf += bnf;
+    x2r += rx2;
+    e2s += bad ? 0.0 : (double)be2;
+    x2s += bad ? 0.0 : (double)bx2;
+  }
+  wg_store_stats(q.part + blockIdx.x, ldexp(e2s, 2 * eS), ldexp(x2s, 2 * eS) + x2r, nf, amax_bits, dred, ured);
 }
 
 // Host-side plan: kernel, tile shape and K split for a problem.
@@ -506,18 +569,18 @@ size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K) {
 }
 
 // Returns false when the plan names a kernel this format has no instance of.
-template <int FMT>
+template <int FMT, bool QO = false>
 static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)(p.tiles + g.fin.n), (unsigned)p.ksplit);
   if constexpr (FMT == SNIP_FP8_E4M3) {
     if (p.bm == 256 && p.bn == 128) {     // 3-stage ring: 72 KiB, two per CU
-      hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 3, 1>), grid, dim3(NT), 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 3, 1, QO>), grid, dim3(NT), 0, s, g);
       return true;
     }
   }
   if constexpr (FMT == SNIP_NVFP4) {
     if (p.bm == 256 && p.bn == 128) {     // 2-stage ring: 54 KiB, two per CU
-      hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 2, 1>), grid, dim3(NT), 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<FMT, 256, 128, 2, 1, QO>), grid, dim3(NT), 0, s, g);
       return true;
     }
   }
@@ -528,9 +591,9 @@ static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
       // NVFP4 12.7 -> 11.7 us), else of single units
       constexpr int K2 = 2 * Unit<FMT>::UE;
       if (g.K % K2 == 0 && g.kchunk % K2 == 0)
-        hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 2>), grid, dim3(NT), 0, s, g);
+        hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 2, QO>), grid, dim3(NT), 0, s, g);
       else
-        hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 1>), grid, dim3(NT), 0, s, g);
+        hipLaunchKernelGGL((gemm_kernel<FMT, 64, 64, 4, 1, QO>), grid, dim3(NT), 0, s, g);
       return true;
     }
   }
@@ -538,23 +601,26 @@ static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
     // NVFP4 has no 256x256 instance: plan_gemm never picks it (its 256x128
     // tiles are estimated faster at every size)
     if constexpr (FMT == SNIP_NVFP4) return false;
-    else hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1>), grid, dim3(NT), 0, s, g);
-  } else if (p.staged) launch_staged(FMT, p.bk, g, grid, s);
+    else hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1, QO>), grid, dim3(NT), 0, s, g);
+  } else if (p.staged) {
+    if constexpr (QO) return false;
+    else launch_staged(FMT, p.bk, g, grid, s);
+  }
   else if constexpr (FMT == SNIP_FP8_E4M3) {
     // FP8 128x128: a 3-stage ring (48 KiB) lets a third workgroup share the
     // CU where registers allow (measured up to 7 % faster). With at most one
     // tile per CU (no third workgroup to gain) two 64-element units per
     // stage halve the barriers per K: 2048x2048x4096 45.0 -> 41.6 us.
     if (p.ksplit == 1 && p.tiles <= 256 && g.K % (2 * Unit<FMT>::UE) == 0)
-      hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2>), grid, dim3(NT), 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 2, QO>), grid, dim3(NT), 0, s, g);
     else
-      hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 3, 1>), grid, dim3(NT), 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 3, 1, QO>), grid, dim3(NT), 0, s, g);
   } else if constexpr (FMT == SNIP_NVFP4) {
     // NVFP4 128x128: a 2-stage ring of single units (36 KiB), three
     // workgroups per CU
-    hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 1>), grid, dim3(NT), 0, s, g);
+    hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 2, 1, QO>), grid, dim3(NT), 0, s, g);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 4, 1>), grid, dim3(NT), 0, s, g);
+    hipLaunchKernelGGL((gemm_kernel<FMT, 128, 128, 4, 1, QO>), grid, dim3(NT), 0, s, g);
   }
   return true;
 }
@@ -622,24 +688,53 @@ hipError_t launch_gemm(int format, const GemmArgs& g_in, hipStream_t s) {
   g.tiles_m = (int)ceil_div(g.M, p.bm);
   g.tiles_n = (int)ceil_div(g.N, p.bn);
   g.kchunk = p.kchunk;
+  // output quantization: in the GEMM's epilogue when unsplit, else in the
+  // split-K reduction (FP8 and NVFP4 operands; NVFP4 or FP8 output)
+  const bool qo = g.q.codes != nullptr;
+  if (qo && ((format != SNIP_NVFP4 && format != SNIP_FP8_E4M3) ||
+             (g.q.fmt != SNIP_NVFP4 && g.q.fmt != SNIP_FP8_E4M3) || g.N % 16))
+    return hipErrorInvalidValue;
   int slot = timing_begin(LaunchTag{SNIP_LAUNCH_GEMM, format, -1, -1, 2.0 * g.M * g.N * g.K}, s);
   bool launched;
+  const bool qo_here = qo && p.ksplit == 1;
   switch (format) {
-    case SNIP_NVFP4: launched = launch_fmt<SNIP_NVFP4>(p, g, s); break;
-    case SNIP_FP8_E4M3: launched = launch_fmt<SNIP_FP8_E4M3>(p, g, s); break;
+    case SNIP_NVFP4:
+      launched = qo_here ? launch_fmt<SNIP_NVFP4, true>(p, g, s) : launch_fmt<SNIP_NVFP4>(p, g, s);
+      break;
+    case SNIP_FP8_E4M3:
+      launched = qo_here ? launch_fmt<SNIP_FP8_E4M3, true>(p, g, s) : launch_fmt<SNIP_FP8_E4M3>(p, g, s);
+      break;
     case SNIP_MXFP4: launched = launch_fmt<SNIP_MXFP4>(p, g, s); break;
     default: launched = launch_fmt<SNIP_BF16>(p, g, s); break;
   }
   hipError_t e = launched ? hipGetLastError() : hipErrorInvalidValue;
   timing_end(slot, s);
   if (e != hipSuccess || p.ksplit == 1) return e;
-  int64_t wg = ceil_div(g.M * g.N, 256);
-  if (wg > 4096) wg = 4096;
   slot = timing_begin(LaunchTag{SNIP_LAUNCH_SPLITK, format, -1, -1, (double)(g.M * g.N)}, s);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)wg), dim3(256), 0, s, g, p.ksplit);
+  if (qo) {
+    const dim3 grid((unsigned)gemm_qout_parts(format, g.M, g.N, g.K));
+    if (g.q.fmt == SNIP_NVFP4) {
+      if (g.q.sr) hipLaunchKernelGGL((splitk_reduce_q_kernel<SNIP_NVFP4, true>), grid, dim3(256), 0, s, g, p.ksplit);
+      else hipLaunchKernelGGL((splitk_reduce_q_kernel<SNIP_NVFP4, false>), grid, dim3(256), 0, s, g, p.ksplit);
+    } else {
+      if (g.q.sr) hipLaunchKernelGGL((splitk_reduce_q_kernel<SNIP_FP8_E4M3, true>), grid, dim3(256), 0, s, g, p.ksplit);
+      else hipLaunchKernelGGL((splitk_reduce_q_kernel<SNIP_FP8_E4M3, false>), grid, dim3(256), 0, s, g, p.ksplit);
+    }
+  } else {
+    int64_t wg = ceil_div(g.M * g.N, 256);
+    if (wg > 4096) wg = 4096;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)wg), dim3(256), 0, s, g, p.ksplit);
+  }
   e = hipGetLastError();
   timing_end(slot, s);
   return e;
+}
+
+int64_t gemm_qout_parts(int format, int64_t M, int64_t N, int64_t K) {
+  const GemmPlan p = plan_gemm(format, M, N, K);
+  if (p.ksplit == 1) return p.tiles;
+  const int64_t wg = ceil_div(M * N / 16, 256);
+  return wg < 1 ? 1 : wg > kQuantWG ? kQuantWG : wg;
 }
 
 }  // namespace snip

@@ -5,6 +5,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "quant_common.h"
 #include "stats_common.h"
 
 namespace snip {
@@ -110,6 +111,96 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const floatx4_t (&
         }
       }
   }
+}
+
+// ---------------------------------------------------------------- output quantization
+// Epilogue that also quantizes C row-wise (blocks of 16 along N; N % 16 ==
+// 0, so a block lies wholly inside or outside C). The operand ring in LDS
+// is idle once the K loop ends: each wave moves one 16-row slice of its
+// accumulators at a time into its own part of it (as C's values
+// y = acc * 2^(ea+eb)), and every lane then takes whole 16-element row
+// blocks of the slice: it writes the block to C (64 contiguous bytes) and
+// quantizes it with the row-wise quantizer's block codec (nvfp4_block /
+// fp8_chunk: the same arithmetic, element index row * N + col for the
+// stochastic draws). Statistics go to one partial per workgroup.
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile_q(const GemmArgs& g, const floatx4_t (&acc)[TM][TN], int64_t r0,
+                                             int64_t c0, int r16, int grp, uint8_t* lds) {
+  __shared__ double dred[8];
+  __shared__ uint32_t ured[8];
+  __shared__ float inv_lut[128];
+  constexpr int PITCH = TN * 16 + 4;                         // floats per staged row
+  const QOut& q = g.q;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
+  const int eS = tensor_exp(*q.amax_in, q.fmt);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *q.texp = eS;
+  __syncthreads();                                           // every wave is done with the ring
+  fill_inv_lut(inv_lut);                                     // (ends with a barrier)
+  float* const st = reinterpret_cast<float*>(lds) + wave * 16 * PITCH;
+  double e2s = 0.0, x2s = 0.0, x2r = 0.0;
+  uint32_t nf = 0u, amax_bits = 0u;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) st[(4 * grp + v) * PITCH + j * 16 + r16] = ldexpf(acc[i][j][v], e);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int b = lane; b < 16 * TN; b += 64) {
+      const int rr = b / TN, jb = b % TN;
+      const int64_t row = r0 + i * 16 + rr, col = c0 + jb * 16;
+      if (row >= g.M || col >= g.N) continue;
+      float x[16];
+      const float4* src = reinterpret_cast<const float4*>(st + rr * PITCH + jb * 16);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 f = src[t];
+        x[4 * t] = f.x;
+        x[4 * t + 1] = f.y;
+        x[4 * t + 2] = f.z;
+        x[4 * t + 3] = f.w;
+      }
+      float4* dst = reinterpret_cast<float4*>(g.c + row * g.ldc + col);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[t] = make_float4(x[4 * t], x[4 * t + 1], x[4 * t + 2], x[4 * t + 3]);
+      const uint64_t i0 = (uint64_t)(row * g.N + col);
+      Words4 d0, d1;
+      if (q.sr) {
+        d0 = draws8(q.seed, q.tensor_id, i0 >> 3);
+        d1 = draws8(q.seed, q.tensor_id, (i0 >> 3) + 1);
+      }
+      float be2, bx2;
+      if (q.fmt == SNIP_NVFP4) {
+        uint32_t lo, hi, sc;
+        if (q.sr) nvfp4_block<true>(x, eS, d0, d1, inv_lut, lo, hi, sc, be2, bx2);
+        else nvfp4_block<false>(x, eS, d0, d1, inv_lut, lo, hi, sc, be2, bx2);
+        *reinterpret_cast<uint2*>(q.codes + i0 / 2) = make_uint2(lo, hi);
+        q.scales[i0 / 16] = (uint8_t)sc;
+      } else {
+        uint32_t out[4];
+        if (q.sr) fp8_chunk<true>(x, eS, d0, d1, out, be2, bx2);
+        else fp8_chunk<false>(x, eS, d0, d1, out, be2, bx2);
+        *reinterpret_cast<uint4*>(q.codes + i0) = make_uint4(out[0], out[1], out[2], out[3]);
+      }
+      const bool bad = !(bx2 <= 3.0e38f);
+      uint32_t bnf = 0u, bam = 0u;
+      double rx2 = 0.0;
+      if (bad) nonfinite_stats<16>(x, bnf, rx2, bam);
+      else bam = block_absmax_bits<16>(x);
+      amax_bits = max(amax_bits, bam);
+      nf += bnf;
+      x2r += rx2;
+      e2s += bad ? 0.0 : (double)be2;
+      x2s += bad ? 0.0 : (double)bx2;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  wg_store_stats(q.part + blockIdx.x, ldexp(e2s, 2 * eS), ldexp(x2s, 2 * eS) + x2r, nf, amax_bits, dred, ured);
 }
 
 // Register-staged 128x128 kernel (MX-FP4 and BF16): K per stage and launch.

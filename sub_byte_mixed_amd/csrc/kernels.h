@@ -93,6 +93,22 @@ struct FJobs {
   int32_t n;
 };
 
+// Row-wise quantization of a GEMM's fp32 output C[M][N] in the launch that
+// computes it (blocks along N): codes, scales and tensor exponent in
+// `fmt` (NVFP4 or FP8), tensor scale from the supplied max, one statistics
+// partial per workgroup.
+struct QOut {
+  uint8_t* codes;          // [M][N/2] (NVFP4) or [M][N] (FP8); null: no quantization
+  uint8_t* scales;         // [M][N/16] E4M3 (NVFP4)
+  int32_t* texp;           // tensor exponent out
+  const float* amax_in;    // supplied max|C| (delayed scaling)
+  StatPart* part;          // [workgroups]
+  uint64_t seed;
+  uint32_t tensor_id;
+  int32_t fmt;
+  int32_t sr;
+};
+
 // GEMM problem: C[M][N] = A[M][K] . B[N][K]^T * 2^(ea + eb).
 struct GemmArgs {
   const uint8_t* a;        // codes (bf16 for BF16)
@@ -118,6 +134,7 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;
   } sec;
   int32_t nsec;            // 0: one problem; 1: `sec` follows
+  QOut q;                  // output quantization (q.codes null: none)
 };
 
 // Tile shape and K split chosen on the host for one GEMM.
@@ -131,6 +148,8 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int format, int64_t M, int64_t N, int64_t K);
 size_t gemm_partial_bytes(int format, int64_t M, int64_t N, int64_t K);
+// Statistics partials (workgroups) of a GEMM launch that quantizes its output.
+int64_t gemm_qout_parts(int format, int64_t M, int64_t N, int64_t K);
 
 // Launchers (all asynchronous on `s`); they return the hipError_t of the launch.
 hipError_t launch_amax(const AJobs& jobs, int total_wg, hipStream_t s);

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
     # and nothing else is exported under the snip_ prefix
@@ -286,10 +286,12 @@ def test_workspace_size_matches_per_call_sizers(L):
                 L.snip_linear_fwd_save_workspace(T, din, dout, fmt)
             assert L.snip_workspace_size(S.OP_LINEAR_BWD_SAVED, T, dout, din, fmt) == \
                 L.snip_linear_bwd_saved_workspace(T, din, dout, fmt)
+            assert L.snip_workspace_size(S.OP_QGEMM_QOUT, T, dout, din, fmt) == \
+                L.snip_qgemm_qout_workspace(T, dout, din, fmt)
     # a split-K plan needs scratch: the skinny K projection's wgrad
     assert L.snip_workspace_size(S.OP_QGEMM, 256, 2048, 4096, S.FP8) > 0
     assert L.snip_workspace_size(S.OP_LINEAR_FWD, 256, 512, 512, S.NVFP4) > 0
-    assert L.snip_workspace_size(7, 256, 512, 512, S.NVFP4) == 0
+    assert L.snip_workspace_size(8, 256, 512, 512, S.NVFP4) == 0
     assert L.snip_workspace_size(-1, 256, 512, 512, S.NVFP4) == 0
     assert L.snip_workspace_size(S.OP_QGEMM, 0, 512, 512, S.NVFP4) == 0
 
