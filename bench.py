@@ -261,8 +261,9 @@ def main():
         achieved_ops = ops / (ms * 1e-3) / 1e12
         alu = {"bound": "alu", "kernel": "quant_dual_kernel (all formats and roundings of the step)",
                "achieved": round(achieved_ops, 2), "peak": round(profiling.VALU_LANE_OPS / 1e12, 2),
-               "unit": "T VALU lane-ops/s", "frac": round(achieved_ops * 1e12 / profiling.VALU_LANE_OPS, 4),
-               "ops_per_element": {" ".join(k): v for k, v in valu.items()}}
+               "unit": "T VALU lane-cycles/s (cycle-weighted: quarter-rate 64-bit multiplies at their cost)",
+               "frac": round(achieved_ops * 1e12 / profiling.VALU_LANE_OPS, 4),
+               "lane_cycles_per_element": {" ".join(k): v for k, v in valu.items()}}
 
     # ------------------------------------------------------- CPU baseline
     cpu = None

@@ -49,17 +49,20 @@ __device__ __forceinline__ int xor2i(int v) { return __builtin_amdgcn_update_dpp
 __device__ __forceinline__ float xor1f(float v) { return __int_as_float(xor1i(__float_as_int(v))); }
 __device__ __forceinline__ float xor2f(float v) { return __int_as_float(xor2i(__float_as_int(v))); }
 
-// Row-wise statistics of one lane.
+// Row-wise statistics of one lane: only the quantization error. Sum x^2,
+// the non-finite count and max|x| are properties of the tensor, the same in
+// both layouts; the column-wise half (which sees every element once) gives
+// them to both statistics records.
 struct RowStats {
-  double e2s = 0.0, x2s = 0.0;      // tensor-scaled domain (NVFP4, FP8)
-  double e2r = 0.0, x2r = 0.0;      // raw domain (MX, non-finite blocks)
-  uint32_t nf = 0u, amax_bits = 0u;
+  double e2s = 0.0;                 // tensor-scaled domain (NVFP4, FP8)
+  double e2r = 0.0;                 // raw domain (MX)
 };
 
 // Eight consecutive row elements of one lane: codes, scale (NVFP4, MX) and
-// statistics, with the block-wide quantities shared over the lanes of the
-// block. `store` is false for a group past the last column (its partner
-// lanes are past it too).
+// error statistics, with the block-wide quantities shared over the lanes of
+// the block. A block holding a non-finite value (its error sum is then NaN
+// or infinite) adds no error. `store` is false for a group past the last
+// column (its partner lanes are past it too).
 template <int FMT, bool SR>
 __device__ __forceinline__ void row_group(const float (&x)[8], int eS, const float* inv_lut,
                                           const Words4& d, int64_t row, int64_t col, int64_t C,
@@ -79,25 +82,18 @@ __device__ __forceinline__ void row_group(const float (&x)[8], int eS, const flo
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = xs[i] * inv;
     const uint32_t code = SR ? fp4x8_sr(r, d) : fp4x8_rne(r);
-    float q[8], be2 = 0.0f, bx2 = 0.0f;
+    float q[8], be2 = 0.0f;
     fp4x8_dec(code, q);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float err = fmaf(q[i], shat, -xs[i]);
       be2 = fmaf(err, err, be2);
-      bx2 = fmaf(xs[i], xs[i], bx2);
     }
-    const int bad = (int)!(bx2 <= 3.0e38f) | xor1i((int)!(bx2 <= 3.0e38f));
+    const int bad = (int)!(be2 <= 3.0e38f) | xor1i((int)!(be2 <= 3.0e38f));
     if (store) {
       *reinterpret_cast<uint32_t*>(o.codes + row * (C / 2) + col / 2) = code;
       if ((col & 15) == 0) o.scales[row * (C / 16) + col / 16] = (uint8_t)sc;
-      uint32_t bnf = 0u, dummy = 0u;
-      double rx2 = 0.0;
-      if (bad) nonfinite_stats<8>(x, bnf, rx2, dummy);
-      st.nf += bnf;
-      st.x2r += rx2;
       st.e2s += bad ? 0.0 : (double)be2;
-      st.x2s += bad ? 0.0 : (double)bx2;
     }
   } else if constexpr (FMT == SNIP_FP8_E4M3) {
     float r[8], c[8];
@@ -108,26 +104,19 @@ __device__ __forceinline__ void row_group(const float (&x)[8], int eS, const flo
     }
     const uint32_t w0 = SR ? fp8x4_sr(c, d, 0) : fp8x4_rne(c);
     const uint32_t w1 = SR ? fp8x4_sr(c + 4, d, 4) : fp8x4_rne(c + 4);
-    float q[8], be2 = 0.0f, bx2 = 0.0f;
+    float q[8], be2 = 0.0f;
     fp8x4_dec(w0, q);
     fp8x4_dec(w1, q + 4);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float e = q[i] - r[i];
       be2 = fmaf(e, e, be2);
-      bx2 = fmaf(r[i], r[i], bx2);
     }
     // non-finite flag over the 16-element chunk of the row-wise pass
-    const int bad = (int)!(bx2 <= 3.0e38f) | xor1i((int)!(bx2 <= 3.0e38f));
+    const int bad = (int)!(be2 <= 3.0e38f) | xor1i((int)!(be2 <= 3.0e38f));
     if (store) {
       *reinterpret_cast<uint2*>(o.codes + row * C + col) = make_uint2(w0, w1);
-      uint32_t bnf = 0u, dummy = 0u;
-      double rx2 = 0.0;
-      if (bad) nonfinite_stats<8>(x, bnf, rx2, dummy);
-      st.nf += bnf;
-      st.x2r += rx2;
       st.e2s += bad ? 0.0 : (double)be2;
-      st.x2s += bad ? 0.0 : (double)bx2;
     }
   } else {  // MX-FP4: 32-element block over four lanes
     float am = 0.0f;
@@ -147,30 +136,20 @@ __device__ __forceinline__ void row_group(const float (&x)[8], int eS, const flo
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = x[i] * pw;
     const uint32_t code = SR ? fp4x8_sr(r, d) : fp4x8_rne(r);
-    float q[8], be2 = 0.0f, bx2 = 0.0f;
+    float q[8], be2 = 0.0f;
     fp4x8_dec(code, q);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float err = q[i] - r[i];
       be2 = fmaf(err, err, be2);
-      bx2 = fmaf(r[i], r[i], bx2);
     }
-    int bad = (int)!(bx2 <= 3.0e38f);
+    int bad = (int)!(be2 <= 3.0e38f);
     bad |= xor1i(bad);
     bad |= xor2i(bad);
     if (store) {
       *reinterpret_cast<uint32_t*>(o.codes + row * (C / 2) + col / 2) = code;
       if ((col & 31) == 0) o.scales[row * (C / 32) + col / 32] = (uint8_t)sc;
-      uint32_t bnf = 0u, bam = __float_as_uint(am);
-      double rx2 = ldexp((double)bx2, 2 * X);
-      if (bad) {
-        bam = 0u;
-        nonfinite_stats<8>(x, bnf, rx2, bam);
-      }
-      st.nf += bnf;
-      st.x2r += rx2;
       st.e2r += bad ? 0.0 : ldexp((double)be2, 2 * X);
-      st.amax_bits = max(st.amax_bits, bam);
     }
   }
 }
@@ -366,17 +345,15 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(DJobs jobs) {
     }
     __syncthreads();
   }
-  if (FMT != SNIP_MXFP4) {
-    // the tensor max used for scaling, or under a supplied max the current
-    // tensor's own (the column blocks cover every element once)
-    const uint32_t rep = J.amax_in ? tmax : __float_as_uint(A);
-    amax_bits = rep;
-    rs.amax_bits = rep;
-  }
-  wg_store_stats(J.col.part + wg, ldexp(e2s, 2 * eS) + e2r, ldexp(x2s, 2 * eS) + x2r, nf, amax_bits, dred, ured);
+  // the tensor max used for scaling, or under a supplied max the current
+  // tensor's own (the column blocks cover every element once)
+  if (FMT != SNIP_MXFP4) amax_bits = J.amax_in ? tmax : __float_as_uint(A);
+  // Sum x^2, the non-finite count and the max from the column blocks serve
+  // both records; only the errors differ
+  const double x2 = ldexp(x2s, 2 * eS) + x2r;
+  wg_store_stats(J.col.part + wg, ldexp(e2s, 2 * eS) + e2r, x2, nf, amax_bits, dred, ured);
   __syncthreads();
-  wg_store_stats(J.row.part + wg, ldexp(rs.e2s, 2 * eS) + rs.e2r, ldexp(rs.x2s, 2 * eS) + rs.x2r, rs.nf,
-                 rs.amax_bits, dred, ured);
+  wg_store_stats(J.row.part + wg, ldexp(rs.e2s, 2 * eS) + rs.e2r, x2, nf, amax_bits, dred, ured);
 }
 
 template <int FMT>

@@ -94,7 +94,7 @@ def load_valu(workload: str):
             d = json.loads(line[len("valu-json:"):])
             if d.get("source_hash") != source_hash(QUANT_SOURCES):
                 return None
-            return {tuple(k["kernel"].split(", ")): k["ops_per_elem"] for k in d["kernels"]}
+            return {tuple(k["kernel"].split(", ")): k.get("weighted_per_elem", k["ops_per_elem"]) for k in d["kernels"]}
     return None
 
 
@@ -288,23 +288,37 @@ def dual_elements_per_step(wl):
 
 
 def cmd_valu(a):
+    """VALU work of the fused quantizers, counted two ways: instructions
+    (SQ_INSTS_VALU, each a full-rate slot) and issue cycles
+    (SQ_ACTIVE_INST_VALU, in quad-cycles per wave: quarter-rate 64-bit
+    multiplies such as Philox's v_mad_u64_u32 count their real cost). The
+    cycle-weighted count is the one the VALU roofline uses."""
     sys.path.insert(0, ROOT)
     import synth
     wl = synth.WORKLOADS[a.workload]
     elems = dual_elements_per_step(wl)
     insts = _per_kernel(a.pmc, "SQ_INSTS_VALU")
+    int64 = _per_kernel(a.pmc, "SQ_INSTS_VALU_INT64")
+    active = _per_kernel(a.pmc, "SQ_ACTIVE_INST_VALU")
     busy = _per_kernel(a.pmc, "VALUBusy")
     stats = _stats_by_name(a.stats)
     names = {0: "bf16", 1: "fp8_e4m3", 2: "nvfp4", 3: "mxfp4"}
     lines = [f"# VALU work of the fused quantize kernels on the {a.workload} workload", "",
-             "One rocprofv3 --pmc run of the benchmark. Lane-ops per element = SQ_INSTS_VALU x 64 over the",
-             f"elements the kernel family quantized in the run's {a.steps} steps (X and W in the forward,",
-             "dY in the backward, one read each). VALU-bound rate = 39.3e12 lane-ops/s (256 CUs x 4 SIMDs",
-             "x 16 lanes x 2.4 GHz, full-rate instructions) over the lane-ops per element; reached = elements",
-             "per dispatch over the average duration of a kernel-trace run of the same benchmark. VALUBusy is",
-             "rocprofv3's derived counter. Commands (from the repository root):", "", "```", a.cmd, "```", "",
-             "| Kernel (format, row rounding, column rounding) | Dispatches | VALU lane-ops / element | VALUBusy % | "
-             "VALU-bound Gelem/s | reached Gelem/s | of VALU bound |", "|---|---|---|---|---|---|---|"]
+             "One rocprofv3 --pmc run of the benchmark. Per element of the kernel family (X and W in the",
+             f"forward, dY in the backward, one read each; the run's {a.steps} steps):",
+             "- lane-ops = SQ_INSTS_VALU x 64 (every VALU instruction one slot);",
+             "- of which int64 = SQ_INSTS_VALU_INT64 x 64 (Philox's 32x32->64-bit multiplies, quarter rate,",
+             "  and 64-bit index arithmetic);",
+             "- lane-cycles = SQ_ACTIVE_INST_VALU x 4 cycles x 16 lanes (the cycles the SIMDs spend issuing",
+             "  VALU work, multi-cycle instructions at their real cost): the cycle-weighted count.",
+             "VALU-bound rate = 39.3e12 lane-slots/s (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz) over the",
+             "cycle-weighted count; reached = elements per dispatch over the average duration of a",
+             "kernel-trace run of the same benchmark. VALUBusy is rocprofv3's derived counter (the SIMDs'",
+             "VALU issue cycles over elapsed cycles). Commands (from the repository root):", "", "```", a.cmd,
+             "```", "",
+             "| Kernel (format, row rounding, column rounding) | Dispatches | VALU lane-ops / elem | int64 / elem | "
+             "lane-cycles / elem | VALUBusy % | VALU-bound Gelem/s | reached Gelem/s | of VALU bound |",
+             "|---|---|---|---|---|---|---|---|---|"]
     out = []
     for name, d in insts.items():
         m = re.search(r"quant_dual_kernel<(\d+), (true|false), (true|false)>", name)
@@ -314,15 +328,20 @@ def cmd_valu(a):
         n = len(d)
         e_total = elems[key] * a.steps
         ops = sum(d.values()) * 64 / e_total
-        bound = VALU_LANE_OPS / ops / 1e9
+        i64 = sum(int64.get(name, {}).values()) * 64 / e_total
+        cyc = sum(active.get(name, {}).values()) * 4 * 16 / e_total
+        weighted = cyc if cyc > 0 else ops
+        bound = VALU_LANE_OPS / weighted / 1e9
         calls, avg_ns = stats[name]
         reached = e_total / n / avg_ns
         vb = sum(busy.get(name, {}).values()) / max(1, len(busy.get(name, {})))
         label = f"{names[key[0]]}, {'SR' if key[1] else 'RNE'}, {'SR' if key[2] else 'RNE'}"
-        out.append({"kernel": label, "ops_per_elem": round(ops, 2), "valu_busy": round(vb, 1),
-                    "bound_gelem_s": round(bound, 1), "reached_gelem_s": round(reached, 1)})
-        lines.append(f"| `quant_dual_kernel` {label} | {n} | {ops:.1f} | {vb:.1f} | {bound:.0f} | {reached:.0f} | "
-                     f"{reached / bound * 100:.1f} % |")
+        out.append({"kernel": label, "ops_per_elem": round(ops, 2), "int64_per_elem": round(i64, 2),
+                    "cycles_per_elem": round(cyc, 2), "weighted_per_elem": round(weighted, 2),
+                    "valu_busy": round(vb, 1), "bound_gelem_s": round(bound, 1),
+                    "reached_gelem_s": round(reached, 1)})
+        lines.append(f"| `quant_dual_kernel` {label} | {n} | {ops:.1f} | {i64:.1f} | {cyc:.1f} | {vb:.1f} | "
+                     f"{bound:.0f} | {reached:.0f} | {reached / bound * 100:.1f} % |")
     lines += ["", "valu-json:" + json.dumps({"workload": a.workload, "source_hash": source_hash(QUANT_SOURCES),
                                               "kernels": out}), ""]
     with open(a.out, "w") as fh:
