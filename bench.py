@@ -243,6 +243,12 @@ def main():
         "frac_of_native_peak": round(achieved / (PEAK["fp4_tflops"] if dom_fmt in (S.NVFP4, S.MXFP4)
                                                  else PEAK["fp8_tflops"]), 4),
     }
+    ceil = profiling.load_mfma_ceiling()
+    if ceil and dom_fmt != S.MXFP4:
+        # the fp16 MFMA rate the chip sustains at the clock it holds under MFMA
+        # load (about 2.0 GHz instead of the 2.4 GHz the published peak assumes)
+        roofline["measured_mfma_ceiling_tflops"] = ceil["sustained_fp16_mfma_tflops"]
+        roofline["frac_of_measured_ceiling"] = round(achieved / ceil["sustained_fp16_mfma_tflops"], 4)
     gemm_detail = {S.FORMAT_NAMES[f]: {"tflops": round(g["flops"] / (g["ms"] * 1e-3) / 1e12, 2),
                                        "ms_per_step": round(g["ms"] / args.steps, 4),
                                        "launches_per_step": g["launches"] // args.steps}

@@ -34,22 +34,74 @@ def hipcc_path() -> str:
 
 
 REPO = os.path.dirname(HERE)
-CHECKER_SRC = os.path.join(REPO, "tests", "helpers", "hw_convert_check.hip")
-CHECKER_BIN = os.path.join(REPO, "tests", "helpers", "hw_convert_check")
+HELPERS = os.path.join(REPO, "tests", "helpers")
+CHECKER_SRC = os.path.join(HELPERS, "hw_convert_check.hip")
+CHECKER_BIN = os.path.join(HELPERS, "hw_convert_check")
+MFMA_PROBE_SRC = os.path.join(HELPERS, "fp8_mfma_accuracy.hip")
+MFMA_PROBE_BIN = os.path.join(HELPERS, "fp8_mfma_accuracy")
+CLOCK_PROBE_SRC = os.path.join(HELPERS, "mfma_clock.hip")
+CLOCK_PROBE_BIN = os.path.join(HELPERS, "mfma_clock")
 
 
-def build_checker(verbose: bool = False) -> str:
-    """The exhaustive hardware-convert checker used by the GPU tests."""
-    cmd = [hipcc_path(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], "-o",
-           CHECKER_BIN + ".tmp", CHECKER_SRC]
+def _build_helper(src: str, out: str, verbose: bool, extra=()) -> str:
+    cmd = [hipcc_path(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], *extra, "-o", out + ".tmp", src]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
-        raise RuntimeError(f"hipcc failed:\n{errs}")
-    os.replace(CHECKER_BIN + ".tmp", CHECKER_BIN)
-    return CHECKER_BIN
+        raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
+ASAN_SRC = os.path.join(HELPERS, "abi_asan_check.cpp")
+ASAN_BIN = os.path.join(HELPERS, "abi_asan_check")
+
+
+def build_asan_check(verbose: bool = False) -> str:
+    """The library's sources and tests/helpers/abi_asan_check.cpp as one
+    executable whose host code is built with AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code is not instrumented): the
+    validation and sizing paths of every entry point, checked on the CPU."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    base = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC", "-O3")] + ["-O1", "-g"]
+
+    def one(src):
+        obj = os.path.join(BUILD_DIR, "asan_" + os.path.splitext(os.path.basename(src))[0] + ".o")
+        cmd = [hipcc_path(), *base, *san, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+            raise RuntimeError(f"hipcc failed on {src}:\n{errs}")
+        return obj
+
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = [os.path.join(CSRC, s) for s in SOURCES] + [ASAN_SRC]
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(one, srcs))
+    cmd = [hipcc_path(), "--offload-arch=gfx950", *san, "-o", ASAN_BIN + ".tmp", *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(ASAN_BIN + ".tmp", ASAN_BIN)
+    return ASAN_BIN
+
+
+def build_checker(verbose: bool = False) -> str:
+    """The GPU test and measurement helpers: the exhaustive hardware-convert
+    checker, the FP8 matrix-instruction accuracy probe and the shader-clock
+    probe."""
+    _build_helper(MFMA_PROBE_SRC, MFMA_PROBE_BIN, verbose)
+    # accumulators in VGPRs: the AGPR form costs register copies in its loop
+    _build_helper(CLOCK_PROBE_SRC, CLOCK_PROBE_BIN, verbose, ("-mllvm", "-amdgpu-mfma-vgpr-form=true"))
+    return _build_helper(CHECKER_SRC, CHECKER_BIN, verbose)
 
 
 def _compile(src: str, verbose: bool) -> str:

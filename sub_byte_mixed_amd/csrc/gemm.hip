@@ -16,10 +16,12 @@
 //          scales per 16.
 //   FP8    E4M3 codes are decoded exactly into fp16 (v_cvt_scalef32_pk_f16_fp8)
 //          and multiplied on v_mfma_f32_16x16x32_f16. The gfx950 8-bit MFMAs
-//          (v_mfma_*_f8f6f4, and v_mfma_f32_16x16x32_fp8_fp8 as well) align
-//          their products to the largest one with too few bits: measured up
-//          to 4e-4 of sum|a||b| on E4M3 data of full range, outside the 1e-5
-//          bound, so they are not used for E4M3 x E4M3.
+//          (v_mfma_scale_f32_16x16x128_f8f6f4 and v_mfma_f32_16x16x32_fp8_fp8)
+//          lose low bits of the products' sum: measured (the probe
+//          tests/helpers/fp8_mfma_accuracy.hip) up to 1.9e-4 of sum|a||b| on
+//          full-range E4M3 data and 2.2e-5 on Gaussian data, against 3.1e-7
+//          for the decode path; the bound is 1e-5, so they are not used for
+//          E4M3 x E4M3.
 //   MXFP4  E2M1 codes and E8M0 scales go straight into
 //          v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 operands, one scale per row
 //          and 32-element K block).

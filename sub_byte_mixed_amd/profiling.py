@@ -33,6 +33,10 @@ except for the `copy` calibration run).
       kernel quantized in the run's N steps), the element rate the chip's
       VALU issue rate allows at that count (256 CUs x 4 SIMDs x 16 lanes x
       2.4 GHz = 39.3e12 lane-operations/s), and the rate reached.
+  python -m sub_byte_mixed_amd.profiling sweep --reps R
+      the 7B Down projection of the precision sweep forward and backward in
+      BF16, FP8, NVFP4 and MX-FP4 (1 + R repetitions each): the program the
+      sweep's GEMM counter summaries are taken on.
   python -m sub_byte_mixed_amd.profiling vendor --workload NAME --out OUT_MD
       times the vendor library's fp16 and bf16 GEMM (torch.mm, hipBLASLt) on
       the workload's forward, dgrad and wgrad shapes: a reference point for
@@ -79,6 +83,19 @@ def load_traffic(workload: str, kernel_prefix: str):
             d = json.loads(line[len(TRAFFIC_TAG):])
             if d.get("source_hash") == source_hash() and d.get("kernel") == kernel_prefix:
                 return d
+    return None
+
+
+def load_mfma_ceiling():
+    """The dense fp16 MFMA rate the chip sustains at the clock it holds under
+    MFMA load (profiles/mfma_clock.md, measured by tests/helpers/mfma_clock),
+    in TFLOP/s, or None."""
+    path = os.path.join(ROOT, "profiles", "mfma_clock.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("mfma-clock-json:"):
+            return json.loads(line[len("mfma-clock-json:"):])
     return None
 
 
@@ -480,6 +497,33 @@ def cmd_vendor(a):
     print(a.out)
 
 
+def cmd_sweep(a):
+    """The 7B Down projection of the precision sweep (T = 16384, 11008 ->
+    4096) forward and backward in every format of the sweep (BF16, FP8,
+    NVFP4, MX-FP4), one warm-up and `reps` timed repetitions each: the
+    program the sweep's GEMM counter summaries are taken on. Prints each
+    format's GEMM TFLOP/s (launch timing) against its MFMA peak."""
+    sys.path.insert(0, ROOT)
+    import torch
+    import synth
+    import sub_byte_mixed_amd as S
+    wl = synth.WORKLOADS["down7b_sweep"]
+    x, w, dy = (t.cuda() for t in synth.gen_layer(wl, 0))
+    peak = {S.BF16: 2516.6e12, S.FP8: 2516.6e12, S.NVFP4: 2516.6e12, S.MXFP4: 10066.3e12}
+    for fmt in (S.BF16, S.FP8, S.NVFP4, S.MXFP4):
+        for rep in range(a.reps + 1):
+            if rep == 1:
+                torch.cuda.synchronize()
+                S.timing_start(4096)
+            S.linear_fwd(x, w, fmt, 0, 0)
+            S.linear_bwd(dy, x, w, fmt, fmt, 0, 0)
+        recs, _ = S.timing_read()
+        g = [r for r in recs if r["kind"] == "gemm"]
+        fl, ms = sum(r["work"] for r in g), sum(r["ms"] for r in g)
+        print(f"{S.FORMAT_NAMES[fmt]}: {len(g)} GEMM launches, {fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s, "
+              f"{fl / (ms * 1e-3) / peak[fmt] * 100:.1f} % of its MFMA peak", flush=True)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -515,13 +559,15 @@ def main(argv=None):
     w.add_argument("--pmc", nargs="+", required=True)
     for key in ("workload", "out", "cmd"):
         w.add_argument("--" + key, dest=key, required=True)
+    sw = sub.add_parser("sweep")
+    sw.add_argument("--reps", type=int, default=3)
     v = sub.add_parser("vendor")
     v.add_argument("--workload", default="tinyllama1b")
     v.add_argument("--out", required=True)
     v.add_argument("--reps", type=int, default=20)
     a = ap.parse_args(argv)
     {"copy": cmd_copy, "trace": cmd_trace, "traffic": cmd_traffic, "kernels": cmd_kernels, "mfma": cmd_mfma,
-     "valu": cmd_valu, "stalls": cmd_stalls,
+     "valu": cmd_valu, "stalls": cmd_stalls, "sweep": cmd_sweep,
      "vendor": cmd_vendor}[a.cmd_name](a)
 
 
