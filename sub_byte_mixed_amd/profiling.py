@@ -270,7 +270,7 @@ def cmd_stalls(a):
                 continue
             vals = _per_kernel(path, c)
             rows.append((c, {k: sum(v.values()) / max(sum(wave.get(k, {}).values()), 1.0) for k, v in vals.items()}))
-    kernels = sorted({k for _, d in rows for k in d if "gemm_kernel" in k})
+    kernels = sorted({k for _, d in rows for k in d if "snip::gemm_" in k})
     head = "| Counter / SQ_WAVE_CYCLES | " + " | ".join(f"`{_short(k, 48)}`" for k in kernels) + " |"
     lines = [f"# Wave-cycle breakdown of the GEMM kernels on the {a.workload} workload", "",
              "SQ counters in quad-cycles, summed over each kernel's dispatches in a --pmc run of the benchmark,",
