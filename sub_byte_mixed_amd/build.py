@@ -116,12 +116,50 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+# Kernels that issue MFMAs as inline asm, per source: their device assembly
+# is checked for the wait states the compiler does not insert for them
+# (asm_hazards.py); a violation fails the build.
+ASM_MFMA_KERNELS = {"gemm.hip": ["gemm_nvfp4_w1_kernel"]}
+
+
+def _device_asm(src: str, verbose: bool) -> str:
+    out = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".device.s")
+    cmd = [hipcc_path(), *[f for f in HIPCC_FLAGS if f != "-shared"], "-S", "--cuda-device-only", "-o", out,
+           os.path.join(CSRC, src)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
+    if res.returncode != 0:
+        errs = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{errs}")
+    return out
+
+
+def check_asm_mfma(asm_path: str, kernels) -> None:
+    """Raise if a listed kernel is missing or breaks an asm-MFMA hazard bound."""
+    from . import asm_hazards
+    text = open(asm_path).read()
+    for part in kernels:
+        res = asm_hazards.check_asm(text, part)
+        if not res or not all(n > 0 for n, _ in res.values()):
+            raise RuntimeError(f"{asm_path}: no asm MFMAs found in kernels matching {part!r}")
+        for name, (_, bad) in res.items():
+            if bad:
+                raise RuntimeError(f"{asm_path}: {name}: asm MFMA hazard:\n  " + "\n  ".join(bad[:10]))
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source to an object (in parallel), then link."""
+    """Compile every source to an object (in parallel), check the device
+    assembly of the asm-MFMA kernels, then link."""
     from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    jobs = [("o", s) for s in SOURCES] + [("s", s) for s in ASM_MFMA_KERNELS]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        outs = list(ex.map(lambda j: _compile(j[1], verbose) if j[0] == "o" else _device_asm(j[1], verbose), jobs))
+    objs = outs[:len(SOURCES)]
+    for (kind, src), path in zip(jobs, outs):
+        if kind == "s":
+            check_asm_mfma(path, ASM_MFMA_KERNELS[src])
     out_tmp = LIB + ".tmp"
     cmd = [hipcc_path(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs]
     if verbose:

@@ -400,6 +400,288 @@ __global__ __launch_bounds__(NT, (gemm_min_wgs<FMT, BM, BN, S, UK>())) void gemm
   else store_tile<TM, TN>(g, acc, m0 + wm * WM, n0 + wn * WN, r16, grp);
 }
 
+// acc += a . b on v_mfma_f32_16x16x32_f16 with the accumulator kept in place
+// in AGPRs: 256 accumulator registers fill the AGPR file, and the compiler's
+// own MFMA selection, which may write a result to other registers than its
+// input, then moves accumulators through VGPRs and spills.
+// The compiler does not model an asm MFMA's hazards: a VALU result it reads
+// needs 2+ independent instructions in between, and reading its result back
+// needs the MFMA's latency. mfma_guard() (32 wait states, fenced against
+// code motion) separates the prologue's decode from the first asm MFMA and
+// the last asm MFMA from the epilogue's accumulator reads; inside the loop
+// every operand is decoded at least four MFMAs before its use.
+__device__ __forceinline__ void mfma_acc_agpr(floatx4_t& acc, const half8_t& a, const half8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_guard() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// NVFP4 on 256x256 tiles, one wave per SIMD, each wave a 128x128 sub-tile.
+//
+// The NVFP4 decode costs one VALU instruction per element (half a
+// v_cvt_scalef32_pk_f16_fp4, half a v_pk_mul_f16: the convert applies only
+// the exponent of its scale operand, so the E4M3 scale's mantissa needs the
+// multiply). A wave's sub-tile of WM x WN decodes (WM + WN) * 32 elements per
+// K slice of 32 for WM * WN / 256 MFMAs: 3 VALU per MFMA on 128x64, 2 on
+// 128x128. Measured on MI355X: while one wave streams
+// v_mfma_f32_16x16x32_f16 (16 cycles each), another wave on the same SIMD
+// issues a VALU instruction every 8-9.5 cycles, so about 2 fit under each
+// MFMA; at 3 per MFMA the 128x64 sub-tiles are bound by VALU issue.
+//
+// Schedule: within K slice q, the MFMAs of A row block i run beside the
+// decode of A row block i+1 and of B block i for slice q+1 (16 VALU per 8
+// MFMAs). The stage's raw codes and scales are in registers, read from the
+// LDS ring before its last slice: a barrier there (stage it+1 has landed,
+// every wave has read stage it) lets the wave refill stage it's slot with
+// stage it+3 and read stage it+1, whose first slice it decodes during the
+// last slice of stage it. Ring: 3 stages of K = 128 (36 KiB each).
+template <bool QO>
+__global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g_in) {
+  constexpr int S = 3, NU = 16;                            // stages; 16-row units per operand
+  constexpr int LA = NU * 1024, LB = NU * 1024;            // code bytes per stage
+  constexpr int LSA = NU * 16 * 8, LSB = NU * 16 * 8;      // scale bytes per stage
+  constexpr int STAGE = LA + LB + LSA + LSB;
+  constexpr int NSA = LSA / 256, NSB = LSB / 256;          // scale DMA instructions
+  constexpr int IA = NU / 4, IB = NU / 4, IS = (NSA + NSB) / 4;
+  constexpr int NIW = IA + IB + IS;                        // DMA instructions per wave and stage
+  constexpr int TM = 8, TN = 8;                            // 16x16 MFMA tiles per wave
+  static_assert(2 * NIW <= 63, "vmcnt range");
+  __shared__ __align__(1024) uint8_t smem[S * STAGE];
+  if (finalize_workgroup(g_in)) return;
+
+  GemmArgs g = g_in;
+  int tile = blockIdx.x;
+  if (g_in.nsec && tile >= g_in.tiles_m * g_in.tiles_n) {
+    tile -= g_in.tiles_m * g_in.tiles_n;
+    g.a = g_in.sec.a;
+    g.b = g_in.sec.b;
+    g.as = g_in.sec.as;
+    g.bs = g_in.sec.bs;
+    g.ea = g_in.sec.ea;
+    g.eb = g_in.sec.eb;
+    g.c = g_in.sec.c;
+    g.M = g_in.sec.M;
+    g.N = g_in.sec.N;
+    g.K = g_in.sec.K;
+    g.ldc = g_in.sec.ldc;
+    g.kchunk = g_in.sec.K;
+    g.tiles_m = g_in.sec.tiles_m;
+    g.tiles_n = g_in.sec.tiles_n;
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, grp = lane >> 4;
+  int tm, tn;
+  tile_coords(tile, g.tiles_m, g.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+  const int64_t rowbytes = g.K / 128 * 64, srow = g.K / 16;
+  const int kt0 = (int)(blockIdx.y * g.kchunk / 128);
+  const int kt1 = min((int)(g.K / 128), (int)((blockIdx.y + 1) * g.kchunk / 128));
+  const int nk = kt1 - kt0;
+
+  // DMA sources, as in gemm_kernel with one unit per stage: wave w loads
+  // code units w, w+4, ... of A and of B and scale instructions w, w+4, ...
+  uint32_t offa[IA], offb[IB], offs[IS], ldss[IS];
+  const uint8_t* sbase[IS];                                // A or B scales, chosen once
+#pragma unroll
+  for (int t = 0; t < IA; ++t)
+    offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + (lane & 3) * 16;
+#pragma unroll
+  for (int t = 0; t < IB; ++t)
+    offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
+#pragma unroll
+  for (int t = 0; t < IS; ++t) {
+    const int pp = wave + 4 * t;
+    const bool isa = pp < NSA;
+    const int p = isa ? pp : pp - NSA;
+    const int blk = 2 * p + (lane >> 5), r = (lane & 31) >> 1, part = (lane & 1) * 4;
+    const int64_t row = isa ? min(m0 + blk * 16 + r, g.M - 1) : min(n0 + blk * 16 + r, g.N - 1);
+    offs[t] = (uint32_t)(row * srow) + part;
+    sbase[t] = isa ? g.as : g.bs;
+    ldss[t] = LA + LB + pp * 256;                          // B scales follow the A scales
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto issue = [&](int kt, int slot) {
+    const uint32_t base = lds0 + slot * STAGE;
+#pragma unroll
+    for (int t = 0; t < IA; ++t) dma16(g.a + (int64_t)kt * 64 + offa[t], base + (wave + 4 * t) * 1024);
+#pragma unroll
+    for (int t = 0; t < IB; ++t) dma16(g.b + (int64_t)kt * 64 + offb[t], base + LA + (wave + 4 * t) * 1024);
+#pragma unroll
+    for (int t = 0; t < IS; ++t) dma4(sbase[t] + (int64_t)kt * 8 + offs[t], base + ldss[t]);
+  };
+
+  // A stage's raw operands in registers: code slices (16 bytes per lane)
+  // and the lane's two E4M3 block-scale bytes per fragment. The scales are
+  // converted to fp16 pairs where first needed, not where read: one wave per
+  // SIMD has no other wave to run while it waits for an LDS read.
+  struct RawA {
+    uint4 a[TM];
+    uint32_t s[TM];
+  };
+  struct RawB {
+    uint4 b[TN];
+    uint32_t s[TN];
+  };
+  auto read_a = [&](RawA& r, int slot) {
+    const uint8_t* base = smem + slot * STAGE;
+    const uint8_t* la = base + (wm * TM) * 1024 + r16 * 64 + grp * 16;
+    const uint8_t* sa = base + LA + LB + ((wm * TM) * 16 + r16) * 8 + grp * 2;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) r.a[i] = *reinterpret_cast<const uint4*>(la + i * 1024);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) r.s[i] = *reinterpret_cast<const uint16_t*>(sa + i * 128);
+  };
+  auto read_b = [&](RawB& r, int slot) {
+    const uint8_t* base = smem + slot * STAGE;
+    const uint8_t* lb = base + LA + (wn * TN) * 1024 + r16 * 64 + grp * 16;
+    const uint8_t* sb = base + LA + LB + LSA + ((wn * TN) * 16 + r16) * 8 + grp * 2;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) r.b[j] = *reinterpret_cast<const uint4*>(lb + j * 1024);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) r.s[j] = *reinterpret_cast<const uint16_t*>(sb + j * 128);
+  };
+  auto scale2 = [](uint32_t raw) -> half2_t { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false); };
+  // Pair p (of 4) of a fragment's decode for K slice q (elements 2p, 2p+1):
+  // the E2M1 convert, then the multiply by the block scale.
+  auto cvt = [](const uint4& w, int q, int p) -> half2_t {
+    const uint32_t x = word_of(w, q);
+    return p == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0)
+         : p == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1)
+         : p == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2)
+                  : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3);
+  };
+  auto mul = [](half2_t h, half2_t s2, int q) -> half2_t {
+    const _Float16 s = q < 2 ? s2[0] : s2[1];
+    return h * half2_t{s, s};
+  };
+  auto piece = [&](const uint4& w, half2_t s2, int q, int p) -> half2_t { return mul(cvt(w, q, p), s2, q); };
+  auto join = [](std::initializer_list<half2_t> l) -> half8_t {
+    const half2_t* h = l.begin();
+    return half8_t{h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+  };
+
+  floatx4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (s < nk) issue(kt0 + s, s);
+  if (nk >= 3) wait_vm_barrier<2 * NIW>();
+  else if (nk == 2) wait_vm_barrier<NIW>();
+  else wait_vm_barrier<0>();
+  RawA RA;
+  RawB RB;
+  read_a(RA, 0);
+  read_b(RB, 0);
+  half2_t sa[TM], sb[TN];                                // scales of the stage's fragments
+#pragma unroll
+  for (int i = 0; i < TM; ++i) sa[i] = scale2(RA.s[i]);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) sb[j] = scale2(RB.s[j]);
+  half8_t bd[TN], ad;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    bd[j] = join({piece(RB.b[j], sb[j], 0, 0), piece(RB.b[j], sb[j], 0, 1), piece(RB.b[j], sb[j], 0, 2),
+                  piece(RB.b[j], sb[j], 0, 3)});
+  }
+  ad = join({piece(RA.a[0], sa[0], 0, 0), piece(RA.a[0], sa[0], 0, 1), piece(RA.a[0], sa[0], 0, 2),
+             piece(RA.a[0], sa[0], 0, 3)});
+  mfma_guard();
+
+  // Stage it. While a stage it+1 follows, its B operands are read after the
+  // barrier at row 6 of slice 2 and decoded for its first slice during slice
+  // 3; its A operands are read at slice 3 (the first A block decoded at slice
+  // 3's last row). Each MFMA is followed by one decode pair (a convert and a
+  // multiply), pinned in that order; a fragment's scale pair is converted in
+  // the group of its first decode (A blocks 1-7 of a stage in slice 0). All
+  // stages run the same code, so the accumulators keep their registers: a
+  // stage with its own copy of the loop body lets the register allocator
+  // move them, and a compiler-inserted AGPR move right before an asm MFMA
+  // that reads it is a hazard the compiler does not see. The last stage reads
+  // (and decodes, unused) the next slot as it stands: no load targets it any
+  // more.
+  int slot = 0;                                          // slot of stage it
+  for (int it = 0; it < nk; ++it) {
+    const bool more = it + 1 < nk;
+    const int next = slot == S - 1 ? 0 : slot + 1;
+    RawA NA;
+    RawB NB;
+    half2_t nsb[TN], nsa0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q == 3) read_a(NA, next);
+      half8_t bn[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (q == 2 && i == 6) {
+          if (it + 2 < nk) wait_vm_barrier<NIW>();      // stage it+1 has landed
+          else if (more) wait_vm_barrier<0>();
+          if (it + 3 < nk) issue(kt0 + it + 3, slot);   // every wave has read stage it
+          read_b(NB, next);
+        }
+        // pieces 0-3: A block i+1 (or the next slice's block 0), pieces
+        // 4-7: B block i for the next slice; group j converts piece j and
+        // multiplies piece j-1, so no multiply waits on the convert just
+        // issued (the last piece's multiply closes group 7)
+        if (i < TM - 1) {
+          if (q == 0) sa[i + 1] = scale2(RA.s[i + 1]);
+        } else if (q == 3) {
+          nsa0 = scale2(NA.s[0]);
+        }
+        if (q == 3) nsb[i] = scale2(NB.s[i]);
+        auto cvt_j = [&](int j) -> half2_t {
+          if (j < 4) return i < TM - 1 ? cvt(RA.a[i + 1], q, j) : q < 3 ? cvt(RA.a[0], q + 1, j) : cvt(NA.a[0], 0, j);
+          return q < 3 ? cvt(RB.b[i], q + 1, j - 4) : cvt(NB.b[i], 0, j - 4);
+        };
+        auto mul_j = [&](int j, half2_t t) -> half2_t {
+          if (j < 4) return i < TM - 1 ? mul(t, sa[i + 1], q) : q < 3 ? mul(t, sa[0], q + 1) : mul(t, nsa0, 0);
+          return q < 3 ? mul(t, sb[i], q + 1) : mul(t, nsb[i], 0);
+        };
+        half2_t t[8], h[8];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          mfma_acc_agpr(acc[i][j], ad, bd[j]);
+          t[j] = cvt_j(j);
+          if (j > 0) h[j - 1] = mul_j(j - 1, t[j - 1]);
+          if (j == TN - 1) h[j] = mul_j(j, t[j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        ad = join({h[0], h[1], h[2], h[3]});
+        bn[i] = join({h[4], h[5], h[6], h[7]});
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bd[j] = bn[j];
+    }
+    RA = NA;
+    RB = NB;
+    sa[0] = nsa0;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sb[j] = nsb[j];
+    slot = next;
+    // before any accumulator read: at the end of every stage (under 1 % of
+    // its time) rather than after the loop, so that what the compiler places
+    // on the loop's exit edge comes after it; a guard on the last stage only
+    // branches inside the loop and its register allocation then spills
+    mfma_guard();
+  }
+
+  if constexpr (QO) {
+    static_assert(4 * 16 * (TN * 16 + 4) * 4 <= S * STAGE, "output staging fits in the operand ring");
+    store_tile_q<TM, TN>(g, acc, m0 + wm * 128, n0 + wn * 128, r16, grp, smem);
+  } else {
+    store_tile<TM, TN>(g, acc, m0 + wm * 128, n0 + wn * 128, r16, grp);
+  }
+}
+
 // Split-K reduction: C = 2^(ea+eb) * sum over splits, in split order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nsplit) {
   const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
@@ -483,10 +765,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_q_kernel(GemmArgs g, int ns
 // CU, running faster alone). The plan takes the cheapest shape, in units of
 // one round of 128x128 tiles; problems with fewer than 192 small tiles split
 // K so that about 256 workgroups run.
-static double big_tile_gain(int format) {
+// NVFP4 256x256 tiles (gemm_nvfp4_w1_kernel, one per CU) run their K loop
+// about 10 % faster than the 256x128 tiles but pay more per tile at its
+// ends (pipeline fill and the store of a 256 KiB tile, with no second
+// workgroup on the CU to overlap them): measured on MI355X, faster by 3-9 %
+// for K >= 8192 (4096x8192x28672 1.486 -> 1.359 ms), mixed at K = 4096 and
+// slower below (4096x8192x1024 0.069 -> 0.087 ms), so planned only for
+// K >= 8192.
+static double big_tile_gain(int format, int64_t K) {
   switch (format) {
     case SNIP_FP8_E4M3: return 1.15;
     case SNIP_MXFP4: return 1.03;
+    case SNIP_NVFP4: return K >= 8192 ? 1.18 : 0.0;
     default: return 1.02;
   }
 }
@@ -508,13 +798,14 @@ struct TileTimes {
   int64_t t128, t256, trect;
   double time128, time256, timerect;
 };
-static TileTimes tile_times(int format, int64_t M, int64_t N) {
+static TileTimes tile_times(int format, int64_t M, int64_t N, int64_t K) {
   TileTimes t;
   t.t256 = ceil_div(M, 256) * ceil_div(N, 256);
   t.t128 = ceil_div(M, 128) * ceil_div(N, 128);
   t.trect = ceil_div(M, 256) * ceil_div(N, 128);
   t.time128 = rounds2(t.t128);
-  t.time256 = format == SNIP_NVFP4 ? 1e30 : (double)ceil_div(t.t256, 256) * 2.0 / big_tile_gain(format);
+  const double g256 = big_tile_gain(format, K);
+  t.time256 = g256 > 0.0 ? (double)ceil_div(t.t256, 256) * 2.0 / g256 : 1e30;
   t.timerect = rect_gain(format) > 0.0 ? rounds2(t.trect) * 2.0 / rect_gain(format) : 1e30;
   // FP8 256x128 tiles whose last round is less than half full leave CUs idle
   // that the 128x128 tiles, three per CU, fill. Measured on MI355X for
@@ -527,7 +818,7 @@ static TileTimes tile_times(int format, int64_t M, int64_t N) {
 
 GemmPlan plan_gemm(int format, int64_t M, int64_t N, int64_t K) {
   GemmPlan p;
-  const TileTimes tt = tile_times(format, M, N);
+  const TileTimes tt = tile_times(format, M, N, K);
   const int64_t t256 = tt.t256, t128 = tt.t128, trect = tt.trect;
   const double time128 = tt.time128, time256 = tt.time256, timerect = tt.timerect;
   p.staged = 0;
@@ -600,9 +891,7 @@ static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
     }
   }
   if (p.bm == 256) {
-    // NVFP4 has no 256x256 instance: plan_gemm never picks it (its 256x128
-    // tiles are estimated faster at every size)
-    if constexpr (FMT == SNIP_NVFP4) return false;
+    if constexpr (FMT == SNIP_NVFP4) hipLaunchKernelGGL((gemm_nvfp4_w1_kernel<QO>), grid, dim3(NT), 0, s, g);
     else hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1, QO>), grid, dim3(NT), 0, s, g);
   } else if (p.staged) {
     if constexpr (QO) return false;
@@ -638,7 +927,7 @@ static bool pair_grouped(int format, const GemmArgs& g1, const GemmArgs& g2) {
   if (format != SNIP_FP8_E4M3 && format != SNIP_NVFP4) return false;
   const GemmPlan p1 = plan_gemm(format, g1.M, g1.N, g1.K), p2 = plan_gemm(format, g2.M, g2.N, g2.K);
   if (!(p1.ksplit == 1 && p2.ksplit == 1 && p1.bm >= 128 && p2.bm >= 128)) return false;
-  const TileTimes a = tile_times(format, g1.M, g1.N), b = tile_times(format, g2.M, g2.N);
+  const TileTimes a = tile_times(format, g1.M, g1.N, g1.K), b = tile_times(format, g2.M, g2.N, g2.K);
   auto planned = [](const TileTimes& t) { return std::min(t.time128, std::min(t.time256, t.timerect)); };
   const double separate = planned(a) * (double)g1.K + planned(b) * (double)g2.K;
   const double grouped = ((double)a.t128 * (double)g1.K + (double)b.t128 * (double)g2.K) / 512.0;
