@@ -226,13 +226,14 @@ def main():
     avg_launch_s = dom["ms"] / dom["launches"] * 1e-3
     flops_per_launch = dom["flops"] / dom["launches"]
     achieved = flops_per_launch / avg_launch_s / 1e12
-    kernel_prefix = f"void snip::gemm_kernel<{dom_fmt},"
     from sub_byte_mixed_amd import profiling
+    kernel_prefix = profiling.gemm_kernel_prefixes(dom_fmt)
     tr = profiling.load_traffic(wl.name, kernel_prefix)
     roofline = {
         "bound": "mfma",
-        "kernel": f"gemm_kernel<{S.FORMAT_NAMES[dom_fmt]}> (fp16 MFMA after exact decode)"
-        if dom_fmt in (S.NVFP4, S.FP8) else f"gemm_kernel<{S.FORMAT_NAMES[dom_fmt]}>",
+        "kernel": (f"every {S.FORMAT_NAMES[dom_fmt]} GEMM launch: "
+                   + " and ".join(k.replace("void snip::", "") + "...>" for k in kernel_prefix.split("|"))
+                   + (" (fp16 MFMA after exact decode)" if dom_fmt in (S.NVFP4, S.FP8) else "")),
         "achieved": round(achieved, 2), "peak": PEAK["fp16_tflops"], "unit": "TFLOP/s",
         "frac": round(achieved / PEAK["fp16_tflops"], 4),
         "traffic": tr["traffic_bytes_per_launch"] if tr else None,

@@ -120,15 +120,26 @@ def _counter_rows(path):
         return list(csv.DictReader(fh))
 
 
+def gemm_kernel_prefixes(fmt: int) -> str:
+    """Kernel-name prefixes of every GEMM kernel that runs format `fmt`,
+    '|'-separated: the tile kernels of gemm_kernel and, for NVFP4, the
+    256x256 one-wave-per-SIMD kernel."""
+    p = [f"void snip::gemm_kernel<{fmt},"]
+    if fmt == 2:
+        p.append("void snip::gemm_nvfp4_w1_kernel<")
+    return "|".join(p)
+
+
 def _per_dispatch(path, counter, prefix=None, contains=None):
     """{dispatch id: value} for the kernels whose name starts with `prefix`
-    (or contains `contains`)."""
+    (one of several, '|'-separated; or contains `contains`)."""
     out = {}
+    prefixes = tuple(prefix.split("|")) if prefix is not None else None
     for r in _counter_rows(path):
         if r["Counter_Name"] != counter:
             continue
         name = r["Kernel_Name"]
-        if prefix is not None and not name.startswith(prefix):
+        if prefixes is not None and not name.startswith(prefixes):
             continue
         if contains is not None and contains not in name:
             continue
@@ -239,7 +250,7 @@ def cmd_mfma(a):
              "LDS bytes |", "|---|---|---|---|---|---|---|"]
     total = 0.0
     for name in sorted(util, key=lambda n: -sum(util[n].values())):
-        if "gemm_kernel" not in name:
+        if "snip::gemm_" not in name:
             continue
         ud = util[name]
         fl = {k: sum(m.get(name, {}).values()) * 512 for k, m in mops.items()}
@@ -437,7 +448,8 @@ def cmd_traffic(a):
          "read_bytes_per_launch": round(mf * 1024 * f_r), "write_bytes_per_launch": round(mw * 1024 * f_w),
          "traffic_bytes_per_launch": round(mf * 1024 * f_r + mw * 1024 * f_w),
          "source_hash": source_hash()}
-    lines = [f"# HBM traffic of `{a.kernel}...` on the {a.workload} workload", "",
+    names = " and ".join(f"`{k}...`" for k in a.kernel.split("|"))
+    lines = [f"# HBM traffic of {names} on the {a.workload} workload", "",
              "Two rocprofv3 `--pmc` runs of the benchmark (FETCH_SIZE, then WRITE_SIZE; KiB per",
              "dispatch, averaged over the kernel's dispatches), each scaled by the factor that makes",
              f"a plain fp32 elementwise copy of {a.copy_mib} MiB (`torch.mul(x, 1.0, out=y)`) read and",
