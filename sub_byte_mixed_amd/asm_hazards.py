@@ -16,7 +16,8 @@ every path:
   accumulates into exactly the same registers touches its accumulator
   registers within ``AFTER_MFMA`` wait states;
 * into an asm MFMA backward, no instruction other than an MFMA writes one of
-  its A, B or C registers within ``BEFORE_MFMA`` wait states.
+  its A, B or C registers (or, for the scaled MFMAs, a scale register)
+  within ``BEFORE_MFMA`` wait states.
 
 Wait states are counted as the hardware documentation counts them: one per
 instruction, N + 1 for ``s_nop N``. The bounds are above what gfx950 asks
@@ -76,8 +77,10 @@ def _parse_insn(line: str, asm: bool) -> Insn:
     ops = [o.split()[0] for o in ops if o]
     ins = Insn(text=body, op=op, asm=asm)
     if op.startswith("v_mfma"):
+        # every register operand after the destination is read: A, B, C and,
+        # for the scaled MFMAs, the two scale registers
         ins.writes = _regs(ops[0])
-        for o in ops[1:4]:
+        for o in ops[1:]:
             ins.reads |= _regs(o)
         return ins
     dest_first = ops and not op.startswith(_NO_DEST) and (

@@ -682,6 +682,172 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g_in) {
   }
 }
 
+// acc += A . B on the scaled 4-bit MFMA (MX-FP4: E2M1 codes, one E8M0
+// scale per row and 32-element K block, passed in the instruction) with
+// the accumulator kept in place in AGPRs, as mfma_acc_agpr.
+// The instruction reads byte 0 of each scale register (op_sel 0); the
+// other bytes are ignored.
+__device__ __forceinline__ void mfma_mx_acc_agpr(floatx4_t& acc, const uint4& a, const uint4& b, uint32_t sa,
+                                                 uint32_t sb) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+               : "+a"(acc)
+               : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)), "v"(sa), "v"(sb));
+}
+
+// MX-FP4 on 256x256 tiles, one wave per SIMD, each wave a 128x128 sub-tile:
+// the structure of gemm_nvfp4_w1_kernel without a decode (the MFMA takes
+// the codes and block scales as they are). A stage (K = 128) is 64 MFMAs
+// per wave, 16 cycles each at the FP4 rate, against 16 LDS reads of codes,
+// 16 of scale bytes and 10 DMA instructions, so the ring runs 4 stages
+// deep (34 KiB each) and the next stage's operands are read during the
+// current one: after row 3 of the 8 MFMA rows a barrier (stage it+1 has
+// landed, every wave has read stage it) opens the refill of stage it's
+// slot with stage it+4, and the reads of stage it+1 go one per MFMA into
+// rows 4-7. Stages past the end reload the last one (never read as
+// operands), so every stage issues the same loads and waits the same.
+__global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
+  constexpr int S = 4, NU = 16;                            // stages; 16-row units per operand
+  constexpr int LA = NU * 1024, LB = NU * 1024;            // code bytes per stage
+  constexpr int LSA = NU * 16 * 4, LSB = NU * 16 * 4;      // E8M0 scale bytes per stage
+  constexpr int STAGE = LA + LB + LSA + LSB;
+  constexpr int NSA = LSA / 256, NSB = LSB / 256;          // scale DMA instructions
+  constexpr int IA = NU / 4, IB = NU / 4, IS = (NSA + NSB) / 4;
+  constexpr int NIW = IA + IB + IS;                        // DMA instructions per wave and stage
+  constexpr int TM = 8, TN = 8;
+  static_assert((S - 1) * NIW <= 63, "vmcnt range");
+  static_assert(NIW <= 4 * TN, "the refill fits in rows 4-7");
+  static_assert(NSA % 4 == 0 || (NSA + NSB) % 4 == 0, "scale DMA split over 4 waves");
+  __shared__ __align__(1024) uint8_t smem[S * STAGE];
+  if (finalize_workgroup(g_in)) return;
+
+  const GemmArgs& g = g_in;                                // grouped launches never take this kernel
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, grp = lane >> 4;
+  int tm, tn;
+  tile_coords(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+  const int64_t rowbytes = g.K / 128 * 64, srow = g.K / 32;
+  const int kt0 = (int)(blockIdx.y * g.kchunk / 128);
+  const int kt1 = min((int)(g.K / 128), (int)((blockIdx.y + 1) * g.kchunk / 128));
+  const int nk = kt1 - kt0;
+
+  // DMA sources: wave w loads code units w, w+4, ... of A and of B, and
+  // scale instructions w, w+4, ... (one instruction: 4 units of 16 rows x
+  // 4 bytes), A scales first
+  uint32_t offa[IA], offb[IB], offs[IS], ldss[IS];
+  const uint8_t* sbase[IS];
+#pragma unroll
+  for (int t = 0; t < IA; ++t)
+    offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + (lane & 3) * 16;
+#pragma unroll
+  for (int t = 0; t < IB; ++t)
+    offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
+#pragma unroll
+  for (int t = 0; t < IS; ++t) {
+    const int pp = wave + 4 * t;
+    const bool isa = pp < NSA;
+    const int p = isa ? pp : pp - NSA;
+    const int blk = 4 * p + (lane >> 4), r = lane & 15;
+    const int64_t row = isa ? min(m0 + blk * 16 + r, g.M - 1) : min(n0 + blk * 16 + r, g.N - 1);
+    offs[t] = (uint32_t)(row * srow);
+    sbase[t] = isa ? g.as : g.bs;
+    ldss[t] = LA + LB + pp * 256;                          // B scales follow the A scales
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  auto issue1 = [&](int kt, int slot, int d) {
+    const uint32_t base = lds0 + slot * STAGE;
+    if (d < IA) dma16(g.a + (int64_t)kt * 64 + offa[d], base + (wave + 4 * d) * 1024);
+    else if (d < IA + IB) dma16(g.b + (int64_t)kt * 64 + offb[d - IA], base + LA + (wave + 4 * (d - IA)) * 1024);
+    else dma4(sbase[d - IA - IB] + (int64_t)kt * 4 + offs[d - IA - IB], base + ldss[d - IA - IB]);
+  };
+
+  // A stage's operands in registers: code slices (lane (r16, grp) holds K
+  // elements 32 grp .. 32 grp + 31 of row r16) and, per fragment, the E8M0
+  // scales of row r16's four K blocks (one aligned LDS word), shifted so
+  // that byte 0 holds the lane's block grp
+  struct Frags {
+    uint4 a[TM], b[TN];
+    uint32_t sa[TM], sb[TN];                               // the row's 4 block scales; the lane's is byte grp
+  };
+  // read k of 32: A codes, B codes, A scales, B scales (8 each)
+  auto read1 = [&](Frags& f, int slot, int k) {
+    const uint8_t* base = smem + slot * STAGE;
+    if (k < 8) f.a[k] = *reinterpret_cast<const uint4*>(base + (wm * TM + k) * 1024 + r16 * 64 + grp * 16);
+    else if (k < 16) f.b[k - 8] = *reinterpret_cast<const uint4*>(base + LA + (wn * TN + k - 8) * 1024 + r16 * 64 + grp * 16);
+    else if (k < 24) f.sa[k - 16] = *reinterpret_cast<const uint32_t*>(base + LA + LB + ((wm * TM + k - 16) * 16 + r16) * 4);
+    else f.sb[k - 24] = *reinterpret_cast<const uint32_t*>(base + LA + LB + LSA + ((wn * TN + k - 24) * 16 + r16) * 4);
+  };
+
+  floatx4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int d = 0; d < NIW; ++d) issue1(min(kt0 + s, kt1 - 1), s, d);
+  wait_vm_barrier<(S - 1) * NIW>();                      // stage 0 has landed
+  Frags F;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) read1(F, 0, k);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    F.sa[i] >>= 8 * grp;
+    F.sb[i] >>= 8 * grp;
+  }
+  mfma_guard();
+
+  // Stage it with its operands in `cur`, reading stage it+1's into `nxt`.
+  // Two stages per loop iteration with the fragment sets swapped, so no
+  // registers are copied between stages (the loop holds a barrier, which
+  // keeps the compiler from unrolling it); an odd last stage follows.
+  int slot = 0;                                          // slot of stage it
+  auto stage = [&](int it, const Frags& cur, Frags& nxt) {
+    const int next = slot == S - 1 ? 0 : slot + 1;
+    const int kt_refill = min(kt0 + it + S, kt1 - 1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      // stage it+1 has landed (stages it+2, it+3 may still be in flight),
+      // every wave has read stage it
+      if (i == 4) wait_vm_barrier<(S - 2) * NIW>();
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        mfma_mx_acc_agpr(acc[i][j], cur.a[i], cur.b[j], cur.sa[i], cur.sb[j]);
+        // the refill: NIW loads, one per MFMA from row 4 on
+        if (i >= 4 && (i - 4) * TN + j < NIW) issue1(kt_refill, slot, (i - 4) * TN + j);
+        // next stage's reads, the earliest needed first: B codes and scales
+        // (row 0), A scales, A codes (A block i is first used in row i)
+        if (i >= 4) read1(nxt, next, i == 4 ? 8 + j : i == 5 ? 24 + j : i == 6 ? 16 + j : j);
+        // in the last row, the next stage's scale words (read in rows 5-6)
+        // get the lane's byte (K block grp) shifted to byte 0, long before
+        // an MFMA reads them
+        if (i == TM - 1) {
+          nxt.sa[j] >>= 8 * grp;
+          nxt.sb[j] >>= 8 * grp;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    slot = next;
+  };
+  // nk >= 1: K is a positive multiple of 128
+  Frags N;
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
+    stage(it, F, N);
+    stage(it + 1, N, F);
+  }
+  if (it < nk) stage(it, F, N);
+  mfma_guard();                                          // before any accumulator read
+  wait_vm_barrier<0>();                                  // the reloads have landed before the workgroup ends
+  store_tile<TM, TN>(g, acc, m0 + wm * 128, n0 + wn * 128, r16, grp);
+}
+
 // Split-K reduction: C = 2^(ea+eb) * sum over splits, in split order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int nsplit) {
   const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
@@ -892,6 +1058,7 @@ static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
   }
   if (p.bm == 256) {
     if constexpr (FMT == SNIP_NVFP4) hipLaunchKernelGGL((gemm_nvfp4_w1_kernel<QO>), grid, dim3(NT), 0, s, g);
+    else if constexpr (FMT == SNIP_MXFP4 && !QO) hipLaunchKernelGGL(gemm_mxfp4_w1_kernel, grid, dim3(NT), 0, s, g);
     else hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1, QO>), grid, dim3(NT), 0, s, g);
   } else if (p.staged) {
     if constexpr (QO) return false;

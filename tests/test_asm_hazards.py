@@ -55,6 +55,14 @@ def test_valu_write_right_before_operand_read_is_flagged():
     assert _violations(spaced)[1] == []
 
 
+def test_scale_operand_write_is_flagged():
+    # a scaled MFMA reads its two E8M0 scale registers as well
+    mx = (";;#ASMSTART\n\tv_mfma_scale_f32_16x16x128_f8f6f4 a[0:3], v[0:3], v[4:7], a[0:3], v8, v9 "
+          "op_sel_hi:[0,0,0] cbsz:4 blgp:4\n;;#ASMEND")
+    assert _violations("\n".join(["\tv_lshrrev_b32_e32 v9, v10, v11", mx]))[1]
+    assert _violations("\n".join(["\tv_lshrrev_b32_e32 v9, v10, v11", "\ts_nop 3", mx]))[1] == []
+
+
 def test_hazard_on_one_branch_path_is_flagged():
     # the straight-line order is safe; the taken branch skips the guard
     body = "\n".join([
