@@ -699,26 +699,38 @@ __device__ __forceinline__ void mfma_mx_acc_agpr(floatx4_t& acc, const uint4& a,
 // the structure of gemm_nvfp4_w1_kernel without a decode (the MFMA takes
 // the codes and block scales as they are). A stage (K = 128) is 64 MFMAs
 // per wave, 16 cycles each at the FP4 rate, against 16 LDS reads of codes,
-// 16 of scale bytes and 10 DMA instructions, so the ring runs 4 stages
-// deep (34 KiB each) and the next stage's operands are read during the
-// current one: after row 3 of the 8 MFMA rows a barrier (stage it+1 has
-// landed, every wave has read stage it) opens the refill of stage it's
+// 16 of scale words and 10 DMA instructions, so the code ring runs 4
+// stages deep (32 KiB each) and the next stage's operands are read during
+// the current one: after row 3 of the 8 MFMA rows a barrier (stage it+1
+// has landed, every wave has read stage it) opens the refill of stage it's
 // slot with stage it+4, and the reads of stage it+1 go one per MFMA into
 // rows 4-7. Stages past the end reload the last one (never read as
 // operands), so every stage issues the same loads and waits the same.
+//
+// Scales. A row holds 4 E8M0 bytes per stage, and rows lie K/32 bytes
+// apart, so loading one stage's scales costs one L2 request per row: as
+// many requests as the stage's 64-byte code segments (measured: without the
+// scale loads the kernel ran 26-34 % faster). They are loaded 4 stages at a
+// time instead, the 16 contiguous bytes of a row by a quad of lanes (one
+// request), into a 3-slot ring of 8 KiB groups (512 rows x 16 bytes). A
+// group's 32 instructions (16 rows each) are spread over the 4 stages that
+// run 8 to 5 stages before its first stage, 2 per wave and stage, so every
+// stage still issues 10 loads and group g is in LDS by the barrier that
+// precedes its first read (which waits for everything issued 3 or more
+// stages earlier).
 __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
-  constexpr int S = 4, NU = 16;                            // stages; 16-row units per operand
+  constexpr int S = 4, NU = 16;                            // code stages; 16-row units per operand
   constexpr int LA = NU * 1024, LB = NU * 1024;            // code bytes per stage
-  constexpr int LSA = NU * 16 * 4, LSB = NU * 16 * 4;      // E8M0 scale bytes per stage
-  constexpr int STAGE = LA + LB + LSA + LSB;
-  constexpr int NSA = LSA / 256, NSB = LSB / 256;          // scale DMA instructions
-  constexpr int IA = NU / 4, IB = NU / 4, IS = (NSA + NSB) / 4;
+  constexpr int STAGE = LA + LB;
+  constexpr int SG = 512 * 16, NG = 3;                     // scale group bytes (4 stages), ring slots
+  constexpr int IA = NU / 4, IB = NU / 4, IS = 2;          // per wave and stage: 32 instructions per group
   constexpr int NIW = IA + IB + IS;                        // DMA instructions per wave and stage
   constexpr int TM = 8, TN = 8;
   static_assert((S - 1) * NIW <= 63, "vmcnt range");
   static_assert(NIW <= 4 * TN, "the refill fits in rows 4-7");
-  static_assert(NSA % 4 == 0 || (NSA + NSB) % 4 == 0, "scale DMA split over 4 waves");
-  __shared__ __align__(1024) uint8_t smem[S * STAGE];
+  static_assert(4 * 4 * IS == 32, "a group is 32 instructions over 4 stages and 4 waves");
+  static_assert(S * STAGE + NG * SG <= 160 * 1024, "LDS");
+  __shared__ __align__(1024) uint8_t smem[S * STAGE + NG * SG];
   if (finalize_workgroup(g_in)) return;
 
   const GemmArgs& g = g_in;                                // grouped launches never take this kernel
@@ -734,51 +746,55 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
   const int kt1 = min((int)(g.K / 128), (int)((blockIdx.y + 1) * g.kchunk / 128));
   const int nk = kt1 - kt0;
 
-  // DMA sources: wave w loads code units w, w+4, ... of A and of B, and
-  // scale instructions w, w+4, ... (one instruction: 4 units of 16 rows x
-  // 4 bytes), A scales first
-  uint32_t offa[IA], offb[IB], offs[IS], ldss[IS];
-  const uint8_t* sbase[IS];
+  // code DMA sources: wave w loads units w, w+4, ... of A and of B
+  uint32_t offa[IA], offb[IB];
 #pragma unroll
   for (int t = 0; t < IA; ++t)
     offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + (lane & 3) * 16;
 #pragma unroll
   for (int t = 0; t < IB; ++t)
     offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
-#pragma unroll
-  for (int t = 0; t < IS; ++t) {
-    const int pp = wave + 4 * t;
-    const bool isa = pp < NSA;
-    const int p = isa ? pp : pp - NSA;
-    const int blk = 4 * p + (lane >> 4), r = lane & 15;
-    const int64_t row = isa ? min(m0 + blk * 16 + r, g.M - 1) : min(n0 + blk * 16 + r, g.N - 1);
-    offs[t] = (uint32_t)(row * srow);
-    sbase[t] = isa ? g.as : g.bs;
-    ldss[t] = LA + LB + pp * 256;                          // B scales follow the A scales
-  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto issue1 = [&](int kt, int slot, int d) {
+  const uint32_t sl0 = lds0 + S * STAGE;                   // scale ring
+  auto code1 = [&](int kt, int slot, int d) {
     const uint32_t base = lds0 + slot * STAGE;
     if (d < IA) dma16(g.a + (int64_t)kt * 64 + offa[d], base + (wave + 4 * d) * 1024);
-    else if (d < IA + IB) dma16(g.b + (int64_t)kt * 64 + offb[d - IA], base + LA + (wave + 4 * (d - IA)) * 1024);
-    else dma4(sbase[d - IA - IB] + (int64_t)kt * 4 + offs[d - IA - IB], base + ldss[d - IA - IB]);
+    else dma16(g.b + (int64_t)kt * 64 + offb[d - IA], base + LA + (wave + 4 * (d - IA)) * 1024);
+  };
+  // scale instruction k (of 32) of group gi: 16 rows (A rows for k < 16,
+  // then B rows), lane l the word l % 4 (stage 4 gi + l % 4) of row l / 4;
+  // words past the last stage repeat the last stage's (kept in the row)
+  auto scale1 = [&](int gi, int k) {
+    const bool isa = k < 16;
+    const int64_t row = isa ? min(m0 + (k & 15) * 16 + (lane >> 2), g.M - 1)
+                            : min(n0 + (k & 15) * 16 + (lane >> 2), g.N - 1);
+    const int word = min(kt0 + 4 * gi + (lane & 3), kt1 - 1);
+    dma4((isa ? g.as : g.bs) + row * srow + word * 4, sl0 + (gi % NG) * SG + k * 256);
+  };
+  // the loads stage it issues (d of NIW): codes of stage it+4, then phase
+  // it % 4 of scale group it/4 + 2
+  auto issue1 = [&](int it, int slot, int d) {
+    if (d < IA + IB) code1(min(kt0 + it + S, kt1 - 1), slot, d);
+    else scale1(it / 4 + 2, (it & 3) * 8 + wave * 2 + (d - IA - IB));
   };
 
   // A stage's operands in registers: code slices (lane (r16, grp) holds K
-  // elements 32 grp .. 32 grp + 31 of row r16) and, per fragment, the E8M0
-  // scales of row r16's four K blocks (one aligned LDS word), shifted so
-  // that byte 0 holds the lane's block grp
+  // elements 32 grp .. 32 grp + 31 of row r16) and, per fragment, row
+  // r16's 4 block scales of the stage (one LDS word), shifted so that byte
+  // 0 holds the lane's block grp
   struct Frags {
     uint4 a[TM], b[TN];
-    uint32_t sa[TM], sb[TN];                               // the row's 4 block scales; the lane's is byte grp
+    uint32_t sa[TM], sb[TN];
   };
-  // read k of 32: A codes, B codes, A scales, B scales (8 each)
-  auto read1 = [&](Frags& f, int slot, int k) {
+  // read k of 32 of stage it (code slot `slot`): A codes, B codes, A scales,
+  // B scales (8 each)
+  auto read1 = [&](Frags& f, int it, int slot, int k) {
     const uint8_t* base = smem + slot * STAGE;
+    const uint8_t* sg = smem + S * STAGE + ((it / 4) % NG) * SG + (it & 3) * 4;
     if (k < 8) f.a[k] = *reinterpret_cast<const uint4*>(base + (wm * TM + k) * 1024 + r16 * 64 + grp * 16);
     else if (k < 16) f.b[k - 8] = *reinterpret_cast<const uint4*>(base + LA + (wn * TN + k - 8) * 1024 + r16 * 64 + grp * 16);
-    else if (k < 24) f.sa[k - 16] = *reinterpret_cast<const uint32_t*>(base + LA + LB + ((wm * TM + k - 16) * 16 + r16) * 4);
-    else f.sb[k - 24] = *reinterpret_cast<const uint32_t*>(base + LA + LB + LSA + ((wn * TN + k - 24) * 16 + r16) * 4);
+    else if (k < 24) f.sa[k - 16] = *reinterpret_cast<const uint32_t*>(sg + ((wm * TM + k - 16) * 16 + r16) * 16);
+    else f.sb[k - 24] = *reinterpret_cast<const uint32_t*>(sg + 4096 + ((wn * TN + k - 24) * 16 + r16) * 16);
   };
 
   floatx4_t acc[TM][TN];
@@ -787,14 +803,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+  // prologue: scale group 0, then code stages 0-3 each with a quarter of
+  // scale group 1, so that every stage's loads number NIW
 #pragma unroll
-  for (int s = 0; s < S; ++s)
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int d = 0; d < NIW; ++d) issue1(min(kt0 + s, kt1 - 1), s, d);
-  wait_vm_barrier<(S - 1) * NIW>();                      // stage 0 has landed
+    for (int t = 0; t < IS; ++t) scale1(0, p * 8 + wave * 2 + t);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+#pragma unroll
+    for (int d = 0; d < IA + IB; ++d) code1(min(kt0 + s, kt1 - 1), s, d);
+#pragma unroll
+    for (int t = 0; t < IS; ++t) scale1(1, s * 8 + wave * 2 + t);
+  }
+  wait_vm_barrier<(S - 1) * NIW>();                      // scale group 0 and code stage 0 have landed
   Frags F;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) read1(F, 0, k);
+  for (int k = 0; k < 32; ++k) read1(F, 0, 0, k);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     F.sa[i] >>= 8 * grp;
@@ -806,10 +831,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
   // Two stages per loop iteration with the fragment sets swapped, so no
   // registers are copied between stages (the loop holds a barrier, which
   // keeps the compiler from unrolling it); an odd last stage follows.
-  int slot = 0;                                          // slot of stage it
+  int slot = 0;                                          // code slot of stage it
   auto stage = [&](int it, const Frags& cur, Frags& nxt) {
     const int next = slot == S - 1 ? 0 : slot + 1;
-    const int kt_refill = min(kt0 + it + S, kt1 - 1);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       // stage it+1 has landed (stages it+2, it+3 may still be in flight),
@@ -819,10 +843,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
       for (int j = 0; j < TN; ++j) {
         mfma_mx_acc_agpr(acc[i][j], cur.a[i], cur.b[j], cur.sa[i], cur.sb[j]);
         // the refill: NIW loads, one per MFMA from row 4 on
-        if (i >= 4 && (i - 4) * TN + j < NIW) issue1(kt_refill, slot, (i - 4) * TN + j);
+        if (i >= 4 && (i - 4) * TN + j < NIW) issue1(it, slot, (i - 4) * TN + j);
         // next stage's reads, the earliest needed first: B codes and scales
         // (row 0), A scales, A codes (A block i is first used in row i)
-        if (i >= 4) read1(nxt, next, i == 4 ? 8 + j : i == 5 ? 24 + j : i == 6 ? 16 + j : j);
+        if (i >= 4) read1(nxt, it + 1, next, i == 4 ? 8 + j : i == 5 ? 24 + j : i == 6 ? 16 + j : j);
         // in the last row, the next stage's scale words (read in rows 5-6)
         // get the lane's byte (K block grp) shifted to byte 0, long before
         // an MFMA reads them
