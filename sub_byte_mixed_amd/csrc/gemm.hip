@@ -62,6 +62,8 @@
 // workgroups into fp32 partials that a second kernel sums in a fixed order.
 #include "gemm_common.h"
 
+#include <utility>
+
 namespace snip {
 
 constexpr int NT = 256;
@@ -93,6 +95,17 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
                : "memory", "m0");
 }
 
+// The same with a wave-uniform base address (scalar registers) and a 32-bit
+// per-lane offset: no per-lane address arithmetic.
+__device__ __forceinline__ void dma16s(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector-memory loads are outstanding
 // and all its LDS reads have returned, then barrier. One asm statement with
 // a memory clobber, so that no LDS access moves across it and no implicit
@@ -119,6 +132,17 @@ __device__ __forceinline__ half8_t fp8x8_to_half8(uint32_t w0, uint32_t w1) {
   const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
   const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
   return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{}):
+// a loop unrolled whatever the size of its body.
+template <class F, int... I>
+__device__ __forceinline__ void static_unroll_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_unroll(F&& f) {
+  static_unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
@@ -421,6 +445,60 @@ __device__ __forceinline__ void mfma_guard() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Epilogue of a wave's 128x128 sub-tile whose MFMAs took B as the first
+// operand: lane (r16, grp) holds C[r0 + 16 i + r16][c0 + 16 j + 4 grp + v],
+// v = 0..3, so each 16x16 block is one 16-byte write per lane, scaled by
+// 2^e. A sub-tile wholly inside C with 16-byte aligned rows is stored as
+// TM * TN such writes per lane, all lanes active; otherwise element by
+// element with bounds checks. Returns true for the first form.
+template <int TM, int TN>
+__device__ __forceinline__ bool store_tile_rows(const GemmArgs& g, const floatx4_t (&acc)[TM][TN], int64_t r0,
+                                                int64_t c0, int r16, int grp, int e) {
+  if (r0 + 16 * TM <= g.M && c0 + 16 * TN <= g.N && (g.ldc & 3) == 0 && ((uintptr_t)g.c & 15) == 0) {
+    // one lane address, stepped by 16 rows per row block (kept opaque, so
+    // that no per-block addresses are precomputed into registers: the
+    // caller's next-stage operands are live here)
+    float* rowp = g.c + (r0 + r16) * g.ldc + c0 + 4 * grp;
+    int64_t step = 16 * g.ldc;
+    asm volatile("" : "+s"(step));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        *reinterpret_cast<floatx4_t*>(rowp + j * 16) =
+            floatx4_t{ldexpf(acc[i][j][0], e), ldexpf(acc[i][j][1], e), ldexpf(acc[i][j][2], e),
+                      ldexpf(acc[i][j][3], e)};
+      rowp += step;
+      asm volatile("" : "+v"(rowp));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return true;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = r0 + i * 16 + r16, col = c0 + j * 16 + 4 * grp + v;
+        if (row < g.M && col < g.N) g.c[row * g.ldc + col] = ldexpf(acc[i][j][v], e);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  return false;
+}
+
+// Multiprocessors (CUs) of the current device, cached per device.
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
 // NVFP4 on 256x256 tiles, one wave per SIMD, each wave a 128x128 sub-tile.
 //
 // The NVFP4 decode costs one VALU instruction per element (half a
@@ -438,11 +516,27 @@ __device__ __forceinline__ void mfma_guard() {
 // MFMAs). The stage's raw codes and scales are in registers, read from the
 // LDS ring before its last slice: a barrier there (stage it+1 has landed,
 // every wave has read stage it) lets the wave refill stage it's slot with
-// stage it+3 and read stage it+1, whose first slice it decodes during the
-// last slice of stage it. Ring: 3 stages of K = 128 (36 KiB each).
+// stage it+4 and read stage it+1, whose first slice it decodes during the
+// last slice of stage it. Ring: 4 stages of K = 128 (36 KiB each).
+//
+// Persistent (without QO): the launch has one workgroup per CU, P in all,
+// and workgroup b runs tiles b, b + P, b + 2P, ... Every tile takes the same
+// time, so with one tile per workgroup each round of 256 tiles ends with all
+// of them writing their 256 KiB at once, and the next round's tiles start
+// only then (measured on MI355X: the kernel without its C store was 13 %
+// faster at K = 4096 and 6 % at K = 8192). Here a tile's end loads the next
+// tile's first four stages, then issues the tile's store, which drains
+// while the next tile multiplies. The MFMAs take B as the first operand,
+// so a lane's four results of a 16x16 block lie in one row of C and the
+// store is 64 16-byte writes per lane. Loads issued after it share their
+// counter (vmcnt counts loads and stores, in order): in the first three
+// stages after a store, the wait for the next stage allows 63 operations in
+// flight, which the 64 writes issued after that stage's loads guarantee;
+// the fourth stage's wait covers the store. QO runs one tile per
+// workgroup: its epilogue stages C in the ring.
 template <bool QO>
-__global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g_in) {
-  constexpr int S = 3, NU = 16;                            // stages; 16-row units per operand
+__global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
+  constexpr int S = 4, NU = 16;                            // stages; 16-row units per operand
   constexpr int LA = NU * 1024, LB = NU * 1024;            // code bytes per stage
   constexpr int LSA = NU * 16 * 8, LSB = NU * 16 * 8;      // scale bytes per stage
   constexpr int STAGE = LA + LB + LSA + LSB;
@@ -450,72 +544,66 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g_in) {
   constexpr int IA = NU / 4, IB = NU / 4, IS = (NSA + NSB) / 4;
   constexpr int NIW = IA + IB + IS;                        // DMA instructions per wave and stage
   constexpr int TM = 8, TN = 8;                            // 16x16 MFMA tiles per wave
-  static_assert(2 * NIW <= 63, "vmcnt range");
+  static_assert((S - 1) * NIW <= 63, "vmcnt range");
+  static_assert(TM * TN >= 63, "a tile's 16-byte writes alone fill the vmcnt window");
   __shared__ __align__(1024) uint8_t smem[S * STAGE];
-  if (finalize_workgroup(g_in)) return;
 
-  GemmArgs g = g_in;
-  int tile = blockIdx.x;
-  if (g_in.nsec && tile >= g_in.tiles_m * g_in.tiles_n) {
-    tile -= g_in.tiles_m * g_in.tiles_n;
-    g.a = g_in.sec.a;
-    g.b = g_in.sec.b;
-    g.as = g_in.sec.as;
-    g.bs = g_in.sec.bs;
-    g.ea = g_in.sec.ea;
-    g.eb = g_in.sec.eb;
-    g.c = g_in.sec.c;
-    g.M = g_in.sec.M;
-    g.N = g_in.sec.N;
-    g.K = g_in.sec.K;
-    g.ldc = g_in.sec.ldc;
-    g.kchunk = g_in.sec.K;
-    g.tiles_m = g_in.sec.tiles_m;
-    g.tiles_n = g_in.sec.tiles_n;
+  const int P = (int)gridDim.x - g.fin.n;                  // tile workgroups
+  if ((int)blockIdx.x >= P) {
+    if (blockIdx.y == 0) finalize_one(g.fin.j[blockIdx.x - P]);
+    return;
   }
+  const int tiles = g.tiles_m * g.tiles_n;
+  const int nk = (int)(g.K / 128);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int r16 = lane & 15, grp = lane >> 4;
-  int tm, tn;
-  tile_coords(tile, g.tiles_m, g.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
   const int64_t rowbytes = g.K / 128 * 64, srow = g.K / 16;
-  const int kt0 = (int)(blockIdx.y * g.kchunk / 128);
-  const int kt1 = min((int)(g.K / 128), (int)((blockIdx.y + 1) * g.kchunk / 128));
-  const int nk = kt1 - kt0;
 
-  // DMA sources, as in gemm_kernel with one unit per stage: wave w loads
-  // code units w, w+4, ... of A and of B and scale instructions w, w+4, ...
-  uint32_t offa[IA], offb[IB], offs[IS], ldss[IS];
-  const uint8_t* sbase[IS];                                // A or B scales, chosen once
+  // DMA sources of the tile at (m0, n0), as in gemm_kernel with one unit per
+  // stage: wave w loads code units w, w+4, ... of A and of B and scale
+  // instructions w, w+4, ... (the first two A's, the last two B's); rows
+  // past M or N read the last row. Per lane a 32-bit offset from the
+  // operand's start.
+  static_assert(NSA == 8 && NSB == 8 && IS == 4, "scale instructions 0-1 of a wave load A, 2-3 load B");
+  uint32_t offa[IA], offb[IB], offs[IS];
+  auto sources = [&](int64_t m0, int64_t n0) {
 #pragma unroll
-  for (int t = 0; t < IA; ++t)
-    offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + (lane & 3) * 16;
+    for (int t = 0; t < IA; ++t)
+      offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + (lane & 3) * 16;
 #pragma unroll
-  for (int t = 0; t < IB; ++t)
-    offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
+    for (int t = 0; t < IB; ++t)
+      offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
 #pragma unroll
-  for (int t = 0; t < IS; ++t) {
-    const int pp = wave + 4 * t;
-    const bool isa = pp < NSA;
-    const int p = isa ? pp : pp - NSA;
-    const int blk = 2 * p + (lane >> 5), r = (lane & 31) >> 1, part = (lane & 1) * 4;
-    const int64_t row = isa ? min(m0 + blk * 16 + r, g.M - 1) : min(n0 + blk * 16 + r, g.N - 1);
-    offs[t] = (uint32_t)(row * srow) + part;
-    sbase[t] = isa ? g.as : g.bs;
-    ldss[t] = LA + LB + pp * 256;                          // B scales follow the A scales
-  }
+    for (int t = 0; t < IS; ++t) {
+      const int pp = wave + 4 * t;
+      const bool isa = pp < NSA;
+      const int p = isa ? pp : pp - NSA;
+      const int blk = 2 * p + (lane >> 5), r = (lane & 31) >> 1, part = (lane & 1) * 4;
+      const int64_t row = isa ? min(m0 + blk * 16 + r, g.M - 1) : min(n0 + blk * 16 + r, g.N - 1);
+      offs[t] = (uint32_t)(row * srow) + part;
+    }
+  };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-  auto issue = [&](int kt, int slot) {
-    const uint32_t base = lds0 + slot * STAGE;
+  // stage kt of the tile whose rows lie dm (A) and dn (B) rows past the
+  // tile the offsets were worked out for; the bases are scalar, and the
+  // wave's LDS base is made opaque per call so that the compiler does not
+  // keep each instruction's LDS address in a register of its own
+  auto issue = [&](int kt, int slot, int dm, int dn) {
+    uint32_t lw = lds0 + slot * STAGE + wave * 1024, ls = lds0 + slot * STAGE + LA + LB + wave * 256;
+    asm volatile("" : "+s"(lw), "+s"(ls));
+    const uint8_t* pa = g.a + (int64_t)dm * rowbytes + (int64_t)kt * 64;
+    const uint8_t* pb = g.b + (int64_t)dn * rowbytes + (int64_t)kt * 64;
+    const uint8_t* psa = g.as + (int64_t)dm * srow + (int64_t)kt * 8;
+    const uint8_t* psb = g.bs + (int64_t)dn * srow + (int64_t)kt * 8;
 #pragma unroll
-    for (int t = 0; t < IA; ++t) dma16(g.a + (int64_t)kt * 64 + offa[t], base + (wave + 4 * t) * 1024);
+    for (int t = 0; t < IA; ++t) dma16s(pa, offa[t], lw + t * 4096);
 #pragma unroll
-    for (int t = 0; t < IB; ++t) dma16(g.b + (int64_t)kt * 64 + offb[t], base + LA + (wave + 4 * t) * 1024);
+    for (int t = 0; t < IB; ++t) dma16s(pb, offb[t], lw + LA + t * 4096);
 #pragma unroll
-    for (int t = 0; t < IS; ++t) dma4(sbase[t] + (int64_t)kt * 8 + offs[t], base + ldss[t]);
+    for (int t = 0; t < IS; ++t) dma4s(t < 2 ? psa : psb, offs[t], ls + t * 1024);   // B scales follow the A scales
   };
 
   // A stage's raw operands in registers: code slices (16 bytes per lane)
@@ -574,113 +662,190 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g_in) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+  const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
+  auto interior = [&](int64_t r0, int64_t c0) { return r0 + 256 <= g.M && c0 + 256 <= g.N; };
+  // Whether tile `tile` at (m0, n0) loads the first stages of the
+  // workgroup's next tile during its own last stages, through its own
+  // offsets shifted by (dm, dn) rows: both tiles wholly inside A and B, so
+  // that neither has clamped rows.
+  bool ahead = false;
+  int dm = 0, dn = 0;
+  auto plan_ahead = [&](int tile, int64_t m0, int64_t n0) {
+    ahead = false;
+    if (nk >= S && tile + P < tiles && interior(m0, n0)) {
+      int tm2, tn2;
+      tile_coords(tile + P, g.tiles_m, g.tiles_n, tm2, tn2);
+      if (interior((int64_t)tm2 * 256, (int64_t)tn2 * 256)) {
+        ahead = true;
+        dm = (int)((int64_t)tm2 * 256 - m0);
+        dn = (int)((int64_t)tn2 * 256 - n0);
+      }
+    }
+  };
+  int tile = blockIdx.x;
+  int tm, tn;
+  tile_coords(tile, g.tiles_m, g.tiles_n, tm, tn);
+  int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
+  sources(m0, n0);
+  int slot = 0;                                          // slot of the stage to multiply next
 #pragma unroll
   for (int s = 0; s < S; ++s)
-    if (s < nk) issue(kt0 + s, s);
-  if (nk >= 3) wait_vm_barrier<2 * NIW>();
-  else if (nk == 2) wait_vm_barrier<NIW>();
-  else wait_vm_barrier<0>();
-  RawA RA;
-  RawB RB;
-  read_a(RA, 0);
-  read_b(RB, 0);
-  half2_t sa[TM], sb[TN];                                // scales of the stage's fragments
+    if (s < nk) issue(s, s, 0, 0);
+  if constexpr (!QO) plan_ahead(tile, m0, n0);
+  bool stored = false;                                   // a store was issued after this tile's first loads
+  for (;;) {
+    if (stored) wait_vm_barrier<63>();                   // the store's 64 writes follow the loads
+    else if (nk >= 4) wait_vm_barrier<3 * NIW>();
+    else if (nk == 3) wait_vm_barrier<2 * NIW>();
+    else if (nk == 2) wait_vm_barrier<NIW>();
+    else wait_vm_barrier<0>();
+    RawA RA;
+    RawB RB;
+    read_a(RA, slot);
+    read_b(RB, slot);
+    half2_t sa[TM], sb[TN];                              // scales of the stage's fragments
 #pragma unroll
-  for (int i = 0; i < TM; ++i) sa[i] = scale2(RA.s[i]);
+    for (int i = 0; i < TM; ++i) sa[i] = scale2(RA.s[i]);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) sb[j] = scale2(RB.s[j]);
-  half8_t bd[TN], ad;
+    for (int j = 0; j < TN; ++j) sb[j] = scale2(RB.s[j]);
+    half8_t bd[TN], ad;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    bd[j] = join({piece(RB.b[j], sb[j], 0, 0), piece(RB.b[j], sb[j], 0, 1), piece(RB.b[j], sb[j], 0, 2),
-                  piece(RB.b[j], sb[j], 0, 3)});
-  }
-  ad = join({piece(RA.a[0], sa[0], 0, 0), piece(RA.a[0], sa[0], 0, 1), piece(RA.a[0], sa[0], 0, 2),
-             piece(RA.a[0], sa[0], 0, 3)});
-  mfma_guard();
-
-  // Stage it. While a stage it+1 follows, its B operands are read after the
-  // barrier at row 6 of slice 2 and decoded for its first slice during slice
-  // 3; its A operands are read at slice 3 (the first A block decoded at slice
-  // 3's last row). Each MFMA is followed by one decode pair (a convert and a
-  // multiply), pinned in that order; a fragment's scale pair is converted in
-  // the group of its first decode (A blocks 1-7 of a stage in slice 0). All
-  // stages run the same code, so the accumulators keep their registers: a
-  // stage with its own copy of the loop body lets the register allocator
-  // move them, and a compiler-inserted AGPR move right before an asm MFMA
-  // that reads it is a hazard the compiler does not see. The last stage reads
-  // (and decodes, unused) the next slot as it stands: no load targets it any
-  // more.
-  int slot = 0;                                          // slot of stage it
-  for (int it = 0; it < nk; ++it) {
-    const bool more = it + 1 < nk;
-    const int next = slot == S - 1 ? 0 : slot + 1;
-    RawA NA;
-    RawB NB;
-    half2_t nsb[TN], nsa0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q == 3) read_a(NA, next);
-      half8_t bn[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        if (q == 2 && i == 6) {
-          if (it + 2 < nk) wait_vm_barrier<NIW>();      // stage it+1 has landed
-          else if (more) wait_vm_barrier<0>();
-          if (it + 3 < nk) issue(kt0 + it + 3, slot);   // every wave has read stage it
-          read_b(NB, next);
-        }
-        // pieces 0-3: A block i+1 (or the next slice's block 0), pieces
-        // 4-7: B block i for the next slice; group j converts piece j and
-        // multiplies piece j-1, so no multiply waits on the convert just
-        // issued (the last piece's multiply closes group 7)
-        if (i < TM - 1) {
-          if (q == 0) sa[i + 1] = scale2(RA.s[i + 1]);
-        } else if (q == 3) {
-          nsa0 = scale2(NA.s[0]);
-        }
-        if (q == 3) nsb[i] = scale2(NB.s[i]);
-        auto cvt_j = [&](int j) -> half2_t {
-          if (j < 4) return i < TM - 1 ? cvt(RA.a[i + 1], q, j) : q < 3 ? cvt(RA.a[0], q + 1, j) : cvt(NA.a[0], 0, j);
-          return q < 3 ? cvt(RB.b[i], q + 1, j - 4) : cvt(NB.b[i], 0, j - 4);
-        };
-        auto mul_j = [&](int j, half2_t t) -> half2_t {
-          if (j < 4) return i < TM - 1 ? mul(t, sa[i + 1], q) : q < 3 ? mul(t, sa[0], q + 1) : mul(t, nsa0, 0);
-          return q < 3 ? mul(t, sb[i], q + 1) : mul(t, nsb[i], 0);
-        };
-        half2_t t[8], h[8];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          mfma_acc_agpr(acc[i][j], ad, bd[j]);
-          t[j] = cvt_j(j);
-          if (j > 0) h[j - 1] = mul_j(j - 1, t[j - 1]);
-          if (j == TN - 1) h[j] = mul_j(j, t[j]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        ad = join({h[0], h[1], h[2], h[3]});
-        bn[i] = join({h[4], h[5], h[6], h[7]});
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bd[j] = bn[j];
+    for (int j = 0; j < TN; ++j) {
+      bd[j] = join({piece(RB.b[j], sb[j], 0, 0), piece(RB.b[j], sb[j], 0, 1), piece(RB.b[j], sb[j], 0, 2),
+                    piece(RB.b[j], sb[j], 0, 3)});
     }
-    RA = NA;
-    RB = NB;
-    sa[0] = nsa0;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sb[j] = nsb[j];
-    slot = next;
-    // before any accumulator read: at the end of every stage (under 1 % of
-    // its time) rather than after the loop, so that what the compiler places
-    // on the loop's exit edge comes after it; a guard on the last stage only
-    // branches inside the loop and its register allocation then spills
+    ad = join({piece(RA.a[0], sa[0], 0, 0), piece(RA.a[0], sa[0], 0, 1), piece(RA.a[0], sa[0], 0, 2),
+               piece(RA.a[0], sa[0], 0, 3)});
     mfma_guard();
+
+    // Stage it. While a stage it+1 follows, its B operands are read after
+    // the barrier at row 6 of slice 2 and decoded for its first slice during
+    // slice 3; its A operands are read at slice 3 (the first A block decoded
+    // at slice 3's last row). Each MFMA is followed by one decode pair (a
+    // convert and a multiply), pinned in that order; a fragment's scale pair
+    // is converted in the group of its first decode (A blocks 1-7 of a stage
+    // in slice 0). All stages run the same code, so the accumulators keep
+    // their registers: a stage with its own copy of the loop body lets the
+    // register allocator move them, and a compiler-inserted AGPR move right
+    // before an asm MFMA that reads it is a hazard the compiler does not
+    // see. The last stage reads (and decodes, unused) the next slot as it
+    // stands: no load targets it any more.
+    for (int it = 0; it < nk; ++it) {                    // stage it, in slot `slot`
+      const bool more = it + 1 < nk;
+      const int next = slot == S - 1 ? 0 : slot + 1;
+      RawA NA;
+      RawB NB;
+      half2_t nsb[TN], nsa0;
+      // slices and row blocks unrolled by templates: the unroller's size
+      // limit would otherwise leave the slice loop rolled, its register
+      // arrays indexed at run time (in scratch)
+      static_unroll<4>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (q == 3) read_a(NA, next);
+        half8_t bn[TN];
+        static_unroll<TM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (q == 2 && i == 6) {
+            // the stream's stage it+1 has landed (and, as below, every wave
+            // has read stage it). With `ahead` the stream runs on into the
+            // next tile, two stages always following
+            if (more || ahead) {
+              if (stored && it < S - 1) wait_vm_barrier<63>();
+              else if (ahead || it + 3 < nk) wait_vm_barrier<2 * NIW>();
+              else if (it + 2 < nk) wait_vm_barrier<NIW>();
+              else wait_vm_barrier<0>();
+            }
+            // every wave has read stage it: its slot takes stage it+4, or
+            // the next tile's stage it+4-nk
+            const bool own = it + S < nk;
+            if (own || ahead) issue(own ? it + S : it + S - nk, slot, own ? 0 : dm, own ? 0 : dn);
+            read_b(NB, next);
+          }
+          // pieces 0-3: A block i+1 (or the next slice's block 0), pieces
+          // 4-7: B block i for the next slice; group j converts piece j and
+          // multiplies piece j-1, so no multiply waits on the convert just
+          // issued (the last piece's multiply closes group 7)
+          if constexpr (i < TM - 1) {
+            if constexpr (q == 0) sa[i + 1] = scale2(RA.s[i + 1]);
+          } else if constexpr (q == 3) {
+            nsa0 = scale2(NA.s[0]);
+          }
+          if constexpr (q == 3) nsb[i] = scale2(NB.s[i]);
+          auto cvt_j = [&](int j) -> half2_t {
+            if (j < 4) return i < TM - 1 ? cvt(RA.a[i + 1], q, j) : q < 3 ? cvt(RA.a[0], q + 1, j) : cvt(NA.a[0], 0, j);
+            return q < 3 ? cvt(RB.b[i], q + 1, j - 4) : cvt(NB.b[i], 0, j - 4);
+          };
+          auto mul_j = [&](int j, half2_t t) -> half2_t {
+            if (j < 4) return i < TM - 1 ? mul(t, sa[i + 1], q) : q < 3 ? mul(t, sa[0], q + 1) : mul(t, nsa0, 0);
+            return q < 3 ? mul(t, sb[i], q + 1) : mul(t, nsb[i], 0);
+          };
+          half2_t t[8], h[8];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (QO) mfma_acc_agpr(acc[i][j], ad, bd[j]);
+            else mfma_acc_agpr(acc[i][j], bd[j], ad);  // C transposed: a lane's results lie in one row
+            t[j] = cvt_j(j);
+            asm volatile("" : "+v"(t[j]));             // computed here, not sunk to its use
+            if (j > 0) {
+              h[j - 1] = mul_j(j - 1, t[j - 1]);
+              asm volatile("" : "+v"(h[j - 1]));
+            }
+            if (j == TN - 1) {
+              h[j] = mul_j(j, t[j]);
+              asm volatile("" : "+v"(h[j]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          ad = join({h[0], h[1], h[2], h[3]});
+          bn[i] = join({h[4], h[5], h[6], h[7]});
+        });
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bd[j] = bn[j];
+      });
+      RA = NA;
+      RB = NB;
+      sa[0] = nsa0;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb[j] = nsb[j];
+      slot = next;
+      // before any accumulator read: at the end of every stage (under 1 %
+      // of its time) rather than after the loop, so that what the compiler
+      // places on the loop's exit edge comes after it
+      mfma_guard();
+    }
+    if constexpr (QO) break;
+    // the tile is complete: unless its last stages loaded them, the next
+    // tile's first stages go into the ring once every wave is done with
+    // it; then this tile's store is issued
+    const int64_t cm0 = m0, cn0 = n0;
+    tile += P;
+    const bool last = tile >= tiles;
+    if (!last) {
+      tile_coords(tile, g.tiles_m, g.tiles_n, tm, tn);
+      m0 = (int64_t)tm * 256;
+      n0 = (int64_t)tn * 256;
+      sources(m0, n0);
+      if (!ahead) {
+        wait_vm_barrier<63>();
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+          if (s < nk) issue(s, (slot + s) & (S - 1), 0, 0);
+      }
+      plan_ahead(tile, m0, n0);
+    }
+    stored = store_tile_rows<TM, TN>(g, acc, cm0 + wm * 128, cn0 + wn * 128, r16, grp, e);
+    if (!stored) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the checked form may write less
+    if (last) break;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    mfma_guard();                                        // the cleared accumulators before the next MFMA
   }
 
-  if constexpr (QO) {
+  if constexpr (QO) {                                    // the workgroup's one tile
     static_assert(4 * 16 * (TN * 16 + 4) * 4 <= S * STAGE, "output staging fits in the operand ring");
     store_tile_q<TM, TN>(g, acc, m0 + wm * 128, n0 + wn * 128, r16, grp, smem);
-  } else {
-    store_tile<TM, TN>(g, acc, m0 + wm * 128, n0 + wn * 128, r16, grp);
   }
 }
 
@@ -959,16 +1124,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_q_kernel(GemmArgs g, int ns
 // K so that about 256 workgroups run.
 // NVFP4 256x256 tiles (gemm_nvfp4_w1_kernel, one per CU) run their K loop
 // about 10 % faster than the 256x128 tiles but pay more per tile at its
-// ends (pipeline fill and the store of a 256 KiB tile, with no second
-// workgroup on the CU to overlap them): measured on MI355X, faster by 3-9 %
-// for K >= 8192 (4096x8192x28672 1.486 -> 1.359 ms), mixed at K = 4096 and
-// slower below (4096x8192x1024 0.069 -> 0.087 ms), so planned only for
-// K >= 8192.
+// ends (pipeline fill and the store of a 256 KiB tile). Measured on MI355X
+// with one tile per workgroup: faster by 3-9 % for K >= 8192
+// (4096x8192x28672 1.486 -> 1.359 ms), mixed at K = 4096 and slower below
+// (4096x8192x1024 0.069 -> 0.087 ms). Persistent, with each tile's store
+// overlapping the next tile: also 1-3 % faster than 256x128 tiles at
+// K = 4096 (28672x8192x4096 1.546 -> 1.527 ms; the Llama-70B block step
+// 18.73 -> 18.51 ms), so planned for K >= 4096.
 static double big_tile_gain(int format, int64_t K) {
   switch (format) {
     case SNIP_FP8_E4M3: return 1.15;
     case SNIP_MXFP4: return 1.03;
-    case SNIP_NVFP4: return K >= 8192 ? 1.18 : 0.0;
+    case SNIP_NVFP4: return K >= 4096 ? 1.18 : 0.0;
     default: return 1.02;
   }
 }
@@ -1083,8 +1250,13 @@ static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
     }
   }
   if (p.bm == 256) {
-    if constexpr (FMT == SNIP_NVFP4) hipLaunchKernelGGL((gemm_nvfp4_w1_kernel<QO>), grid, dim3(NT), 0, s, g);
-    else if constexpr (FMT == SNIP_MXFP4 && !QO) hipLaunchKernelGGL(gemm_mxfp4_w1_kernel, grid, dim3(NT), 0, s, g);
+    if constexpr (FMT == SNIP_NVFP4) {
+      // one workgroup per CU, each running its tiles in turn; with QO one
+      // per tile (its epilogue uses the operand ring)
+      if (p.ksplit != 1 || g.nsec) return false;
+      const int64_t wgs = QO ? p.tiles : std::min<int64_t>(p.tiles, device_cus());
+      hipLaunchKernelGGL((gemm_nvfp4_w1_kernel<QO>), dim3((unsigned)(wgs + g.fin.n)), dim3(NT), 0, s, g);
+    } else if constexpr (FMT == SNIP_MXFP4 && !QO) hipLaunchKernelGGL(gemm_mxfp4_w1_kernel, grid, dim3(NT), 0, s, g);
     else hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1, QO>), grid, dim3(NT), 0, s, g);
   } else if (p.staged) {
     if constexpr (QO) return false;

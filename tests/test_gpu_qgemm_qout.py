@@ -46,7 +46,7 @@ def exact_operand(rows, k, fmt, seed):
 
 
 # (operand format, M, N, K, output format, rounding, amax factor): the shapes
-# select 256x128 (NVFP4, FP8), 256x256 (FP8, and NVFP4 for K >= 8192),
+# select 256x128 (NVFP4, FP8), 256x256 (FP8, and NVFP4 for K >= 4096),
 # 128x128, 64x64 unsplit and split-K plans, ragged in M.
 CASES = [
     (S.NVFP4, 4000, 4096, 256, S.NVFP4, S.RNE, 1.0),      # 256x128
