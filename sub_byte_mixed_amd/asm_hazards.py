@@ -19,6 +19,11 @@ every path:
   its A, B or C registers (or, for the scaled MFMAs, a scale register)
   within ``BEFORE_MFMA`` wait states.
 
+It also flags flat memory instructions in these kernels: a flat access
+counts in both vmcnt and lgkmcnt, and their barriers wait for lgkmcnt(0)
+(the LDS reads), so a flat store would be drained at the next barrier
+instead of overlapping the K loop.
+
 Wait states are counted as the hardware documentation counts them: one per
 instruction, N + 1 for ``s_nop N``. The bounds are above what gfx950 asks
 for a 16x16x32 MFMA (its result is read back after at most 19 wait states
@@ -155,7 +160,8 @@ def _cfg(insns: List[Insn]) -> Tuple[List[List[int]], List[List[int]]]:
 def check_kernel(insns: List[Insn]) -> List[str]:
     """Violations (empty when every path keeps the bounds)."""
     succ, pred = _cfg(insns)
-    bad: List[str] = []
+    bad: List[str] = [f"{x.text!r} is a flat memory access" for x in insns
+                      if x.op.startswith(("flat_load", "flat_store", "flat_atomic"))]
     for k, m in enumerate(insns):
         if not (m.is_mfma and m.asm):
             continue

@@ -455,21 +455,24 @@ template <int TM, int TN>
 __device__ __forceinline__ bool store_tile_rows(const GemmArgs& g, const floatx4_t (&acc)[TM][TN], int64_t r0,
                                                 int64_t c0, int r16, int grp, int e) {
   if (r0 + 16 * TM <= g.M && c0 + 16 * TN <= g.N && (g.ldc & 3) == 0 && ((uintptr_t)g.c & 15) == 0) {
-    // one lane address, stepped by 16 rows per row block (kept opaque, so
-    // that no per-block addresses are precomputed into registers: the
-    // caller's next-stage operands are live here)
-    float* rowp = g.c + (r0 + r16) * g.ldc + c0 + 4 * grp;
-    int64_t step = 16 * g.ldc;
+    // one lane offset, stepped by 16 rows per row block (kept opaque, so
+    // that no per-block addresses are precomputed into registers). The
+    // offset, not the pointer, goes through the asm: a pointer would lose
+    // its address space, and flat stores also count in lgkmcnt, which every
+    // barrier of the K loop waits to zero.
+    int64_t off = ((r0 + r16) * g.ldc + c0 + 4 * grp) * 4;
+    int64_t step = 16 * g.ldc * 4;
     asm volatile("" : "+s"(step));
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      float* const rowp = reinterpret_cast<float*>(reinterpret_cast<char*>(g.c) + off);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         *reinterpret_cast<floatx4_t*>(rowp + j * 16) =
             floatx4_t{ldexpf(acc[i][j][0], e), ldexpf(acc[i][j][1], e), ldexpf(acc[i][j][2], e),
                       ldexpf(acc[i][j][3], e)};
-      rowp += step;
-      asm volatile("" : "+v"(rowp));
+      off += step;
+      asm volatile("" : "+v"(off));
       __builtin_amdgcn_sched_barrier(0);
     }
     return true;

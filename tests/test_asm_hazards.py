@@ -75,6 +75,14 @@ def test_hazard_on_one_branch_path_is_flagged():
     assert _violations(body)[1]
 
 
+def test_flat_memory_access_is_flagged():
+    # a flat store also counts in lgkmcnt, which the K loop's barriers wait on
+    body = "\n".join([_mfma("a[0:3]"), "\tflat_store_dwordx4 v[34:35], v[0:3] offset:64"])
+    assert any("flat memory access" in b for b in _violations(body)[1])
+    body = "\n".join([_mfma("a[0:3]"), "\tglobal_store_dwordx4 v[34:35], v[0:3], off offset:64"])
+    assert _violations(body)[1] == []
+
+
 def test_compiler_selected_mfma_is_not_checked():
     # outside an asm region the compiler inserts the wait states itself
     body = "\tv_mfma_f32_16x16x32_f16 a[0:3], v[0:3], v[4:7], a[0:3]\n\tv_accvgpr_read_b32 v8, a0"
