@@ -98,9 +98,9 @@ PLAN_CASES = [
     (S.FP8, 4000, 5600, 1024),      # 128x128 (256x128 would leave a last round of 192 tiles)
     (S.NVFP4, 8000, 4000, 512),     # 256x128, 2-stage ring
     (S.NVFP4, 4000, 3900, 8320),    # 256x256, one wave per SIMD (K >= 4096; 65 stages)
-    (S.NVFP4, 3800, 17400, 4224),   # the same kernel persistent: 1020 tiles on 256 workgroups, ragged
-                                    # edges, loads running on into the next tile between interior tiles,
-                                    # first tiles split (33 stages, odd) with their rest added last
+    (S.NVFP4, 3800, 17400, 4224),   # the same kernel persistent: 1020 tiles on 256 workgroups (3-4 each),
+                                    # ragged edges, loads running on into the next tile between interior
+                                    # tiles, 33 stages (the ring's slots rotate from tile to tile)
     (S.NVFP4, 4000, 5600, 1024),    # 256x128, 2-stage ring
     (S.FP8, 8000, 4000, 512),       # 256x128
     (S.FP8, 1500, 35500, 512),      # 256x256 (834 tiles: 256x128 would leave a last round of 132)
