@@ -520,12 +520,22 @@ static int device_cus() {
 // LDS ring before its last slice: a barrier there (stage it+1 has landed,
 // every wave has read stage it) lets the wave refill stage it's slot with
 // stage it+4 and read stage it+1, whose first slice it decodes during the
-// last slice of stage it. The refill's 12 loads and the 32 reads go one
+// last slice of stage it. The refill's loads and the 32 reads go one
 // after each MFMA (rows 6-7 of slice 2, rows 0-1 of slice 3): issued in a
 // burst they left the lone wave's MFMA pipe idle (measured on MI355X:
 // without the refill loads a timing copy ran 20 % faster; spread, the
 // Llama-70B block step went from 17.99 to 17.69 ms). Ring: 4 stages of
-// K = 128 (36 KiB each).
+// K = 128 codes (32 KiB each).
+//
+// Scales. A row holds 8 E4M3 bytes per stage, rows K/16 bytes apart. Each
+// load instruction costs the MFMA stream about the same whatever it moves
+// (measured on MI355X: a timing copy without the scale refills, a third of
+// the loads and 1/9 of the bytes, ran 4-5 % faster), so a row's scales of
+// two stages (16 contiguous bytes) come in one 16-byte load per lane: a
+// group of 256 A and 256 B rows is 8 KiB, two loads per wave, issued with
+// the even stage's refill into a 3-slot ring of groups (the slot's previous
+// group was last read before the stage before). K % 256 == 0, so the
+// stages of a workgroup's stream alternate even and odd from tile to tile.
 //
 // Persistent (without QO): the launch has one workgroup per CU, P in all,
 // and workgroup b runs tiles b, b + P, b + 2P, ... Every tile takes the same
@@ -546,16 +556,17 @@ template <bool QO>
 __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
   constexpr int S = 4, NU = 16;                            // stages; 16-row units per operand
   constexpr int LA = NU * 1024, LB = NU * 1024;            // code bytes per stage
-  constexpr int LSA = NU * 16 * 8, LSB = NU * 16 * 8;      // scale bytes per stage
-  constexpr int STAGE = LA + LB + LSA + LSB;
-  constexpr int NSA = LSA / 256, NSB = LSB / 256;          // scale DMA instructions
-  constexpr int IA = NU / 4, IB = NU / 4, IS = (NSA + NSB) / 4;
-  constexpr int NIW = IA + IB + IS;                        // DMA instructions per wave and stage
+  constexpr int STAGE = LA + LB;
+  constexpr int SG = 2 * NU * 16 * 16, NG = 3;             // scale group (two stages of A and B rows); ring slots
+  constexpr int IA = NU / 4, IB = NU / 4, IS = 2;          // per wave: code loads of a stage, scale loads of a group
+  constexpr int NE = IA + IB + IS, NO = IA + IB;           // loads per wave of an even and of an odd stage
   constexpr int TM = 8, TN = 8;                            // 16x16 MFMA tiles per wave
-  static_assert((S - 1) * NIW <= 63, "vmcnt range");
+  static_assert(NE + NO + NE <= 63, "vmcnt range");
   static_assert(TM * TN >= 63, "a tile's 16-byte writes alone fill the vmcnt window");
-  static_assert(NIW <= 2 * TN, "a stage's loads go out in two rows of MFMAs");
-  __shared__ __align__(1024) uint8_t smem[S * STAGE];
+  static_assert(NE <= 2 * TN, "a stage's loads go out in two rows of MFMAs");
+  static_assert(SG == 4 * IS * 1024, "a group is the waves' 16-byte loads of 64 rows each");
+  static_assert(S * STAGE + NG * SG <= 160 * 1024, "LDS");
+  __shared__ __align__(1024) uint8_t smem[S * STAGE + NG * SG];
 
   const int P = (int)gridDim.x - g.fin.n;                  // tile workgroups
   if ((int)blockIdx.x >= P) {
@@ -572,11 +583,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
   const int64_t rowbytes = g.K / 128 * 64, srow = g.K / 16;
 
   // DMA sources of the tile at (m0, n0), as in gemm_kernel with one unit per
-  // stage: wave w loads code units w, w+4, ... of A and of B and scale
-  // instructions w, w+4, ... (the first two A's, the last two B's); rows
-  // past M or N read the last row. Per lane a 32-bit offset from the
+  // stage: wave w loads code units w, w+4, ... of A and of B, and of a scale
+  // group A rows 64 w .. 64 w + 63 and B rows the same, lane l row 64 w + l;
+  // rows past M or N read the last row. Per lane a 32-bit offset from the
   // operand's start.
-  static_assert(NSA == 8 && NSB == 8 && IS == 4, "scale instructions 0-1 of a wave load A, 2-3 load B");
   uint32_t offa[IA], offb[IB], offs[IS];
   auto sources = [&](int64_t m0, int64_t n0) {
 #pragma unroll
@@ -585,47 +595,43 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
 #pragma unroll
     for (int t = 0; t < IB; ++t)
       offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
-#pragma unroll
-    for (int t = 0; t < IS; ++t) {
-      const int pp = wave + 4 * t;
-      const bool isa = pp < NSA;
-      const int p = isa ? pp : pp - NSA;
-      const int blk = 2 * p + (lane >> 5), r = (lane & 31) >> 1, part = (lane & 1) * 4;
-      const int64_t row = isa ? min(m0 + blk * 16 + r, g.M - 1) : min(n0 + blk * 16 + r, g.N - 1);
-      offs[t] = (uint32_t)(row * srow) + part;
-    }
+    offs[0] = (uint32_t)(min(m0 + wave * 64 + lane, g.M - 1) * srow);
+    offs[1] = (uint32_t)(min(n0 + wave * 64 + lane, g.N - 1) * srow);
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const uint32_t sg0 = S * STAGE;                          // scale ring, bytes into smem
   // stage kt of the tile whose rows lie dm (A) and dn (B) rows past the
-  // tile the offsets were worked out for; the bases are scalar, and the
-  // wave's LDS base is made opaque per call so that the compiler does not
-  // keep each instruction's LDS address in a register of its own
-  auto issue = [&](int kt, int slot, int dm, int dn) {
-    uint32_t lw = lds0 + slot * STAGE + wave * 1024, ls = lds0 + slot * STAGE + LA + LB + wave * 256;
+  // tile the offsets were worked out for, and with an even kt the scale
+  // group of stages kt and kt+1 into group slot gsl; the bases are scalar,
+  // and the wave's LDS base is made opaque per call so that the compiler
+  // does not keep each instruction's LDS address in a register of its own
+  auto issue = [&](int kt, int slot, int dm, int dn, int gsl) {
+    uint32_t lw = lds0 + slot * STAGE + wave * 1024, ls = lds0 + sg0 + gsl * SG + wave * 1024;
     asm volatile("" : "+s"(lw), "+s"(ls));
     const uint8_t* pa = g.a + (int64_t)dm * rowbytes + (int64_t)kt * 64;
     const uint8_t* pb = g.b + (int64_t)dn * rowbytes + (int64_t)kt * 64;
-    const uint8_t* psa = g.as + (int64_t)dm * srow + (int64_t)kt * 8;
-    const uint8_t* psb = g.bs + (int64_t)dn * srow + (int64_t)kt * 8;
 #pragma unroll
     for (int t = 0; t < IA; ++t) dma16s(pa, offa[t], lw + t * 4096);
 #pragma unroll
     for (int t = 0; t < IB; ++t) dma16s(pb, offb[t], lw + LA + t * 4096);
-#pragma unroll
-    for (int t = 0; t < IS; ++t) dma4s(t < 2 ? psa : psb, offs[t], ls + t * 1024);   // B scales follow the A scales
+    if ((kt & 1) == 0) {
+      dma16s(g.as + (int64_t)dm * srow + (int64_t)kt * 8, offs[0], ls);
+      dma16s(g.bs + (int64_t)dn * srow + (int64_t)kt * 8, offs[1], ls + SG / 2);
+    }
   };
-  // load d of the NIW of issue(kt, slot, dm, dn): A codes, B codes, scales
-  auto issue1 = [&](int kt, int slot, int dm, int dn, int d) {
-    uint32_t lw = lds0 + slot * STAGE + wave * 1024, ls = lds0 + slot * STAGE + LA + LB + wave * 256;
+  // load d of issue(kt, slot, dm, dn, gsl): A codes, B codes, A scales, B
+  // scales (the last two with an even kt only)
+  auto issue1 = [&](int kt, int slot, int dm, int dn, int gsl, int d) {
+    uint32_t lw = lds0 + slot * STAGE + wave * 1024, ls = lds0 + sg0 + gsl * SG + wave * 1024;
     asm volatile("" : "+s"(lw), "+s"(ls));
     if (d < IA) {
       dma16s(g.a + (int64_t)dm * rowbytes + (int64_t)kt * 64, offa[d], lw + d * 4096);
     } else if (d < IA + IB) {
       dma16s(g.b + (int64_t)dn * rowbytes + (int64_t)kt * 64, offb[d - IA], lw + LA + (d - IA) * 4096);
+    } else if (d == IA + IB) {
+      dma16s(g.as + (int64_t)dm * srow + (int64_t)kt * 8, offs[0], ls);
     } else {
-      const int t = d - IA - IB;
-      dma4s(t < 2 ? g.as + (int64_t)dm * srow + (int64_t)kt * 8 : g.bs + (int64_t)dn * srow + (int64_t)kt * 8,
-            offs[t], ls + t * 1024);
+      dma16s(g.bs + (int64_t)dn * srow + (int64_t)kt * 8, offs[1], ls + SG / 2);
     }
   };
 
@@ -641,34 +647,37 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
     uint4 b[TN];
     uint32_t s[TN];
   };
-  auto read_a = [&](RawA& r, int slot) {
-    const uint8_t* base = smem + slot * STAGE;
-    const uint8_t* la = base + (wm * TM) * 1024 + r16 * 64 + grp * 16;
-    const uint8_t* sa = base + LA + LB + ((wm * TM) * 16 + r16) * 8 + grp * 2;
+  // A stage's codes are in ring slot `slot`, its scales at byte sg of smem
+  // (its group's slot, plus 8 for an odd stage): A row r's at sg + 16 r, B
+  // row r's SG / 2 further
+  auto read_a = [&](RawA& r, int slot, int sg) {
+    const uint8_t* la = smem + slot * STAGE + (wm * TM) * 1024 + r16 * 64 + grp * 16;
+    const uint8_t* sa = smem + sg + ((wm * TM) * 16 + r16) * 16 + grp * 2;
 #pragma unroll
     for (int i = 0; i < TM; ++i) r.a[i] = *reinterpret_cast<const uint4*>(la + i * 1024);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) r.s[i] = *reinterpret_cast<const uint16_t*>(sa + i * 128);
+    for (int i = 0; i < TM; ++i) r.s[i] = *reinterpret_cast<const uint16_t*>(sa + i * 256);
   };
   // read k of 16 of a stage's A (or B) operands: codes 0-7, scales 8-15
-  auto read_a1 = [&](RawA& r, int slot, int k) {
-    const uint8_t* base = smem + slot * STAGE;
-    if (k < TM) r.a[k] = *reinterpret_cast<const uint4*>(base + (wm * TM + k) * 1024 + r16 * 64 + grp * 16);
-    else r.s[k - TM] = *reinterpret_cast<const uint16_t*>(base + LA + LB + ((wm * TM + k - TM) * 16 + r16) * 8 + grp * 2);
+  auto read_a1 = [&](RawA& r, int slot, int sg, int k) {
+    if (k < TM)
+      r.a[k] = *reinterpret_cast<const uint4*>(smem + slot * STAGE + (wm * TM + k) * 1024 + r16 * 64 + grp * 16);
+    else r.s[k - TM] = *reinterpret_cast<const uint16_t*>(smem + sg + ((wm * TM + k - TM) * 16 + r16) * 16 + grp * 2);
   };
-  auto read_b1 = [&](RawB& r, int slot, int k) {
-    const uint8_t* base = smem + slot * STAGE;
-    if (k < TN) r.b[k] = *reinterpret_cast<const uint4*>(base + LA + (wn * TN + k) * 1024 + r16 * 64 + grp * 16);
-    else r.s[k - TN] = *reinterpret_cast<const uint16_t*>(base + LA + LB + LSA + ((wn * TN + k - TN) * 16 + r16) * 8 + grp * 2);
+  auto read_b1 = [&](RawB& r, int slot, int sg, int k) {
+    if (k < TN)
+      r.b[k] = *reinterpret_cast<const uint4*>(smem + slot * STAGE + LA + (wn * TN + k) * 1024 + r16 * 64 + grp * 16);
+    else
+      r.s[k - TN] =
+          *reinterpret_cast<const uint16_t*>(smem + sg + SG / 2 + ((wn * TN + k - TN) * 16 + r16) * 16 + grp * 2);
   };
-  auto read_b = [&](RawB& r, int slot) {
-    const uint8_t* base = smem + slot * STAGE;
-    const uint8_t* lb = base + LA + (wn * TN) * 1024 + r16 * 64 + grp * 16;
-    const uint8_t* sb = base + LA + LB + LSA + ((wn * TN) * 16 + r16) * 8 + grp * 2;
+  auto read_b = [&](RawB& r, int slot, int sg) {
+    const uint8_t* lb = smem + slot * STAGE + LA + (wn * TN) * 1024 + r16 * 64 + grp * 16;
+    const uint8_t* sb = smem + sg + SG / 2 + ((wn * TN) * 16 + r16) * 16 + grp * 2;
 #pragma unroll
     for (int j = 0; j < TN; ++j) r.b[j] = *reinterpret_cast<const uint4*>(lb + j * 1024);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) r.s[j] = *reinterpret_cast<const uint16_t*>(sb + j * 128);
+    for (int j = 0; j < TN; ++j) r.s[j] = *reinterpret_cast<const uint16_t*>(sb + j * 256);
   };
   auto scale2 = [](uint32_t raw) -> half2_t { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false); };
   // Pair p (of 4) of a fragment's decode for K slice q (elements 2p, 2p+1):
@@ -722,21 +731,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
   int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
   sources(m0, n0);
   int slot = 0;                                          // slot of the stage to multiply next
+  int gq = 0;                                            // its scale group's slot
 #pragma unroll
   for (int s = 0; s < S; ++s)
-    if (s < nk) issue(s, s, 0, 0);
+    if (s < nk) issue(s, s, 0, 0, s >> 1);
   if constexpr (!QO) plan_ahead(tile, m0, n0);
   bool stored = false;                                   // a store was issued after this tile's first loads
   for (;;) {
+    // stage 0's loads are followed by those of stages 1-3 (odd, even, odd)
     if (stored) wait_vm_barrier<63>();                   // the store's 64 writes follow the loads
-    else if (nk >= 4) wait_vm_barrier<3 * NIW>();
-    else if (nk == 3) wait_vm_barrier<2 * NIW>();
-    else if (nk == 2) wait_vm_barrier<NIW>();
-    else wait_vm_barrier<0>();
+    else if (nk >= 4) wait_vm_barrier<NO + NE + NO>();
+    else wait_vm_barrier<NO>();
     RawA RA;
     RawB RB;
-    read_a(RA, slot);
-    read_b(RB, slot);
+    read_a(RA, slot, sg0 + gq * SG);
+    read_b(RB, slot, sg0 + gq * SG);
     half2_t sa[TM], sb[TN];                              // scales of the stage's fragments
 #pragma unroll
     for (int i = 0; i < TM; ++i) sa[i] = scale2(RA.s[i]);
@@ -767,6 +776,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
     for (int it = 0; it < nk; ++it) {                    // stage it, in slot `slot`
       const bool more = it + 1 < nk;
       const int next = slot == S - 1 ? 0 : slot + 1;
+      const bool odd = it & 1;
+      const int gn = odd ? (gq == NG - 1 ? 0 : gq + 1) : gq;   // group slot of stage it+1,
+      const int nsg = sg0 + gn * SG + (odd ? 0 : 8);           // its scales
+      const int rgs = gq == 0 ? NG - 1 : gq - 1;               // of stage it+4 (even it)
       RawA NA;
       RawB NB;
       half2_t nsb[TN], nsa0;
@@ -784,10 +797,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
             // the stream's stage it+1 has landed (and, as below, every wave
             // has read stage it). With `ahead` the stream runs on into the
             // next tile, two stages always following
+            // (the loads of stages it+2 and it+3 follow stage it+1's, the
+            // scales of an odd stage it+1 came with stage it's; near the
+            // end only stage it+2, odd as nk is even, follows)
             if (more || ahead) {
               if (stored && it < S - 1) wait_vm_barrier<63>();
-              else if (ahead || it + 3 < nk) wait_vm_barrier<2 * NIW>();
-              else if (it + 2 < nk) wait_vm_barrier<NIW>();
+              else if (ahead || it + 3 < nk) wait_vm_barrier<NE + NO>();
+              else if (it + 2 < nk) wait_vm_barrier<NO>();
               else wait_vm_barrier<0>();
             }
             // every wave has read stage it: its slot takes stage it+4, or
@@ -824,15 +840,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
             if constexpr (QO) mfma_acc_agpr(acc[i][j], ad, bd[j]);
             else mfma_acc_agpr(acc[i][j], bd[j], ad);  // C transposed: a lane's results lie in one row
             if constexpr (q == 2 && i == 6) {
-              if (rf) issue1(rkt, slot, rdm, rdn, j);
-              read_b1(NB, next, j);
+              if (rf) issue1(rkt, slot, rdm, rdn, rgs, j);
+              read_b1(NB, next, nsg, j);
             }
             if constexpr (q == 2 && i == 7) {
-              if (j < NIW - TN && rf) issue1(rkt, slot, rdm, rdn, TN + j);
-              read_b1(NB, next, TN + j);
+              if (j < IS && rf && !odd) issue1(rkt, slot, rdm, rdn, rgs, TN + j);
+              read_b1(NB, next, nsg, TN + j);
             }
-            if constexpr (q == 3 && i == 0) read_a1(NA, next, j);
-            if constexpr (q == 3 && i == 1) read_a1(NA, next, TM + j);
+            if constexpr (q == 3 && i == 0) read_a1(NA, next, nsg, j);
+            if constexpr (q == 3 && i == 1) read_a1(NA, next, nsg, TM + j);
             t[j] = cvt_j(j);
             asm volatile("" : "+v"(t[j]));             // computed here, not sunk to its use
             if (j > 0) {
@@ -857,6 +873,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) sb[j] = nsb[j];
       slot = next;
+      gq = gn;
       // before any accumulator read: at the end of every stage (under 1 %
       // of its time) rather than after the loop, so that what the compiler
       // places on the loop's exit edge comes after it
@@ -878,7 +895,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
         wait_vm_barrier<63>();
 #pragma unroll
         for (int s = 0; s < S; ++s)
-          if (s < nk) issue(s, (slot + s) & (S - 1), 0, 0);
+          if (s < nk) issue(s, (slot + s) & (S - 1), 0, 0, s < 2 ? gq : gq == NG - 1 ? 0 : gq + 1);
       }
       plan_ahead(tile, m0, n0);
     }
@@ -1179,12 +1196,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_q_kernel(GemmArgs g, int ns
 // (4096x8192x1024 0.069 -> 0.087 ms). Persistent, with each tile's store
 // overlapping the next tile: also 1-3 % faster than 256x128 tiles at
 // K = 4096 (28672x8192x4096 1.546 -> 1.527 ms; the Llama-70B block step
-// 18.73 -> 18.51 ms), so planned for K >= 4096.
+// 18.73 -> 18.51 ms), so planned for K >= 4096 (in pairs of 128-element
+// stages: the kernel loads each row's scales of two stages at once).
 static double big_tile_gain(int format, int64_t K) {
   switch (format) {
     case SNIP_FP8_E4M3: return 1.15;
     case SNIP_MXFP4: return 1.03;
-    case SNIP_NVFP4: return K >= 4096 ? 1.18 : 0.0;
+    case SNIP_NVFP4: return K >= 4096 && K % 256 == 0 ? 1.18 : 0.0;
     default: return 1.02;
   }
 }
@@ -1302,7 +1320,7 @@ static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
     if constexpr (FMT == SNIP_NVFP4) {
       // one workgroup per CU, each running its tiles in turn; with QO one
       // per tile (its epilogue uses the operand ring)
-      if (p.ksplit != 1 || g.nsec) return false;
+      if (p.ksplit != 1 || g.nsec || g.K % 256) return false;
       const int64_t wgs = QO ? p.tiles : std::min<int64_t>(p.tiles, device_cus());
       hipLaunchKernelGGL((gemm_nvfp4_w1_kernel<QO>), dim3((unsigned)(wgs + g.fin.n)), dim3(NT), 0, s, g);
     } else if constexpr (FMT == SNIP_MXFP4 && !QO) hipLaunchKernelGGL(gemm_mxfp4_w1_kernel, grid, dim3(NT), 0, s, g);
