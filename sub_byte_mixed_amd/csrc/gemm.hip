@@ -945,23 +945,33 @@ __device__ __forceinline__ void mfma_mx_acc_agpr(floatx4_t& acc, const uint4& a,
 // many requests as the stage's 64-byte code segments (measured: without the
 // scale loads the kernel ran 26-34 % faster). They are loaded 4 stages at a
 // time instead, the 16 contiguous bytes of a row by a quad of lanes (one
-// request), into a 3-slot ring of 8 KiB groups (512 rows x 16 bytes). A
-// group's 32 instructions (16 rows each) are spread over the 4 stages that
-// run 8 to 5 stages before its first stage, 2 per wave and stage, so every
-// stage still issues 10 loads and group g is in LDS by the barrier that
-// precedes its first read (which waits for everything issued 3 or more
-// stages earlier).
+// request), into a 3-slot ring of 8 KiB groups (512 rows x 16 bytes),
+// group g issued during the 4 stages that run 8 to 5 stages before its
+// first one, so that it is in LDS by the barrier that precedes its first
+// read (which waits for everything issued 3 or more stages earlier). With
+// whole groups (WG: the K range a 4-stage multiple, so a row's 16 bytes lie
+// in it) a lane loads a row's 16 bytes: 8 instructions of 64 rows per
+// group, A rows by each wave in the group's first stage and B rows in its
+// third (each load instruction costs the MFMA stream about the same
+// whatever it moves). Otherwise a quad of lanes loads them, 32 instructions
+// of 16 rows, 2 per wave and stage, words past the last stage repeating
+// it. Either way the refills of two successive stages are the same count
+// of loads, which the waits rely on.
+template <bool WG>
 __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
   constexpr int S = 4, NU = 16;                            // code stages; 16-row units per operand
   constexpr int LA = NU * 1024, LB = NU * 1024;            // code bytes per stage
   constexpr int STAGE = LA + LB;
   constexpr int SG = 512 * 16, NG = 3;                     // scale group bytes (4 stages), ring slots
-  constexpr int IA = NU / 4, IB = NU / 4, IS = 2;          // per wave and stage: 32 instructions per group
-  constexpr int NIW = IA + IB + IS;                        // DMA instructions per wave and stage
+  constexpr int IA = NU / 4, IB = NU / 4;                  // code loads per wave and stage
+  constexpr int IS = WG ? 1 : 2;                           // scale loads per wave of an even stage
+  constexpr int ISO = WG ? 0 : 2;                          // and of an odd one
+  constexpr int NIW = IA + IB + IS;                        // DMA instructions of an even stage
+  constexpr int NIW2 = 2 * (IA + IB) + IS + ISO;           // of two successive stages
   constexpr int TM = 8, TN = 8;
-  static_assert((S - 1) * NIW <= 63, "vmcnt range");
+  static_assert(NIW + NIW2 <= 63, "vmcnt range");
   static_assert(NIW <= 4 * TN, "the refill fits in rows 4-7");
-  static_assert(4 * 4 * IS == 32, "a group is 32 instructions over 4 stages and 4 waves");
+  static_assert(WG ? 2 * 4 * 64 == 512 : 4 * 4 * IS == 32, "a group's rows: 8 loads of 64 or 32 of 16");
   static_assert(S * STAGE + NG * SG <= 160 * 1024, "LDS");
   __shared__ __align__(1024) uint8_t smem[S * STAGE + NG * SG];
   if (finalize_workgroup(g_in)) return;
@@ -994,20 +1004,31 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
     if (d < IA) dma16(g.a + (int64_t)kt * 64 + offa[d], base + (wave + 4 * d) * 1024);
     else dma16(g.b + (int64_t)kt * 64 + offb[d - IA], base + LA + (wave + 4 * (d - IA)) * 1024);
   };
-  // scale instruction k (of 32) of group gi: 16 rows (A rows for k < 16,
-  // then B rows), lane l the word l % 4 (stage 4 gi + l % 4) of row l / 4;
-  // words past the last stage repeat the last stage's (kept in the row)
+  // Scale instruction k of group gi. WG (k < 8): 64 rows (A rows for k < 4,
+  // then B rows), lane l row 64 (k % 4) + l, groups past the last reloading
+  // it (never read). Otherwise (k < 32): 16 rows (A rows for k < 16, then
+  // B rows), lane l the word l % 4 (stage 4 gi + l % 4) of row l / 4; words
+  // past the last stage repeat the last stage's (kept in the row).
   auto scale1 = [&](int gi, int k) {
-    const bool isa = k < 16;
-    const int64_t row = isa ? min(m0 + (k & 15) * 16 + (lane >> 2), g.M - 1)
-                            : min(n0 + (k & 15) * 16 + (lane >> 2), g.N - 1);
-    const int word = min(kt0 + 4 * gi + (lane & 3), kt1 - 1);
-    dma4((isa ? g.as : g.bs) + row * srow + word * 4, sl0 + (gi % NG) * SG + k * 256);
+    if constexpr (WG) {
+      const bool isa = k < 4;
+      const int64_t row = isa ? min(m0 + (k & 3) * 64 + lane, g.M - 1) : min(n0 + (k & 3) * 64 + lane, g.N - 1);
+      const int word = kt0 + 4 * min(gi, nk / 4 - 1);
+      dma16((isa ? g.as : g.bs) + row * srow + word * 4, sl0 + (gi % NG) * SG + k * 1024);
+    } else {
+      const bool isa = k < 16;
+      const int64_t row = isa ? min(m0 + (k & 15) * 16 + (lane >> 2), g.M - 1)
+                              : min(n0 + (k & 15) * 16 + (lane >> 2), g.N - 1);
+      const int word = min(kt0 + 4 * gi + (lane & 3), kt1 - 1);
+      dma4((isa ? g.as : g.bs) + row * srow + word * 4, sl0 + (gi % NG) * SG + k * 256);
+    }
   };
-  // the loads stage it issues (d of NIW): codes of stage it+4, then phase
-  // it % 4 of scale group it/4 + 2
+  // the loads stage it issues (d of NIW): codes of stage it+4, then its
+  // part of scale group it/4 + 2 (WG: A rows in phase 0, B rows in phase 2
+  // of the group's 4 stages; else phase it % 4 of the 32 instructions)
   auto issue1 = [&](int it, int slot, int d) {
     if (d < IA + IB) code1(min(kt0 + it + S, kt1 - 1), slot, d);
+    else if constexpr (WG) scale1(it / 4 + 2, (it & 2) * 2 + wave);
     else scale1(it / 4 + 2, (it & 3) * 8 + wave * 2 + (d - IA - IB));
   };
 
@@ -1036,20 +1057,29 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: scale group 0, then code stages 0-3 each with a quarter of
-  // scale group 1, so that every stage's loads number NIW
+  // prologue: scale group 0, then code stages 0-3 each with its part of
+  // scale group 1, as the stages 4 later issue theirs
+  if constexpr (WG) {
+    scale1(0, wave);
+    scale1(0, 4 + wave);
+  } else {
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
+    for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int t = 0; t < IS; ++t) scale1(0, p * 8 + wave * 2 + t);
+      for (int t = 0; t < IS; ++t) scale1(0, p * 8 + wave * 2 + t);
+  }
 #pragma unroll
   for (int s = 0; s < S; ++s) {
 #pragma unroll
     for (int d = 0; d < IA + IB; ++d) code1(min(kt0 + s, kt1 - 1), s, d);
+    if constexpr (WG) {
+      if ((s & 1) == 0) scale1(1, (s & 2) * 2 + wave);
+    } else {
 #pragma unroll
-    for (int t = 0; t < IS; ++t) scale1(1, s * 8 + wave * 2 + t);
+      for (int t = 0; t < IS; ++t) scale1(1, s * 8 + wave * 2 + t);
+    }
   }
-  wait_vm_barrier<(S - 1) * NIW>();                      // scale group 0 and code stage 0 have landed
+  wait_vm_barrier<NIW2 + IA + IB + ISO>();               // scale group 0 and code stage 0 have landed
   Frags F;
 #pragma unroll
   for (int k = 0; k < 32; ++k) read1(F, 0, 0, k);
@@ -1071,12 +1101,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
     for (int i = 0; i < TM; ++i) {
       // stage it+1 has landed (stages it+2, it+3 may still be in flight),
       // every wave has read stage it
-      if (i == 4) wait_vm_barrier<(S - 2) * NIW>();
+      if (i == 4) wait_vm_barrier<NIW2>();
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         mfma_mx_acc_agpr(acc[i][j], cur.a[i], cur.b[j], cur.sa[i], cur.sb[j]);
-        // the refill: NIW loads, one per MFMA from row 4 on
-        if (i >= 4 && (i - 4) * TN + j < NIW) issue1(it, slot, (i - 4) * TN + j);
+        // the refill, one load per MFMA from row 4 on (WG: the scale load in
+        // even stages only)
+        if (i >= 4 && (i - 4) * TN + j < NIW && (!WG || (i - 4) * TN + j < IA + IB || (it & 1) == 0))
+          issue1(it, slot, (i - 4) * TN + j);
         // next stage's reads, the earliest needed first: B codes and scales
         // (row 0), A scales, A codes (A block i is first used in row i)
         if (i >= 4) read1(nxt, it + 1, next, i == 4 ? 8 + j : i == 5 ? 24 + j : i == 6 ? 16 + j : j);
@@ -1323,7 +1355,12 @@ static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
       if (p.ksplit != 1 || g.nsec || g.K % 256) return false;
       const int64_t wgs = QO ? p.tiles : std::min<int64_t>(p.tiles, device_cus());
       hipLaunchKernelGGL((gemm_nvfp4_w1_kernel<QO>), dim3((unsigned)(wgs + g.fin.n)), dim3(NT), 0, s, g);
-    } else if constexpr (FMT == SNIP_MXFP4 && !QO) hipLaunchKernelGGL(gemm_mxfp4_w1_kernel, grid, dim3(NT), 0, s, g);
+    } else if constexpr (FMT == SNIP_MXFP4 && !QO) {
+      if (g.K % 512 == 0 && g.kchunk % 512 == 0)
+        hipLaunchKernelGGL(gemm_mxfp4_w1_kernel<true>, grid, dim3(NT), 0, s, g);
+      else
+        hipLaunchKernelGGL(gemm_mxfp4_w1_kernel<false>, grid, dim3(NT), 0, s, g);
+    }
     else hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1, QO>), grid, dim3(NT), 0, s, g);
   } else if (p.staged) {
     if constexpr (QO) return false;
