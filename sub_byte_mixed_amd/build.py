@@ -119,7 +119,7 @@ def _compile(src: str, verbose: bool) -> str:
 # Kernels that issue MFMAs as inline asm, per source: their device assembly
 # is checked for the wait states the compiler does not insert for them
 # (asm_hazards.py); a violation fails the build.
-ASM_MFMA_KERNELS = {"gemm.hip": ["gemm_nvfp4_w1_kernel", "gemm_mxfp4_w1_kernel"]}
+ASM_MFMA_KERNELS = {"gemm.hip": ["gemm_nvfp4_w1_kernel", "gemm_mxfp4_w1_kernel", "gemm_mxfp4_w1p_kernel"]}
 
 
 def _device_asm(src: str, verbose: bool) -> str:

@@ -928,8 +928,9 @@ __device__ __forceinline__ void mfma_mx_acc_agpr(floatx4_t& acc, const uint4& a,
                : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)), "v"(sa), "v"(sb));
 }
 
-// MX-FP4 on 256x256 tiles, one wave per SIMD, each wave a 128x128 sub-tile:
-// the structure of gemm_nvfp4_w1_kernel without a decode (the MFMA takes
+// MX-FP4 on 256x256 tiles, one wave per SIMD, each wave a 128x128 sub-tile,
+// one tile per workgroup (K % 512 != 0; gemm_mxfp4_w1p_kernel below takes
+// the rest): the structure of gemm_nvfp4_w1_kernel without a decode (the MFMA takes
 // the codes and block scales as they are). A stage (K = 128) is 64 MFMAs
 // per wave, 16 cycles each at the FP4 rate, against 16 LDS reads of codes,
 // 16 of scale words and 10 DMA instructions, so the code ring runs 4
@@ -945,33 +946,23 @@ __device__ __forceinline__ void mfma_mx_acc_agpr(floatx4_t& acc, const uint4& a,
 // many requests as the stage's 64-byte code segments (measured: without the
 // scale loads the kernel ran 26-34 % faster). They are loaded 4 stages at a
 // time instead, the 16 contiguous bytes of a row by a quad of lanes (one
-// request), into a 3-slot ring of 8 KiB groups (512 rows x 16 bytes),
-// group g issued during the 4 stages that run 8 to 5 stages before its
-// first one, so that it is in LDS by the barrier that precedes its first
-// read (which waits for everything issued 3 or more stages earlier). With
-// whole groups (WG: the K range a 4-stage multiple, so a row's 16 bytes lie
-// in it) a lane loads a row's 16 bytes: 8 instructions of 64 rows per
-// group, A rows by each wave in the group's first stage and B rows in its
-// third (each load instruction costs the MFMA stream about the same
-// whatever it moves). Otherwise a quad of lanes loads them, 32 instructions
-// of 16 rows, 2 per wave and stage, words past the last stage repeating
-// it. Either way the refills of two successive stages are the same count
-// of loads, which the waits rely on.
-template <bool WG>
+// request), into a 3-slot ring of 8 KiB groups (512 rows x 16 bytes). A
+// group's 32 instructions (16 rows each) are spread over the 4 stages that
+// run 8 to 5 stages before its first stage, 2 per wave and stage, so every
+// stage still issues 10 loads and group g is in LDS by the barrier that
+// precedes its first read (which waits for everything issued 3 or more
+// stages earlier).
 __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
   constexpr int S = 4, NU = 16;                            // code stages; 16-row units per operand
   constexpr int LA = NU * 1024, LB = NU * 1024;            // code bytes per stage
   constexpr int STAGE = LA + LB;
   constexpr int SG = 512 * 16, NG = 3;                     // scale group bytes (4 stages), ring slots
-  constexpr int IA = NU / 4, IB = NU / 4;                  // code loads per wave and stage
-  constexpr int IS = WG ? 1 : 2;                           // scale loads per wave of an even stage
-  constexpr int ISO = WG ? 0 : 2;                          // and of an odd one
-  constexpr int NIW = IA + IB + IS;                        // DMA instructions of an even stage
-  constexpr int NIW2 = 2 * (IA + IB) + IS + ISO;           // of two successive stages
+  constexpr int IA = NU / 4, IB = NU / 4, IS = 2;          // per wave and stage: 32 instructions per group
+  constexpr int NIW = IA + IB + IS;                        // DMA instructions per wave and stage
   constexpr int TM = 8, TN = 8;
-  static_assert(NIW + NIW2 <= 63, "vmcnt range");
+  static_assert((S - 1) * NIW <= 63, "vmcnt range");
   static_assert(NIW <= 4 * TN, "the refill fits in rows 4-7");
-  static_assert(WG ? 2 * 4 * 64 == 512 : 4 * 4 * IS == 32, "a group's rows: 8 loads of 64 or 32 of 16");
+  static_assert(4 * 4 * IS == 32, "a group is 32 instructions over 4 stages and 4 waves");
   static_assert(S * STAGE + NG * SG <= 160 * 1024, "LDS");
   __shared__ __align__(1024) uint8_t smem[S * STAGE + NG * SG];
   if (finalize_workgroup(g_in)) return;
@@ -1004,31 +995,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
     if (d < IA) dma16(g.a + (int64_t)kt * 64 + offa[d], base + (wave + 4 * d) * 1024);
     else dma16(g.b + (int64_t)kt * 64 + offb[d - IA], base + LA + (wave + 4 * (d - IA)) * 1024);
   };
-  // Scale instruction k of group gi. WG (k < 8): 64 rows (A rows for k < 4,
-  // then B rows), lane l row 64 (k % 4) + l, groups past the last reloading
-  // it (never read). Otherwise (k < 32): 16 rows (A rows for k < 16, then
-  // B rows), lane l the word l % 4 (stage 4 gi + l % 4) of row l / 4; words
-  // past the last stage repeat the last stage's (kept in the row).
+  // scale instruction k (of 32) of group gi: 16 rows (A rows for k < 16,
+  // then B rows), lane l the word l % 4 (stage 4 gi + l % 4) of row l / 4;
+  // words past the last stage repeat the last stage's (kept in the row)
   auto scale1 = [&](int gi, int k) {
-    if constexpr (WG) {
-      const bool isa = k < 4;
-      const int64_t row = isa ? min(m0 + (k & 3) * 64 + lane, g.M - 1) : min(n0 + (k & 3) * 64 + lane, g.N - 1);
-      const int word = kt0 + 4 * min(gi, nk / 4 - 1);
-      dma16((isa ? g.as : g.bs) + row * srow + word * 4, sl0 + (gi % NG) * SG + k * 1024);
-    } else {
-      const bool isa = k < 16;
-      const int64_t row = isa ? min(m0 + (k & 15) * 16 + (lane >> 2), g.M - 1)
-                              : min(n0 + (k & 15) * 16 + (lane >> 2), g.N - 1);
-      const int word = min(kt0 + 4 * gi + (lane & 3), kt1 - 1);
-      dma4((isa ? g.as : g.bs) + row * srow + word * 4, sl0 + (gi % NG) * SG + k * 256);
-    }
+    const bool isa = k < 16;
+    const int64_t row = isa ? min(m0 + (k & 15) * 16 + (lane >> 2), g.M - 1)
+                            : min(n0 + (k & 15) * 16 + (lane >> 2), g.N - 1);
+    const int word = min(kt0 + 4 * gi + (lane & 3), kt1 - 1);
+    dma4((isa ? g.as : g.bs) + row * srow + word * 4, sl0 + (gi % NG) * SG + k * 256);
   };
-  // the loads stage it issues (d of NIW): codes of stage it+4, then its
-  // part of scale group it/4 + 2 (WG: A rows in phase 0, B rows in phase 2
-  // of the group's 4 stages; else phase it % 4 of the 32 instructions)
+  // the loads stage it issues (d of NIW): codes of stage it+4, then phase
+  // it % 4 of scale group it/4 + 2
   auto issue1 = [&](int it, int slot, int d) {
     if (d < IA + IB) code1(min(kt0 + it + S, kt1 - 1), slot, d);
-    else if constexpr (WG) scale1(it / 4 + 2, (it & 2) * 2 + wave);
     else scale1(it / 4 + 2, (it & 3) * 8 + wave * 2 + (d - IA - IB));
   };
 
@@ -1057,29 +1037,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: scale group 0, then code stages 0-3 each with its part of
-  // scale group 1, as the stages 4 later issue theirs
-  if constexpr (WG) {
-    scale1(0, wave);
-    scale1(0, 4 + wave);
-  } else {
+  // prologue: scale group 0, then code stages 0-3 each with a quarter of
+  // scale group 1, so that every stage's loads number NIW
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
-      for (int t = 0; t < IS; ++t) scale1(0, p * 8 + wave * 2 + t);
-  }
+    for (int t = 0; t < IS; ++t) scale1(0, p * 8 + wave * 2 + t);
 #pragma unroll
   for (int s = 0; s < S; ++s) {
 #pragma unroll
     for (int d = 0; d < IA + IB; ++d) code1(min(kt0 + s, kt1 - 1), s, d);
-    if constexpr (WG) {
-      if ((s & 1) == 0) scale1(1, (s & 2) * 2 + wave);
-    } else {
 #pragma unroll
-      for (int t = 0; t < IS; ++t) scale1(1, s * 8 + wave * 2 + t);
-    }
+    for (int t = 0; t < IS; ++t) scale1(1, s * 8 + wave * 2 + t);
   }
-  wait_vm_barrier<NIW2 + IA + IB + ISO>();               // scale group 0 and code stage 0 have landed
+  wait_vm_barrier<(S - 1) * NIW>();                      // scale group 0 and code stage 0 have landed
   Frags F;
 #pragma unroll
   for (int k = 0; k < 32; ++k) read1(F, 0, 0, k);
@@ -1101,14 +1072,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
     for (int i = 0; i < TM; ++i) {
       // stage it+1 has landed (stages it+2, it+3 may still be in flight),
       // every wave has read stage it
-      if (i == 4) wait_vm_barrier<NIW2>();
+      if (i == 4) wait_vm_barrier<(S - 2) * NIW>();
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         mfma_mx_acc_agpr(acc[i][j], cur.a[i], cur.b[j], cur.sa[i], cur.sb[j]);
-        // the refill, one load per MFMA from row 4 on (WG: the scale load in
-        // even stages only)
-        if (i >= 4 && (i - 4) * TN + j < NIW && (!WG || (i - 4) * TN + j < IA + IB || (it & 1) == 0))
-          issue1(it, slot, (i - 4) * TN + j);
+        // the refill: NIW loads, one per MFMA from row 4 on
+        if (i >= 4 && (i - 4) * TN + j < NIW) issue1(it, slot, (i - 4) * TN + j);
         // next stage's reads, the earliest needed first: B codes and scales
         // (row 0), A scales, A codes (A block i is first used in row i)
         if (i >= 4) read1(nxt, it + 1, next, i == 4 ? 8 + j : i == 5 ? 24 + j : i == 6 ? 16 + j : j);
@@ -1135,6 +1104,298 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
   mfma_guard();                                          // before any accumulator read
   wait_vm_barrier<0>();                                  // the reloads have landed before the workgroup ends
   store_tile<TM, TN>(g, acc, m0 + wm * 128, n0 + wn * 128, r16, grp);
+}
+
+// MX-FP4 on 256x256 tiles where K is a multiple of 512, persistent: the
+// structure of gemm_mxfp4_w1_kernel (above) with two changes.
+//
+// Scales of whole groups. A row's 4 stages of scales are 16 bytes, which a
+// lane loads in one 16-byte load: 8 instructions of 64 rows per group, A
+// rows by each wave in the group's first stage and B rows in its third
+// (each load instruction costs the MFMA stream about the same whatever it
+// moves), so an even stage issues 9 loads and an odd one 8, and two
+// successive stages always 17, which the waits rely on.
+//
+// Persistent: one workgroup per CU, workgroup b running tiles b, b + P,
+// ... The fp32 C of a 256x256 tile is 256 KiB against 32 KiB of operands
+// per stage, and with one tile per workgroup every round of tiles ended
+// with all of them storing at once (measured on MI355X: without its C
+// store the one-tile kernel ran 12-31 % faster at K = 4096-11008). Here a
+// tile's store drains while the next tile multiplies. The MFMAs take B as
+// the first operand, so a lane's four results of a 16x16 block lie in one
+// row of C and the store is 64 16-byte writes per lane. With at least two
+// groups per tile and both tiles wholly inside A and B, a tile's last 4
+// stages load the next tile's stages 0-3 and its last 8 the next tile's
+// scale groups 0-1 (the stream runs on through the rings: K % 512 == 0
+// brings the code ring back to slot 0, the group ring moves on by K/512);
+// otherwise stages and groups past the end reload the last one, and after
+// its last stage the tile waits for every load and fills the rings afresh.
+// Loads after a store share its counter (vmcnt counts loads and stores, in
+// order): in the first three stages after a store the wait for the next
+// stage allows 63 operations in flight, which the 64 writes issued after
+// that stage's loads guarantee; the fourth stage's wait covers the store.
+__global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1p_kernel(GemmArgs g) {
+  constexpr int S = 4, NU = 16;                            // code stages; 16-row units per operand
+  constexpr int LA = NU * 1024, LB = NU * 1024;            // code bytes per stage
+  constexpr int STAGE = LA + LB;
+  constexpr int SG = 512 * 16, NG = 3;                     // scale group bytes (4 stages), ring slots
+  constexpr int IA = NU / 4, IB = NU / 4;                  // code loads per wave and stage
+  constexpr int NIW = IA + IB + 1;                         // DMA instructions of an even stage
+  constexpr int NIW2 = 2 * (IA + IB) + 1;                  // of two successive stages
+  constexpr int TM = 8, TN = 8;
+  static_assert(NIW + NIW2 <= 63, "vmcnt range");
+  static_assert(TM * TN >= 63, "a tile's 16-byte writes alone fill the vmcnt window");
+  static_assert(NIW <= 4 * TN, "the refill fits in rows 4-7");
+  static_assert(2 * 4 * 64 == 512, "a group's rows: one 16-byte load of 64 rows per wave and operand");
+  static_assert(S * STAGE + NG * SG <= 160 * 1024, "LDS");
+  __shared__ __align__(1024) uint8_t smem[S * STAGE + NG * SG];
+
+  const int P = (int)gridDim.x - g.fin.n;                  // tile workgroups
+  if ((int)blockIdx.x >= P) {
+    if (blockIdx.y == 0) finalize_one(g.fin.j[blockIdx.x - P]);
+    return;
+  }
+  const int tiles = g.tiles_m * g.tiles_n;
+  const int nk = (int)(g.K / 128);                         // stages of a tile
+  const int ng = nk / 4;                                   // scale groups of a tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int64_t rowbytes = g.K / 2, srow = g.K / 32;
+
+  // DMA sources of the tile at (m0, n0), per lane a 32-bit offset from the
+  // operand's start: wave w loads code units w, w+4, ... of A and of B and
+  // scale rows 64 w + lane of A and of B; rows past M or N read the last
+  // row.
+  int64_t m0, n0;
+  uint32_t offa[IA], offb[IB], offs[2];
+  auto sources = [&]() {
+#pragma unroll
+    for (int t = 0; t < IA; ++t)
+      offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + (lane & 3) * 16;
+#pragma unroll
+    for (int t = 0; t < IB; ++t)
+      offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
+    offs[0] = (uint32_t)(min(m0 + wave * 64 + lane, g.M - 1) * srow);
+    offs[1] = (uint32_t)(min(n0 + wave * 64 + lane, g.N - 1) * srow);
+  };
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  const uint32_t sl0 = lds0 + S * STAGE;                   // scale ring
+  // load d of a stage's codes: stage kt of the tile dm (A) and dn (B) rows
+  // past the one the offsets were worked out for, into code slot `slot`
+  auto code1 = [&](int kt, int slot, int d, int dm, int dn) {
+    uint32_t lw = lds0 + slot * STAGE + wave * 1024;
+    asm volatile("" : "+s"(lw));
+    if (d < IA) dma16s(g.a + (int64_t)dm * rowbytes + (int64_t)kt * 64, offa[d], lw + d * 4096);
+    else dma16s(g.b + (int64_t)dn * rowbytes + (int64_t)kt * 64, offb[d - IA], lw + LA + (d - IA) * 4096);
+  };
+  // Scale instruction k (of 8) of group gi (of the tile dm / dn rows on)
+  // into group slot gs: 64 rows (A rows for k < 4, then B rows), lane l row
+  // 64 (k % 4) + l, its 16 bytes at 16 gi
+  auto scale1 = [&](int gi, int k, int gs, int dm, int dn) {
+    uint32_t lw = sl0 + gs * SG + k * 1024;
+    asm volatile("" : "+s"(lw));
+    if (k < 4) dma16s(g.as + (int64_t)dm * srow + (int64_t)gi * 16, offs[0], lw);
+    else dma16s(g.bs + (int64_t)dn * srow + (int64_t)gi * 16, offs[1], lw);
+  };
+  // A tile's prologue (ring slots from 0): scale group 0, then code stages
+  // 0-3 each with its part of scale group 1, as the stages 4 later issue
+  // theirs; stages and groups past the end reload the last one
+  auto prologue = [&]() {
+    const int g1 = min(1, ng - 1);
+    scale1(0, wave, 0, 0, 0);
+    scale1(0, 4 + wave, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+#pragma unroll
+      for (int d = 0; d < IA + IB; ++d) code1(min(s, nk - 1), s, d, 0, 0);
+      if ((s & 1) == 0) scale1(g1, (s & 2) * 2 + wave, 1, 0, 0);
+    }
+  };
+
+  // A stage's operands in registers: code slices (lane (r16, grp) holds K
+  // elements 32 grp .. 32 grp + 31 of row r16) and, per fragment, row
+  // r16's 4 block scales of the stage (one LDS word), shifted so that byte
+  // 0 holds the lane's block grp
+  struct Frags {
+    uint4 a[TM], b[TN];
+    uint32_t sa[TM], sb[TN];
+  };
+  // read k of 32 of a stage in code slot `slot` whose scales are word w of
+  // group slot gs: A codes, B codes, A scales, B scales (8 each)
+  auto read1 = [&](Frags& f, int slot, int gs, int w, int k) {
+    const uint8_t* base = smem + slot * STAGE;
+    const uint8_t* sg = smem + S * STAGE + gs * SG + w * 4;
+    if (k < 8) f.a[k] = *reinterpret_cast<const uint4*>(base + (wm * TM + k) * 1024 + r16 * 64 + grp * 16);
+    else if (k < 16) f.b[k - 8] = *reinterpret_cast<const uint4*>(base + LA + (wn * TN + k - 8) * 1024 + r16 * 64 + grp * 16);
+    else if (k < 24) f.sa[k - 16] = *reinterpret_cast<const uint32_t*>(sg + ((wm * TM + k - 16) * 16 + r16) * 16);
+    else f.sb[k - 24] = *reinterpret_cast<const uint32_t*>(sg + 4096 + ((wn * TN + k - 24) * 16 + r16) * 16);
+  };
+
+  floatx4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int e = (g.ea ? *g.ea : 0) + (g.eb ? *g.eb : 0);
+  auto interior = [&](int64_t r0, int64_t c0) { return r0 + 256 <= g.M && c0 + 256 <= g.N; };
+  // Whether the tile at (m0, n0) streams on into the workgroup's next tile,
+  // through its own offsets shifted by (dm, dn) rows: at least two groups (the next tile's group 0 is loaded 8 to 5 stages before
+  // this tile ends, by its own refills), and both tiles wholly inside A and
+  // B, so that neither has clamped rows.
+  bool ahead = false;
+  int dm = 0, dn = 0;
+  int tile = blockIdx.x;
+  auto plan_ahead = [&]() {
+    ahead = false;
+    if (ng >= 2 && tile + P < tiles && interior(m0, n0)) {
+      int tm2, tn2;
+      tile_coords(tile + P, g.tiles_m, g.tiles_n, tm2, tn2);
+      if (interior((int64_t)tm2 * 256, (int64_t)tn2 * 256)) {
+        ahead = true;
+        dm = (int)((int64_t)tm2 * 256 - m0);
+        dn = (int)((int64_t)tn2 * 256 - n0);
+      }
+    }
+  };
+  {
+    int tm, tn;
+    tile_coords(tile, g.tiles_m, g.tiles_n, tm, tn);
+    m0 = (int64_t)tm * 256;
+    n0 = (int64_t)tn * 256;
+  }
+  sources();
+  prologue();
+  plan_ahead();
+
+  int slot = 0;                                          // code slot of the stage to multiply next
+  int gb = 0;                                            // group slot of the tile's group 0
+  bool stored = false;                                   // a store was issued after this tile's first loads
+  bool have0 = false;                                    // F holds the tile's stage 0
+  Frags F, N;
+  // Stage it with its operands in `cur`, reading stage it+1's (with
+  // `ahead`, after the last stage, the next tile's stage 0) into `nxt`.
+  auto stage = [&](int it, const Frags& cur, Frags& nxt) {
+    const int next = slot == S - 1 ? 0 : slot + 1;
+    const int gr = (gb + (it + 1) / 4) % NG;             // group slot of stage it+1
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      // stage it+1 has landed (stages it+2, it+3 may still be in flight; in
+      // the first three stages after a store, the store's writes too),
+      // every wave has read stage it
+      if (i == 4) {
+        if (stored && it < S - 1) wait_vm_barrier<63>();
+        else wait_vm_barrier<NIW2>();
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        // C transposed: a lane's results lie in one row
+        mfma_mx_acc_agpr(acc[i][j], cur.b[j], cur.a[i], cur.sb[j], cur.sa[i]);
+        // the refill, one load per MFMA from row 4 on: codes of stage it+4
+        // (of the next tile with `ahead`, else the last stage again past the
+        // end), then, in even stages, the stage's part of scale group it/4 + 2
+        const int d = (i - 4) * TN + j;
+        if (i >= 4 && d < NIW && (d < IA + IB || (it & 1) == 0)) {
+          const int st = it + S;
+          const bool own = st < nk;
+          if (d < IA + IB) {
+            code1(own ? st : ahead ? st - nk : nk - 1, slot, d, own || !ahead ? 0 : dm, own || !ahead ? 0 : dn);
+          } else {
+            const int gi = it / 4 + 2;
+            const int gs = (gb + gi) % NG;
+            const bool gown = gi < ng;
+            // (past the end, the next tile's groups 0-1, never past its last)
+            scale1(gown ? gi : ahead ? min(gi - ng, ng - 1) : ng - 1, (it & 2) * 2 + wave, gs,
+                   gown || !ahead ? 0 : dm, gown || !ahead ? 0 : dn);
+          }
+        }
+        // next stage's reads, the earliest needed first: B codes and scales
+        // (row 0), A scales, A codes (A block i is first used in row i)
+        if (i >= 4) read1(nxt, next, gr, (it + 1) & 3, i == 4 ? 8 + j : i == 5 ? 24 + j : i == 6 ? 16 + j : j);
+        // in the last row, the next stage's scale words (read in rows 5-6)
+        // get the lane's byte (K block grp) shifted to byte 0, long before
+        // an MFMA reads them (pinned: left to itself the compiler sinks the
+        // shift into the next stage, right before that MFMA)
+        if (i == TM - 1) {
+          nxt.sa[j] >>= 8 * grp;
+          nxt.sb[j] >>= 8 * grp;
+          asm volatile("" : "+v"(nxt.sa[j]), "+v"(nxt.sb[j]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    slot = next;
+  };
+
+  for (;;) {
+    if (!have0) {
+      // stage 0 and scale group 0 have landed: after a store its 64 writes
+      // follow the prologue's loads, else the loads of stages 1-3 do
+      if (stored) wait_vm_barrier<63>();
+      else wait_vm_barrier<NIW2 + IA + IB>();
+#pragma unroll
+      for (int k = 0; k < 32; ++k) read1(F, slot, gb, 0, k);
+      // shifted here, not sunk next to the MFMA that reads them
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        F.sa[i] >>= 8 * grp;
+        F.sb[i] >>= 8 * grp;
+        asm volatile("" : "+v"(F.sa[i]), "+v"(F.sb[i]));
+      }
+    }
+    mfma_guard();
+    // two stages per loop iteration with the fragment sets swapped, so no
+    // registers are copied between stages (the loop holds a barrier, which
+    // keeps the compiler from unrolling it); nk is a multiple of 4, so the
+    // next tile's stage 0 ends up in F. The odd last stage that follows
+    // never runs, but without it the register allocator moves accumulators
+    // between the loop and the tile's end (AGPR moves next to the asm
+    // MFMAs, a hazard the compiler does not see).
+    int it = 0;
+    for (; it + 1 < nk; it += 2) {
+      stage(it, F, N);
+      stage(it + 1, N, F);
+    }
+    if (it < nk) stage(it, F, N);
+    mfma_guard();                                        // before any accumulator read
+
+    // the tile is complete: with `ahead` the next tile's first stages are
+    // in the rings and its stage 0 in F; otherwise the rings are filled
+    // afresh once every load has landed and every wave is done with them.
+    // Then this tile's store is issued.
+    const int64_t cm0 = m0, cn0 = n0;
+    const bool streamed = ahead;
+    tile += P;
+    const bool last = tile >= tiles;
+    if (!last) {
+      int tm, tn;
+      tile_coords(tile, g.tiles_m, g.tiles_n, tm, tn);
+      m0 = (int64_t)tm * 256;
+      n0 = (int64_t)tn * 256;
+      sources();
+      if (streamed) {
+        gb = (gb + ng) % NG;
+      } else {
+        wait_vm_barrier<0>();
+        slot = 0;
+        gb = 0;
+        prologue();
+      }
+      have0 = streamed;
+      plan_ahead();
+    } else {
+      wait_vm_barrier<0>();                              // the reloads have landed before the workgroup ends
+    }
+    stored = store_tile_rows<TM, TN>(g, acc, cm0 + wm * 128, cn0 + wn * 128, r16, grp, e);
+    if (!stored) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the checked form may write less
+    if (last) break;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
 }
 
 // Split-K reduction: C = 2^(ea+eb) * sum over splits, in split order.
@@ -1356,10 +1617,13 @@ static bool launch_fmt(const GemmPlan& p, const GemmArgs& g, hipStream_t s) {
       const int64_t wgs = QO ? p.tiles : std::min<int64_t>(p.tiles, device_cus());
       hipLaunchKernelGGL((gemm_nvfp4_w1_kernel<QO>), dim3((unsigned)(wgs + g.fin.n)), dim3(NT), 0, s, g);
     } else if constexpr (FMT == SNIP_MXFP4 && !QO) {
-      if (g.K % 512 == 0 && g.kchunk % 512 == 0)
-        hipLaunchKernelGGL(gemm_mxfp4_w1_kernel<true>, grid, dim3(NT), 0, s, g);
-      else
-        hipLaunchKernelGGL(gemm_mxfp4_w1_kernel<false>, grid, dim3(NT), 0, s, g);
+      // K % 512 == 0: one workgroup per CU, each running its tiles in turn
+      if (g.K % 512 == 0 && p.ksplit == 1 && !g.nsec) {
+        const dim3 pgrid((unsigned)(std::min<int64_t>(p.tiles, device_cus()) + g.fin.n));
+        hipLaunchKernelGGL(gemm_mxfp4_w1p_kernel, pgrid, dim3(NT), 0, s, g);
+      } else {
+        hipLaunchKernelGGL(gemm_mxfp4_w1_kernel, grid, dim3(NT), 0, s, g);
+      }
     }
     else hipLaunchKernelGGL((gemm_kernel<FMT, 256, 256, 4, 1, QO>), grid, dim3(NT), 0, s, g);
   } else if (p.staged) {
