@@ -1491,10 +1491,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_q_kernel(GemmArgs g, int ns
 // K = 4096 (28672x8192x4096 1.546 -> 1.527 ms; the Llama-70B block step
 // 18.73 -> 18.51 ms), so planned for K >= 4096 (in pairs of 128-element
 // stages: the kernel loads each row's scales of two stages at once).
+// MX-FP4 256x256 tiles with K % 512 == 0 run persistent
+// (gemm_mxfp4_w1p_kernel): priced at 1.25 instead of 1.03, they take
+// shapes the register-staged 128x128 kernel had (measured on MI355X:
+// 4096x11008x16384 0.562 -> 0.387 ms, 4096x11008x4096 0.154 -> 0.127 ms,
+// 11008x4096x8192 0.277 -> 0.212 ms; no shape slower). At 1.6 some shapes
+// gained and others lost (4096x5632x2048 0.049 -> 0.053 ms).
 static double big_tile_gain(int format, int64_t K) {
   switch (format) {
     case SNIP_FP8_E4M3: return 1.15;
-    case SNIP_MXFP4: return 1.03;
+    case SNIP_MXFP4: return K % 512 == 0 ? 1.25 : 1.03;
     case SNIP_NVFP4: return K >= 4096 && K % 256 == 0 ? 1.18 : 0.0;
     default: return 1.02;
   }

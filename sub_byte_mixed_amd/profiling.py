@@ -250,7 +250,7 @@ def cmd_mfma(a):
              "LDS bytes |", "|---|---|---|---|---|---|---|"]
     total = 0.0
     for name in sorted(util, key=lambda n: -sum(util[n].values())):
-        if "snip::gemm_" not in name:
+        if not _is_gemm(name):
             continue
         ud = util[name]
         fl = {k: sum(m.get(name, {}).values()) * 512 for k, m in mops.items()}
@@ -268,6 +268,12 @@ def cmd_mfma(a):
     print("\n".join(lines))
 
 
+def _is_gemm(name: str) -> bool:
+    """A GEMM kernel of the library, in a named or an anonymous namespace
+    (gemm_kernel, staged_gemm_kernel, gemm_nvfp4_w1_kernel, ...)."""
+    return "snip::" in name and re.search(r"\bgemm_|staged_gemm_", name) is not None
+
+
 def cmd_stalls(a):
     """Where the GEMM kernels' wave time goes: SQ wave-cycle counters of
     several --pmc runs, each as a share of SQ_WAVE_CYCLES taken in the same
@@ -281,7 +287,7 @@ def cmd_stalls(a):
                 continue
             vals = _per_kernel(path, c)
             rows.append((c, {k: sum(v.values()) / max(sum(wave.get(k, {}).values()), 1.0) for k, v in vals.items()}))
-    kernels = sorted({k for _, d in rows for k in d if "snip::gemm_" in k})
+    kernels = sorted({k for _, d in rows for k in d if _is_gemm(k)})
     head = "| Counter / SQ_WAVE_CYCLES | " + " | ".join(f"`{_short(k, 48)}`" for k in kernels) + " |"
     lines = [f"# Wave-cycle breakdown of the GEMM kernels on the {a.workload} workload", "",
              "SQ counters in quad-cycles, summed over each kernel's dispatches in a --pmc run of the benchmark,",
