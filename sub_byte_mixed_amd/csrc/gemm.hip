@@ -635,6 +635,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
     }
   };
 
+  // load d of a refill whose global bases (codes of A and B, scales of A
+  // and B) and LDS bases (code slot, group slot) are given; each LDS base
+  // is copied through an empty asm so that no per-instruction LDS address
+  // is kept in a register of its own
+  auto refill1 = [&](const uint8_t* pa, const uint8_t* pb, const uint8_t* psa, const uint8_t* psb, uint32_t lw0,
+                     uint32_t ls0, int d) {
+    if (d < IA + IB) {
+      uint32_t lw = lw0;
+      asm volatile("" : "+s"(lw));
+      if (d < IA) dma16s(pa, offa[d], lw + d * 4096);
+      else dma16s(pb, offb[d - IA], lw + LA + (d - IA) * 4096);
+    } else {
+      uint32_t ls = ls0;
+      asm volatile("" : "+s"(ls));
+      if (d == IA + IB) dma16s(psa, offs[0], ls);
+      else dma16s(psb, offs[1], ls + SG / 2);
+    }
+  };
+
   // A stage's raw operands in registers: code slices (16 bytes per lane)
   // and the lane's two E4M3 block-scale bytes per fragment. The scales are
   // converted to fp16 pairs where first needed, not where read: one wave per
@@ -670,6 +689,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
     else
       r.s[k - TN] =
           *reinterpret_cast<const uint16_t*>(smem + sg + SG / 2 + ((wn * TN + k - TN) * 16 + r16) * 16 + grp * 2);
+  };
+  // The next stage's reads from lane addresses worked out once per stage
+  // (codes at k KiB on, scales at 256 k bytes on: immediate offsets), each
+  // passed through an empty asm so that the compiler keeps it rather than
+  // rebuilding every read's address (two VALU additions a read).
+  typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(3))) u32x4_t lds_u4;
+  typedef const __attribute__((address_space(3))) uint16_t lds_u16;
+  lds_u8* const lbase = (lds_u8*)smem;
+  auto code_base = [&](int slot, int blk) {               // lane's first code read of 16-row block blk
+    lds_u8* p = lbase + slot * STAGE + blk * 1024 + r16 * 64 + grp * 16;
+    asm volatile("" : "+v"(p));
+    return p;
+  };
+  auto scale_base = [&](int sg, int blk) {                // lane's first scale read of block blk
+    lds_u8* p = lbase + sg + (blk * 16 + r16) * 16 + grp * 2;
+    asm volatile("" : "+v"(p));
+    return p;
   };
   auto read_b = [&](RawB& r, int slot, int sg) {
     const uint8_t* lb = smem + slot * STAGE + LA + (wn * TN) * 1024 + r16 * 64 + grp * 16;
@@ -783,8 +821,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
       RawA NA;
       RawB NB;
       half2_t nsb[TN], nsa0;
-      bool rf = false;                                   // this stage refills its slot: stage kt of
-      int rkt = 0, rdm = 0, rdn = 0;                     // the tile rdm / rdn rows on
+      bool rf = false;                                   // this stage refills its slot: stage rkt of
+      int rkt = 0, rdm = 0, rdn = 0;                     // the tile rdm / rdn rows on, from these bases
+      const uint8_t *rpa = g.a, *rpb = g.b, *rpsa = g.as, *rpsb = g.bs;
+      uint32_t rlw = 0, rls = 0;                         // and into these LDS bases
+      lds_u8 *rcb = lbase, *rsb = lbase, *rca = lbase, *rsa = lbase;   // the next stage's read bases
       // slices and row blocks unrolled by templates: the unroller's size
       // limit would otherwise leave the slice loop rolled, its register
       // arrays indexed at run time (in scratch)
@@ -815,7 +856,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
             rkt = own ? it + S : it + S - nk;
             rdm = own ? 0 : dm;
             rdn = own ? 0 : dn;
+            // the refill's bases, worked out once for its loads
+            rpa = g.a + (int64_t)rdm * rowbytes + (int64_t)rkt * 64;
+            rpb = g.b + (int64_t)rdn * rowbytes + (int64_t)rkt * 64;
+            rpsa = g.as + (int64_t)rdm * srow + (int64_t)rkt * 8;
+            rpsb = g.bs + (int64_t)rdn * srow + (int64_t)rkt * 8;
+            rlw = lds0 + slot * STAGE + wave * 1024;
+            rls = lds0 + sg0 + rgs * SG + wave * 1024;
+            rcb = code_base(next, NU + wn * TN);          // B codes: units after the 16 of A
           }
+          if constexpr (q == 2 && i == 7) rsb = scale_base(nsg + SG / 2, wn * TN);
+          if constexpr (q == 3 && i == 0) rca = code_base(next, wm * TM);
+          if constexpr (q == 3 && i == 1) rsa = scale_base(nsg, wm * TM);
           // pieces 0-3: A block i+1 (or the next slice's block 0), pieces
           // 4-7: B block i for the next slice; group j converts piece j and
           // multiplies piece j-1, so no multiply waits on the convert just
@@ -840,15 +892,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
             if constexpr (QO) mfma_acc_agpr(acc[i][j], ad, bd[j]);
             else mfma_acc_agpr(acc[i][j], bd[j], ad);  // C transposed: a lane's results lie in one row
             if constexpr (q == 2 && i == 6) {
-              if (rf) issue1(rkt, slot, rdm, rdn, rgs, j);
-              read_b1(NB, next, nsg, j);
+              if (rf) refill1(rpa, rpb, rpsa, rpsb, rlw, rls, j);
+              NB.b[j] = __builtin_bit_cast(uint4, *(lds_u4*)(rcb + j * 1024));
             }
             if constexpr (q == 2 && i == 7) {
-              if (j < IS && rf && !odd) issue1(rkt, slot, rdm, rdn, rgs, TN + j);
-              read_b1(NB, next, nsg, TN + j);
+              if (j < IS && rf && !odd) refill1(rpa, rpb, rpsa, rpsb, rlw, rls, TN + j);
+              NB.s[j] = *(lds_u16*)(rsb + j * 256);
             }
-            if constexpr (q == 3 && i == 0) read_a1(NA, next, nsg, j);
-            if constexpr (q == 3 && i == 1) read_a1(NA, next, nsg, TM + j);
+            if constexpr (q == 3 && i == 0) NA.a[j] = __builtin_bit_cast(uint4, *(lds_u4*)(rca + j * 1024));
+            if constexpr (q == 3 && i == 1) NA.s[j] = *(lds_u16*)(rsa + j * 256);
             t[j] = cvt_j(j);
             asm volatile("" : "+v"(t[j]));             // computed here, not sunk to its use
             if (j > 0) {
