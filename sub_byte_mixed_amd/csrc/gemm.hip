@@ -52,7 +52,8 @@
 //
 // Tiling: a workgroup of 256 threads (2x2 waves) owns a BM x BN output tile:
 // 256x256 (one workgroup per CU; for NVFP4 and MX-FP4 the one-wave-per-SIMD
-// kernels gemm_nvfp4_w1_kernel and gemm_mxfp4_w1_kernel below), 256x128
+// kernels gemm_nvfp4_w1_kernel, gemm_mxfp4_w1_kernel and
+// gemm_mxfp4_w1p_kernel below, the first and last persistent), 256x128
 // (FP8 and NVFP4, two per CU), 128x128 (two per CU) or, for skinny FP8 /
 // NVFP4 problems, 64x64, as plan_gemm decides from the problem's tile
 // rounds. Tile order: the hardware hands workgroups to the 8 XCDs
