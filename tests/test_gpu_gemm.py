@@ -107,6 +107,9 @@ PLAN_CASES = [
     (S.FP8, 1500, 35500, 512),      # 256x256 (834 tiles: 256x128 would leave a last round of 132)
     (S.MXFP4, 8000, 4000, 512),     # 256x256, one wave per SIMD (4 stages: one whole scale group)
     (S.MXFP4, 8000, 4000, 2560),    # 256x256, one wave per SIMD (20 stages: 5 whole scale groups, ring of 3)
+    (S.MXFP4, 8000, 4000, 1024),    # persistent, 2 tiles per workgroup: two scale groups, every refill of a
+                                    # streaming tile loads the next tile's stages and groups
+    (S.MXFP4, 8000, 4000, 1536),    # persistent: three scale groups (the group ring moves on by 3 per tile)
     (S.MXFP4, 8000, 4000, 640),     # 256x256, one wave per SIMD (5 stages: the odd last stage, quad-lane scale loads)
     (S.BF16, 8000, 4000, 256),      # 256x256
     (S.MXFP4, 2000, 1600, 768),     # staged 128x128, 256-element stages
