@@ -1220,16 +1220,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1p_kernel(GemmArgs g) {
   // DMA sources of the tile at (m0, n0), per lane a 32-bit offset from the
   // operand's start: wave w loads code units w, w+4, ... of A and of B and
   // scale rows 64 w + lane of A and of B; rows past M or N read the last
-  // row.
+  // row. In LDS a 16-row unit is 16 rows x 64 bytes with row r's 16-byte
+  // chunk c at position c ^ swz(r): the MFMA-side reads (lane (r16, grp)
+  // takes chunk grp of row r16, 16 bytes) then meet no bank twice in a
+  // cycle, with 32 or 64 banks (with chunks in order, rows 64 bytes apart
+  // did); the load's lane l brings the chunk that its slot (row l / 4,
+  // position l % 4) holds.
+  auto swz = [](int r) { return ((r >> 1) ^ (r >> 2)) & 3; };
+  const int chunk = ((lane & 3) ^ swz(lane >> 2)) * 16;
   int64_t m0, n0;
   uint32_t offa[IA], offb[IB], offs[2];
   auto sources = [&]() {
 #pragma unroll
     for (int t = 0; t < IA; ++t)
-      offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + (lane & 3) * 16;
+      offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + chunk;
 #pragma unroll
     for (int t = 0; t < IB; ++t)
-      offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
+      offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + chunk;
     offs[0] = (uint32_t)(min(m0 + wave * 64 + lane, g.M - 1) * srow);
     offs[1] = (uint32_t)(min(n0 + wave * 64 + lane, g.N - 1) * srow);
   };
@@ -1277,11 +1284,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1p_kernel(GemmArgs g) {
   };
   // read k of 32 of a stage in code slot `slot` whose scales are word w of
   // group slot gs: A codes, B codes, A scales, B scales (8 each)
+  const int cpos = r16 * 64 + (grp ^ swz(r16)) * 16;     // the lane's chunk in a 16-row unit
   auto read1 = [&](Frags& f, int slot, int gs, int w, int k) {
     const uint8_t* base = smem + slot * STAGE;
     const uint8_t* sg = smem + S * STAGE + gs * SG + w * 4;
-    if (k < 8) f.a[k] = *reinterpret_cast<const uint4*>(base + (wm * TM + k) * 1024 + r16 * 64 + grp * 16);
-    else if (k < 16) f.b[k - 8] = *reinterpret_cast<const uint4*>(base + LA + (wn * TN + k - 8) * 1024 + r16 * 64 + grp * 16);
+    if (k < 8) f.a[k] = *reinterpret_cast<const uint4*>(base + (wm * TM + k) * 1024 + cpos);
+    else if (k < 16) f.b[k - 8] = *reinterpret_cast<const uint4*>(base + LA + (wn * TN + k - 8) * 1024 + cpos);
     else if (k < 24) f.sa[k - 16] = *reinterpret_cast<const uint32_t*>(sg + ((wm * TM + k - 16) * 16 + r16) * 16);
     else f.sb[k - 24] = *reinterpret_cast<const uint32_t*>(sg + 4096 + ((wn * TN + k - 24) * 16 + r16) * 16);
   };
