@@ -1033,14 +1033,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
   const int kt1 = min((int)(g.K / 128), (int)((blockIdx.y + 1) * g.kchunk / 128));
   const int nk = kt1 - kt0;
 
-  // code DMA sources: wave w loads units w, w+4, ... of A and of B
+  // code DMA sources: wave w loads units w, w+4, ... of A and of B. In LDS
+  // row r's 16-byte chunk c sits at position c ^ swz(r), as in
+  // gemm_mxfp4_w1p_kernel, so the reads meet no bank twice in a cycle.
+  auto swz = [](int r) { return ((r >> 1) ^ (r >> 2)) & 3; };
+  const int chunk = ((lane & 3) ^ swz(lane >> 2)) * 16;
+  const int cpos = r16 * 64 + (grp ^ swz(r16)) * 16;
   uint32_t offa[IA], offb[IB];
 #pragma unroll
   for (int t = 0; t < IA; ++t)
-    offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + (lane & 3) * 16;
+    offa[t] = (uint32_t)(min(m0 + (wave + 4 * t) * 16 + (lane >> 2), g.M - 1) * rowbytes) + chunk;
 #pragma unroll
   for (int t = 0; t < IB; ++t)
-    offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + (lane & 3) * 16;
+    offb[t] = (uint32_t)(min(n0 + (wave + 4 * t) * 16 + (lane >> 2), g.N - 1) * rowbytes) + chunk;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const uint32_t sl0 = lds0 + S * STAGE;                   // scale ring
   auto code1 = [&](int kt, int slot, int d) {
@@ -1078,8 +1083,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_mxfp4_w1_kernel(GemmArgs g_in) {
   auto read1 = [&](Frags& f, int it, int slot, int k) {
     const uint8_t* base = smem + slot * STAGE;
     const uint8_t* sg = smem + S * STAGE + ((it / 4) % NG) * SG + (it & 3) * 4;
-    if (k < 8) f.a[k] = *reinterpret_cast<const uint4*>(base + (wm * TM + k) * 1024 + r16 * 64 + grp * 16);
-    else if (k < 16) f.b[k - 8] = *reinterpret_cast<const uint4*>(base + LA + (wn * TN + k - 8) * 1024 + r16 * 64 + grp * 16);
+    if (k < 8) f.a[k] = *reinterpret_cast<const uint4*>(base + (wm * TM + k) * 1024 + cpos);
+    else if (k < 16) f.b[k - 8] = *reinterpret_cast<const uint4*>(base + LA + (wn * TN + k - 8) * 1024 + cpos);
     else if (k < 24) f.sa[k - 16] = *reinterpret_cast<const uint32_t*>(sg + ((wm * TM + k - 16) * 16 + r16) * 16);
     else f.sb[k - 24] = *reinterpret_cast<const uint32_t*>(sg + 4096 + ((wn * TN + k - 24) * 16 + r16) * 16);
   };
