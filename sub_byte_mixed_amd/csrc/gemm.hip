@@ -620,21 +620,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
       dma16s(g.bs + (int64_t)dn * srow + (int64_t)kt * 8, offs[1], ls + SG / 2);
     }
   };
-  // load d of issue(kt, slot, dm, dn, gsl): A codes, B codes, A scales, B
-  // scales (the last two with an even kt only)
-  auto issue1 = [&](int kt, int slot, int dm, int dn, int gsl, int d) {
-    uint32_t lw = lds0 + slot * STAGE + wave * 1024, ls = lds0 + sg0 + gsl * SG + wave * 1024;
-    asm volatile("" : "+s"(lw), "+s"(ls));
-    if (d < IA) {
-      dma16s(g.a + (int64_t)dm * rowbytes + (int64_t)kt * 64, offa[d], lw + d * 4096);
-    } else if (d < IA + IB) {
-      dma16s(g.b + (int64_t)dn * rowbytes + (int64_t)kt * 64, offb[d - IA], lw + LA + (d - IA) * 4096);
-    } else if (d == IA + IB) {
-      dma16s(g.as + (int64_t)dm * srow + (int64_t)kt * 8, offs[0], ls);
-    } else {
-      dma16s(g.bs + (int64_t)dn * srow + (int64_t)kt * 8, offs[1], ls + SG / 2);
-    }
-  };
 
   // load d of a refill whose global bases (codes of A and B, scales of A
   // and B) and LDS bases (code slot, group slot) are given; each LDS base
@@ -677,19 +662,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_nvfp4_w1_kernel(GemmArgs g) {
     for (int i = 0; i < TM; ++i) r.a[i] = *reinterpret_cast<const uint4*>(la + i * 1024);
 #pragma unroll
     for (int i = 0; i < TM; ++i) r.s[i] = *reinterpret_cast<const uint16_t*>(sa + i * 256);
-  };
-  // read k of 16 of a stage's A (or B) operands: codes 0-7, scales 8-15
-  auto read_a1 = [&](RawA& r, int slot, int sg, int k) {
-    if (k < TM)
-      r.a[k] = *reinterpret_cast<const uint4*>(smem + slot * STAGE + (wm * TM + k) * 1024 + r16 * 64 + grp * 16);
-    else r.s[k - TM] = *reinterpret_cast<const uint16_t*>(smem + sg + ((wm * TM + k - TM) * 16 + r16) * 16 + grp * 2);
-  };
-  auto read_b1 = [&](RawB& r, int slot, int sg, int k) {
-    if (k < TN)
-      r.b[k] = *reinterpret_cast<const uint4*>(smem + slot * STAGE + LA + (wn * TN + k) * 1024 + r16 * 64 + grp * 16);
-    else
-      r.s[k - TN] =
-          *reinterpret_cast<const uint16_t*>(smem + sg + SG / 2 + ((wn * TN + k - TN) * 16 + r16) * 16 + grp * 2);
   };
   // The next stage's reads from lane addresses worked out once per stage
   // (codes at k KiB on, scales at 256 k bytes on: immediate offsets), each
