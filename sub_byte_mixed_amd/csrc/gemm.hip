@@ -1527,8 +1527,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_q_kernel(GemmArgs g, int ns
 // (4096x8192x1024 0.069 -> 0.087 ms). Persistent, with each tile's store
 // overlapping the next tile: also 1-3 % faster than 256x128 tiles at
 // K = 4096 (28672x8192x4096 1.546 -> 1.527 ms; the Llama-70B block step
-// 18.73 -> 18.51 ms), so planned for K >= 4096 (in pairs of 128-element
-// stages: the kernel loads each row's scales of two stages at once).
+// 18.73 -> 18.51 ms), so planned for K >= 4096 at first. With the later
+// refinements of its loop it also wins at K = 2048-3072 (measured on
+// MI355X, outputs bit-identical: 8192x4096x2048 0.117 -> 0.114 ms,
+// 8192x4096x3072 0.169 -> 0.158 ms) but not at K = 1024 (4096x8192x1024
+// 0.070 -> 0.075 ms): planned for K >= 2048, in pairs of 128-element
+// stages (the kernel loads each row's scales of two stages at once).
 // MX-FP4 256x256 tiles with K % 512 == 0 run persistent
 // (gemm_mxfp4_w1p_kernel): priced at 1.25 instead of 1.03, they take
 // shapes the register-staged 128x128 kernel had (measured on MI355X:
@@ -1539,7 +1543,7 @@ static double big_tile_gain(int format, int64_t K) {
   switch (format) {
     case SNIP_FP8_E4M3: return 1.15;
     case SNIP_MXFP4: return K % 512 == 0 ? 1.25 : 1.03;
-    case SNIP_NVFP4: return K >= 4096 && K % 256 == 0 ? 1.18 : 0.0;
+    case SNIP_NVFP4: return K >= 2048 && K % 256 == 0 ? 1.18 : 0.0;
     default: return 1.02;
   }
 }

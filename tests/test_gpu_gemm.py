@@ -90,18 +90,19 @@ def test_gemm_ldc_interior_tiles(fmt, M, N, ldc):
 
 
 # Shapes that make the planner pick each kernel and tile: 256x128 for FP8
-# and NVFP4, 256x256 for FP8, MX-FP4, BF16 and NVFP4 (K >= 4096 in whole
+# and NVFP4, 256x256 for FP8, MX-FP4, BF16 and NVFP4 (K >= 2048 in whole
 # pairs of 128-element stages), the register-staged 128x128 kernel for MX-FP4 and BF16, the
 # LDS-DMA 128x128 kernel for NVFP4 / FP8 and the 64x64 skinny tiles -- all
 # with ragged M and N. Sampled output rows (all columns) against the oracle.
 PLAN_CASES = [
     (S.FP8, 4000, 5600, 1024),      # 128x128 (256x128 would leave a last round of 192 tiles)
     (S.NVFP4, 8000, 4000, 512),     # 256x128, 2-stage ring
-    (S.NVFP4, 4000, 3900, 8448),    # 256x256, one wave per SIMD (K >= 4096; 66 stages)
+    (S.NVFP4, 4000, 3900, 8448),    # 256x256, one wave per SIMD (K >= 2048; 66 stages)
+    (S.NVFP4, 8000, 4000, 2304),    # the same kernel persistent at K = 2304 (18 stages), 2 tiles per workgroup
     (S.NVFP4, 3800, 17400, 4352),   # the same kernel persistent: 1020 tiles on 256 workgroups (3-4 each),
                                     # ragged edges, loads running on into the next tile between interior
                                     # tiles, 34 stages (the code ring's slots rotate from tile to tile)
-    (S.NVFP4, 3800, 17400, 4224),   # 256x128: K >= 4096 in an odd number (33) of stages
+    (S.NVFP4, 3800, 17400, 4224),   # 256x128: K >= 2048 in an odd number (33) of stages
     (S.NVFP4, 4000, 5600, 1024),    # 256x128, 2-stage ring
     (S.FP8, 8000, 4000, 512),       # 256x128
     (S.FP8, 1500, 35500, 512),      # 256x256 (834 tiles: 256x128 would leave a last round of 132)

@@ -46,7 +46,7 @@ def exact_operand(rows, k, fmt, seed):
 
 
 # (operand format, M, N, K, output format, rounding, amax factor): the shapes
-# select 256x128 (NVFP4, FP8), 256x256 (FP8, and NVFP4 for K >= 4096 in
+# select 256x128 (NVFP4, FP8), 256x256 (FP8, and NVFP4 for K >= 2048 in
 # pairs of 128-element stages),
 # 128x128, 64x64 unsplit and split-K plans, ragged in M.
 CASES = [
