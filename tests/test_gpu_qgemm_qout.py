@@ -52,6 +52,7 @@ def exact_operand(rows, k, fmt, seed):
 CASES = [
     (S.NVFP4, 4000, 4096, 256, S.NVFP4, S.RNE, 1.0),      # 256x128
     (S.NVFP4, 4000, 3904, 8448, S.NVFP4, S.SR, 1.0),      # 256x256, one wave per SIMD (66 stages)
+    (S.NVFP4, 4000, 3904, 2304, S.FP8, S.RNE, 1.0),       # the same at K = 2304 (18 stages)
     (S.NVFP4, 2000, 1600, 256, S.FP8, S.SR, 1.0),         # 128x128
     (S.NVFP4, 1000, 1200, 512, S.NVFP4, S.SR, 0.5),       # 64x64 unsplit; stale max below: saturation
     (S.NVFP4, 240, 2000, 2048, S.NVFP4, S.RNE, 4.0),      # 64x64, K split 4 ways: quantized in the reduction
