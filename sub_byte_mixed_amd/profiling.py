@@ -123,10 +123,16 @@ def _counter_rows(path):
 def gemm_kernel_prefixes(fmt: int) -> str:
     """Kernel-name prefixes of every GEMM kernel that runs format `fmt`,
     '|'-separated: the tile kernels of gemm_kernel and, for NVFP4, the
-    256x256 one-wave-per-SIMD kernel."""
+    256x256 one-wave-per-SIMD kernel; for MX-FP4 and BF16 also the
+    register-staged 128x128 kernel, and for MX-FP4 its 256x256
+    one-wave-per-SIMD kernels."""
     p = [f"void snip::gemm_kernel<{fmt},"]
     if fmt == 2:
         p.append("void snip::gemm_nvfp4_w1_kernel<")
+    if fmt in (0, 3):
+        p.append(f"void snip::(anonymous namespace)::staged_gemm_kernel<{fmt},")
+    if fmt == 3:
+        p.append("snip::gemm_mxfp4_w1")
     return "|".join(p)
 
 
