@@ -64,7 +64,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the quantized linear layer is "
+        print(json.dumps({"error": "the benchmark runs on one GPU: the quantized linear layer is "
                                    "measured on a single MI355X; --gpus must be 1"}))
         sys.exit(2)
     import torch
